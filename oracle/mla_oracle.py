@@ -1,0 +1,214 @@
+"""Oracle: absorbed Multi-Head Latent Attention decode, written out plainly in fp64.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the bench's
+CPU-baseline leg use this module; the HIP library neither imports nor calls
+it, and the two share no code.
+
+What is computed, and where the pages state it
+---------------------------------------------
+* Each token's cache entry is one low-rank latent vector c_KV; only that is
+  cached (TPLA abstract, on the taxoreview dblp:408/6122 and dblp:256/5536-3
+  pages).  Next to it sits one decoupled RoPE key that every head uses in
+  common (TransMLA review page, pith.science verdict on arXiv 2502.07864,
+  core_discovery).
+* Keys and values are reconstructed per head: the key's RoPE-free part is the
+  up-projection W_UK[h] of the latent, the value is the up-projection W_UV[h]
+  (early TransMLA abstract on the "GQA-to-MLA" Daily Papers listing, which
+  credits MLA's extra up-projection with its expressiveness).  This oracle
+  reconstructs K = [W_UK c ; k_rope] and V = c W_UV explicitly and runs
+  ordinary softmax attention over them.
+* The absorbed form folds W_UK into the query, so scores are taken against the
+  latent directly (TransMLA review page, key_machinery; the interaction matrix
+  of Eq. (26) in referee_report.major_comments[0]); all heads then read the
+  same cache record, the MQA form of the GQLA abstract.  ``absorb_q`` and
+  ``absorbed_scores`` write that form out so the tests can pin it against the
+  explicit one.
+* Several query tokens per step (multi-token prediction, TransMLA abstract on
+  the taxoreview pages; s_q = 2 in the GQLA abstract) are causal among
+  themselves at the tail of the sequence.
+* The e4m3 cache (FP8 quantization named in the TransMLA abstracts) is decoded
+  from the OCP E4M3 definition and multiplied by the token's fp32 scale.
+
+Readings taken where the pages are silent (each is also listed with the
+design notes): the softmax scale is 1/sqrt(d_nope + d_rope); ``seq_len``
+counts the cached tokens including the S_q new ones and query s sees
+positions t <= L - S_q + s; the log-sum-exp is natural-log; a query row with
+no visible token has output 0 and lse = -inf; one fp32 scale per token covers
+its whole record.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------- decoding
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> exact fp64 values (bf16 is the top half of fp32)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def e4m3_to_f64(bits: np.ndarray) -> np.ndarray:
+    """OCP E4M3 ("e4m3fn") bytes -> fp64, from the format's definition:
+    sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 is
+    subnormal (2^-6 * m/8); 0x7F / 0xFF are NaN; there is no infinity."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    normal = sign * np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))
+    subnormal = sign * np.ldexp(m / 8.0, -6)
+    v = np.where(e == 0, subnormal, normal)
+    return np.where((e == 15) & ((b & 0x7) == 7), np.nan, v)
+
+
+def cache_values(inputs: dict) -> np.ndarray:
+    """The whole paged cache as fp64 records [pages, block, d_c + d_r]; for the
+    e4m3 cache each record is multiplied by its token's fp32 scale."""
+    w = inputs["workload"]
+    if w.cache_dtype == "bf16":
+        return bf16_to_f64(inputs["cache"])
+    vals = e4m3_to_f64(inputs["cache"])
+    return vals * inputs["kv_scale"].astype(np.float64)[..., None]
+
+
+def gather(inputs: dict, b: int, values: np.ndarray | None = None):
+    """Sequence b's records in position order: C [L, d_c], KR [L, d_r].
+    Position t lives in physical page block_table[b][t // block] at slot t % block."""
+    w = inputs["workload"]
+    vals = cache_values(inputs) if values is None else values
+    L = int(inputs["seq_lens"][b])
+    t = np.arange(L)
+    pages = inputs["block_table"][b, t // w.block_size]
+    rec = vals[pages, t % w.block_size]
+    return rec[:, : w.d_latent], rec[:, w.d_latent: w.d_latent + w.d_rope]
+
+
+# ---------------------------------------------------------------- the method
+
+def reconstruct_kv(C: np.ndarray, KR: np.ndarray, w_uk: np.ndarray, w_uv: np.ndarray):
+    """Explicit per-head keys and values for heads ``w_uk.shape[0]``:
+    K[h, t] = [W_UK[h] c_t ; k_rope_t]  (d_n + d_r),  V[h, t] = c_t^T W_UV[h]  (d_v)."""
+    H, dn, dc = w_uk.shape
+    L = C.shape[0]
+    k_nope = (C @ w_uk.reshape(H * dn, dc).T).reshape(L, H, dn).transpose(1, 0, 2)
+    k = np.concatenate([k_nope, np.broadcast_to(KR, (H,) + KR.shape)], axis=2)
+    v = (C @ w_uv.transpose(1, 0, 2).reshape(dc, -1)).reshape(L, H, -1).transpose(1, 0, 2)
+    return k, v
+
+
+def visible_limit(L: int, q_len: int, s: int) -> int:
+    """Number of leading positions query s of a q_len-token step may see: the
+    step's queries are the last q_len positions of the sequence, so query s
+    sits at position L - q_len + s and sees t <= L - q_len + s."""
+    return max(0, L - q_len + 1 + s)
+
+
+def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, limit: int,
+           t0: int = 0, t1: int | None = None):
+    """Naive softmax attention of one query row over positions [t0, min(t1, limit)).
+    Returns (weights over that range, output, lse).  Empty range -> (empty, 0, -inf)."""
+    t1 = k.shape[0] if t1 is None else t1
+    hi = min(t1, limit)
+    if hi <= t0:
+        return np.zeros(0), np.zeros(v.shape[1]), -math.inf
+    z = scale * (k[t0:hi] @ q)
+    m = np.max(z)
+    e = np.exp(z - m)
+    l = np.sum(e)
+    p = e / l
+    return p, p @ v[t0:hi], m + math.log(l)
+
+
+def absorb_q(q_nope: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
+    """Absorbed query: q_lat[..., h, :] = q_nope[..., h, :] W_UK[h]  ([d_n] x [d_n, d_c])."""
+    return np.einsum("...hn,hnc->...hc", q_nope, w_uk)
+
+
+def absorbed_scores(q_lat_h: np.ndarray, q_rope_h: np.ndarray, C: np.ndarray, KR: np.ndarray, scale: float):
+    """Scores of one head in the absorbed form: scale * (q_lat . c_t + q_rope . k_rope_t)."""
+    return scale * (C @ q_lat_h + KR @ q_rope_h)
+
+
+def _heads(inputs: dict):
+    w = inputs["workload"]
+    return (bf16_to_f64(inputs["q_nope"]), bf16_to_f64(inputs["q_rope"]),
+            bf16_to_f64(inputs["w_uk"]), bf16_to_f64(inputs["w_uv"]), w)
+
+
+def decode_one(inputs: dict, b: int, heads=None, t0: int = 0, t1: int | None = None,
+               values: np.ndarray | None = None, _pre=None):
+    """Sequence b, heads ``heads`` (default all), positions [t0, t1):
+    returns out [S_q, nh, d_v], lse [S_q, nh], o_lat [S_q, nh, d_c] where
+    o_lat = sum_t p_t c_t is the attention output in latent space."""
+    q_nope, q_rope, w_uk, w_uv, w = _pre if _pre is not None else _heads(inputs)
+    heads = list(range(w.heads)) if heads is None else list(heads)
+    C, KR = gather(inputs, b, values)
+    L = C.shape[0]
+    S = w.q_len
+    out = np.zeros((S, len(heads), w.d_v))
+    lse = np.full((S, len(heads)), -math.inf)
+    o_lat = np.zeros((S, len(heads), w.d_latent))
+    step = 16
+    for i0 in range(0, len(heads), step):
+        hs = heads[i0: i0 + step]
+        k, v = reconstruct_kv(C, KR, w_uk[hs], w_uv[hs])
+        for j, h in enumerate(hs):
+            for s in range(S):
+                q = np.concatenate([q_nope[b, s, h], q_rope[b, s, h]])
+                p, o, ls = attend(q, k[j], v[j], w.softmax_scale, visible_limit(L, S, s), t0, t1)
+                out[s, i0 + j] = o
+                lse[s, i0 + j] = ls
+                if p.size:
+                    o_lat[s, i0 + j] = p @ C[t0: t0 + p.size]
+    return out, lse, o_lat
+
+
+def decode(inputs: dict, batches=None, heads=None):
+    """The whole decode step (all sequences by default): dict with
+    out [B, S_q, H, d_v], lse [B, S_q, H], o_lat [B, S_q, H, d_c] and the
+    absorbed query q_lat [B, S_q, H, d_c], all fp64."""
+    w = inputs["workload"]
+    pre = _heads(inputs)
+    values = cache_values(inputs)
+    batches = list(range(w.batch)) if batches is None else list(batches)
+    nh = w.heads if heads is None else len(list(heads))
+    out = np.zeros((len(batches), w.q_len, nh, w.d_v))
+    lse = np.zeros((len(batches), w.q_len, nh))
+    o_lat = np.zeros((len(batches), w.q_len, nh, w.d_latent))
+    for i, b in enumerate(batches):
+        out[i], lse[i], o_lat[i] = decode_one(inputs, b, heads, values=values, _pre=pre)
+    q_lat = absorb_q(pre[0], pre[2])
+    if heads is not None:
+        q_lat = q_lat[:, :, list(heads)]
+    return dict(out=out, lse=lse, o_lat=o_lat, q_lat=q_lat[batches])
+
+
+def partial(inputs: dict, b: int, t0: int, t1: int, values: np.ndarray | None = None, heads=None):
+    """One split of sequence b over positions [t0, t1): the latent output
+    normalised within the split and its lse, (o_lat [S_q, H, d_c], lse [S_q, H])."""
+    _, lse, o_lat = decode_one(inputs, b, heads, t0, t1, values)
+    return o_lat, lse
+
+
+def combine(o_parts: np.ndarray, lse_parts: np.ndarray):
+    """Merge split results by their log-sum-exp: L = log sum_k e^{lse_k},
+    o = sum_k e^{lse_k - L} o_k.  Splits with lse = -inf weigh nothing; if all
+    are empty the result is (0, -inf).  Axis 0 indexes the splits."""
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = np.max(lse_parts, axis=0)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    wts = np.where(np.isfinite(lse_parts), np.exp(lse_parts - m_safe), 0.0)
+    tot = np.sum(wts, axis=0)
+    o = np.einsum("k...,k...d->...d", wts, o_parts) / np.where(finite, tot, 1.0)[..., None]
+    lse = np.where(finite, m_safe + np.log(np.where(finite, tot, 1.0)), -math.inf)
+    return np.where(finite[..., None], o, 0.0), lse
+
+
+def up_v(o_lat: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
+    """Up-projection of the latent output: out[..., h, :] = o_lat[..., h, :] W_UV[h]."""
+    return np.einsum("...hc,hcv->...hv", o_lat, w_uv)
