@@ -1,0 +1,226 @@
+// C ABI of libmla_absorbed.so: argument checks, plan sizing and launches.
+// Declarations and the meaning of every argument are in include/mla_absorbed.h.
+#include "mla_absorbed.h"
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "mla_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mla_status_t fail(mla_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+mla_status_t ok() {
+  g_last_error.clear();
+  return MLA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+mla_status_t device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return MLA_OK;
+    }
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || n <= 0) return fail(MLA_ERR_HIP, "CU count query failed: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
+  *cus = n;
+  return MLA_OK;
+}
+
+mla_status_t check_shape(const mla_shape_t* s) {
+  if (!s) return fail(MLA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->batch < 1 || s->num_heads < 1 || s->q_len < 1 || s->d_nope < 1 || s->d_rope < 1 || s->d_latent < 1 ||
+      s->d_v < 1 || s->block_size < 1 || s->max_blocks_per_seq < 1)
+    return fail(MLA_ERR_INVALID_ARG, "shape has a non-positive size");
+  if (!std::isfinite(s->softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (s->cache_dtype != MLA_BF16 && s->cache_dtype != MLA_FP8_E4M3)
+    return fail(MLA_ERR_INVALID_ARG, "cache_dtype must be MLA_BF16 or MLA_FP8_E4M3");
+  if (s->out_dtype != MLA_BF16 && s->out_dtype != MLA_FP32)
+    return fail(MLA_ERR_INVALID_ARG, "out_dtype must be MLA_BF16 or MLA_FP32");
+  if (s->batch > mla::kMaxBatch) return fail(MLA_ERR_UNSUPPORTED, "batch %d > %d", s->batch, mla::kMaxBatch);
+  if (s->q_len > 8) return fail(MLA_ERR_UNSUPPORTED, "q_len %d > 8", s->q_len);
+  if (s->d_latent != 512 && s->d_latent != 256)
+    return fail(MLA_ERR_UNSUPPORTED, "d_latent %d (kernels exist for 512 and 256)", s->d_latent);
+  if (s->d_rope != 64) return fail(MLA_ERR_UNSUPPORTED, "d_rope %d (kernels exist for 64)", s->d_rope);
+  if (s->d_nope % 64 != 0 || s->d_nope > 512)
+    return fail(MLA_ERR_UNSUPPORTED, "d_nope %d (multiple of 64 up to 512)", s->d_nope);
+  if (s->d_v % 64 != 0) return fail(MLA_ERR_UNSUPPORTED, "d_v %d (multiple of 64)", s->d_v);
+  if (s->block_size % MLA_TILE_TOKENS != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "block_size %d (multiple of %d)", s->block_size, MLA_TILE_TOKENS);
+  if ((int64_t)s->batch * s->q_len > (1 << 20)) return fail(MLA_ERR_UNSUPPORTED, "batch * q_len too large");
+  return MLA_OK;
+}
+
+mla_status_t hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status_t status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: no kernel for this request";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime error";
+  }
+  return "unknown mla_status_t";
+}
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+mla_status_t mla_absorb_q(const mla_shape_t* shape, const void* q_nope, const void* w_uk, void* q_lat,
+                          hipStream_t stream) {
+  mla_status_t st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!q_nope || !w_uk || !q_lat) return fail(MLA_ERR_INVALID_ARG, "mla_absorb_q: NULL tensor");
+  if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_lat))
+    return fail(MLA_ERR_INVALID_ARG, "mla_absorb_q: tensors must be 16-byte aligned");
+  mla::HeadGemmParams p{};
+  p.a = q_nope;
+  p.w = static_cast<const uint16_t*>(w_uk);
+  p.c = q_lat;
+  p.M = shape->batch * shape->q_len;
+  p.H = shape->num_heads;
+  p.K = shape->d_nope;
+  p.N = shape->d_latent;
+  return hip_status(mla::launch_head_gemm(p, false, false, stream), "mla_absorb_q launch");
+}
+
+mla_status_t mla_decode_num_parts(const mla_shape_t* shape, int32_t* num_parts) {
+  mla_status_t st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!num_parts) return fail(MLA_ERR_INVALID_ARG, "num_parts is NULL");
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != MLA_OK) return st;
+  const int R = shape->q_len * shape->num_heads;
+  const int wgs = cus * mla::decode_wgs_per_cu(R, shape->d_latent);
+  const int G = std::max(1, wgs / mla::decode_row_groups(R));
+  *num_parts = G + shape->batch - 1;
+  return ok();
+}
+
+mla_status_t mla_decode_paged(const mla_shape_t* shape, const void* q_lat, const void* q_rope, const void* c_kv,
+                              const void* k_rope, int64_t token_stride, int64_t block_stride, const float* kv_scale,
+                              const int32_t* block_table, const int32_t* seq_lens, int32_t num_parts, float* o_part,
+                              float* lse_part, hipStream_t stream) {
+  mla_status_t st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!q_lat || !q_rope || !c_kv || !k_rope || !block_table || !seq_lens || !o_part || !lse_part)
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode_paged: NULL tensor");
+  const bool fp8 = shape->cache_dtype == MLA_FP8_E4M3;
+  if (fp8 && !kv_scale) return fail(MLA_ERR_INVALID_ARG, "mla_decode_paged: fp8 cache needs kv_scale");
+  if (!fp8 && kv_scale) return fail(MLA_ERR_INVALID_ARG, "mla_decode_paged: kv_scale given for a bf16 cache");
+  if (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(c_kv) || !aligned16(k_rope) || !aligned16(o_part))
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode_paged: tensors must be 16-byte aligned");
+  const int elem = fp8 ? 1 : 2;
+  const int64_t rope_off = static_cast<const char*>(k_rope) - static_cast<const char*>(c_kv);
+  if (token_stride <= 0 || token_stride % 16 || block_stride % 16 ||
+      block_stride < (int64_t)shape->block_size * token_stride)
+    return fail(MLA_ERR_INVALID_ARG,
+                "mla_decode_paged: token_stride/block_stride must be positive multiples of 16 with "
+                "block_stride >= block_size * token_stride");
+  if (rope_off < (int64_t)shape->d_latent * elem || rope_off + (int64_t)shape->d_rope * elem > token_stride)
+    return fail(MLA_ERR_INVALID_ARG,
+                "mla_decode_paged: k_rope must follow the latent inside the record (k_rope - c_kv = %lld bytes)",
+                (long long)rope_off);
+  if (num_parts < shape->batch)
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode_paged: num_parts %d < batch %d", num_parts, shape->batch);
+  mla::DecodeParams p{};
+  p.q_lat = static_cast<const uint16_t*>(q_lat);
+  p.q_rope = static_cast<const uint16_t*>(q_rope);
+  p.c_kv = static_cast<const char*>(c_kv);
+  p.rope_off = rope_off;
+  p.token_stride = token_stride;
+  p.block_stride = block_stride;
+  p.kv_scale = kv_scale;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.bt_stride = shape->max_blocks_per_seq;
+  p.B = shape->batch;
+  p.H = shape->num_heads;
+  p.S = shape->q_len;
+  p.R = shape->q_len * shape->num_heads;
+  p.RG = mla::decode_row_groups(p.R);
+  p.G = num_parts - shape->batch + 1;
+  p.block_size = shape->block_size;
+  p.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  if ((int64_t)p.G * p.RG > (int64_t)1 << 30) return fail(MLA_ERR_UNSUPPORTED, "too many decode work-groups");
+  return hip_status(mla::launch_decode(p, shape->d_latent, fp8, stream), "mla_decode_paged launch");
+}
+
+mla_status_t mla_combine_lse(const mla_shape_t* shape, int32_t num_parts, const float* o_part, const float* lse_part,
+                             const int32_t* seq_lens, float* o_lat, float* lse, hipStream_t stream) {
+  mla_status_t st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!o_part || !lse_part || !seq_lens || !o_lat || !lse)
+    return fail(MLA_ERR_INVALID_ARG, "mla_combine_lse: NULL tensor");
+  if (!aligned16(o_part) || !aligned16(o_lat))
+    return fail(MLA_ERR_INVALID_ARG, "mla_combine_lse: o_part and o_lat must be 16-byte aligned");
+  if (num_parts < shape->batch)
+    return fail(MLA_ERR_INVALID_ARG, "mla_combine_lse: num_parts %d < batch %d", num_parts, shape->batch);
+  mla::CombineParams p{};
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.seq_lens = seq_lens;
+  p.B = shape->batch;
+  p.R = shape->q_len * shape->num_heads;
+  p.G = num_parts - shape->batch + 1;
+  p.DC = shape->d_latent;
+  p.o_lat = o_lat;
+  p.lse = lse;
+  return hip_status(mla::launch_combine(p, stream), "mla_combine_lse launch");
+}
+
+mla_status_t mla_up_v(const mla_shape_t* shape, const float* o_lat, const void* w_uv, void* out,
+                      hipStream_t stream) {
+  mla_status_t st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!o_lat || !w_uv || !out) return fail(MLA_ERR_INVALID_ARG, "mla_up_v: NULL tensor");
+  if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out))
+    return fail(MLA_ERR_INVALID_ARG, "mla_up_v: tensors must be 16-byte aligned");
+  mla::HeadGemmParams p{};
+  p.a = o_lat;
+  p.w = static_cast<const uint16_t*>(w_uv);
+  p.c = out;
+  p.M = shape->batch * shape->q_len;
+  p.H = shape->num_heads;
+  p.K = shape->d_latent;
+  p.N = shape->d_v;
+  return hip_status(mla::launch_head_gemm(p, true, shape->out_dtype == MLA_FP32, stream), "mla_up_v launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// Device-side helpers shared by the gfx950 kernels of the absorbed-MLA library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+constexpr int kWave = 64;
+constexpr int kTile = 32;  // tokens per decode tile (the M extent of one 32x32 MFMA)
+
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).
+// Lane l holds A[l%32][8*(l/32) .. +8], B[8*(l/32) .. +8][l%32] and
+// D[8*(i/4) + 4*(l/32) + i%4][l%32] in accumulator register i.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read of 4 bf16: within each 16-lane group, lane i receives
+// element (i % 4) of the 8-byte words addressed by lanes 4*j + i/4, j = 0..3.
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(lds_void_ptr)(p));
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void_ptr)(p);
+}
+
+// 16-byte global -> LDS copy without passing through VGPRs: lane i reads
+// base + voff_i (base wave-uniform, voff_i a 32-bit byte offset) and the 64
+// lanes write consecutive 16-byte slots starting at LDS offset `lds`
+// (wave-uniform).  Issued from inline asm so that the compiler does not put a
+// full vmcnt(0) wait in front of every LDS read; completion is tracked by
+// hand with vm_wait<N>().  M0 is saved and restored around the load.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "s"(lds)
+      : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)v[i];
+  return r;
+}
+
+__device__ __forceinline__ float wave_max_pair(float x) {
+  // max over lanes l and l ^ 32
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+// XOR swizzle of the 16-byte granules of one cache record in LDS: token t's
+// granule g is stored at position g ^ swz(t).  Eight consecutive tokens map a
+// granule to eight distinct bank groups (the K-operand reads), and four
+// consecutive aligned tokens map an even/odd granule pair to eight distinct
+// bank groups (the transposing V-operand reads).
+__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+
+// Sequence tile bookkeeping shared by the decode and combine kernels: the
+// prefix sum cu[0..B] of ceil(seq_len / kTile) over the batch, built in LDS by
+// one wave.  Returns cu[B].
+__device__ inline int build_tile_prefix(const int32_t* __restrict__ seq_lens, int B, int* cu, int lane) {
+  int run = 0;
+  if (lane == 0) cu[0] = 0;
+  for (int base = 0; base < B; base += kWave) {
+    int i = base + lane;
+    int n = 0;
+    if (i < B) {
+      int L = seq_lens[i];
+      n = L > 0 ? (L + kTile - 1) / kTile : 0;
+    }
+    int x = n;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (i < B) cu[i + 1] = run + x;
+    run += __shfl(x, kWave - 1);
+  }
+  return run;
+}
+
+}  // namespace mla

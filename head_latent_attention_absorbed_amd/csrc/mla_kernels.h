@@ -1,0 +1,61 @@
+// Host-visible parameter blocks and launchers of the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Largest batch the decode/combine kernels accept (their tile prefix sums live in LDS).
+constexpr int kMaxBatch = 1024;
+
+struct DecodeParams {
+  const uint16_t* q_lat;     // bf16 [B, S, H, DC]
+  const uint16_t* q_rope;    // bf16 [B, S, H, 64]
+  const char* c_kv;          // page 0 slot 0 of the latent part
+  int64_t rope_off;          // bytes from a token's latent to its RoPE key
+  int64_t token_stride;      // bytes between consecutive slots of a page
+  int64_t block_stride;      // bytes between consecutive pages
+  const float* kv_scale;     // fp8 only: [pages][block_size]
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int32_t bt_stride;         // entries per block_table row
+  int32_t B, H, S, R;        // batch, heads, query tokens, rows = S * H
+  int32_t RG;                // row groups (work-groups sharing one token range)
+  int32_t G;                 // token parts
+  int32_t block_size;
+  float scale_log2;          // softmax_scale * log2(e)
+  float* o_part;             // fp32 [parts, R, DC]
+  float* lse_part;           // fp32 [parts, R]
+};
+
+// Waves per work-group and row groups the decode uses for R rows.
+int decode_waves(int R);
+int decode_row_groups(int R);
+// Work-groups of one row group the device runs at once (token parts).
+int decode_wgs_per_cu(int R, int d_latent);
+
+hipError_t launch_decode(const DecodeParams& p, int d_latent, bool fp8, hipStream_t stream);
+
+struct CombineParams {
+  const float* o_part;
+  const float* lse_part;
+  const int32_t* seq_lens;
+  int32_t B, R, G, DC;
+  float* o_lat;              // fp32 [B, R, DC]
+  float* lse;                // fp32 [B, R]
+};
+
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+
+// Per-head product C[m, h, :] = A[m, h, :] . W[h]  (A: [M, H, K], W: [H, K, N], C: [M, H, N]).
+struct HeadGemmParams {
+  const void* a;             // bf16 or fp32
+  const uint16_t* w;         // bf16
+  void* c;                   // bf16 or fp32
+  int32_t M, H, K, N;
+};
+
+hipError_t launch_head_gemm(const HeadGemmParams& p, bool a_fp32, bool c_fp32, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,109 @@
+"""One decode step on device: the four C-ABI calls in order on one stream.
+
+``DecodeStep`` holds device copies of a workload's inputs (torch tensors used
+as plain device buffers), allocates the intermediate and output buffers, and
+issues mla_absorb_q -> mla_decode_paged -> mla_combine_lse -> mla_up_v.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .binding import (
+    MLA_BF16, MLA_FP8_E4M3, MLA_FP32, MLA_TILE_TOKENS, MlaShape,
+    mla_absorb_q, mla_decode_num_parts, mla_decode_paged, mla_combine_lse, mla_up_v,
+)
+
+
+def split_plan(seq_lens, num_parts: int, tile: int = MLA_TILE_TOKENS):
+    """The documented split plan of mla_decode_paged: a list of
+    (slot, sequence, first position, end position) for every partial written."""
+    lens = [int(x) for x in seq_lens]
+    B = len(lens)
+    n = [(L + tile - 1) // tile if L > 0 else 0 for L in lens]
+    cu = [0]
+    for x in n:
+        cu.append(cu[-1] + x)
+    N = cu[-1]
+    G = num_parts - B + 1
+    if N == 0:
+        return []
+    W = (N + G - 1) // G
+    plan = []
+    for b in range(B):
+        if n[b] == 0:
+            continue
+        for g in range(cu[b] // W, (cu[b + 1] - 1) // W + 1):
+            lo = max(cu[b], g * W) - cu[b]
+            hi = min(cu[b + 1], (g + 1) * W) - cu[b]
+            plan.append((b + g, b, lo * tile, min(hi * tile, lens[b])))
+    return plan
+
+
+def _dev_bits(torch, arr: np.ndarray, device, dtype):
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(dtype)
+    return torch.from_numpy(a).to(device)
+
+
+class DecodeStep:
+    def __init__(self, inputs: dict, device: str = "cuda", num_parts: int | None = None):
+        import torch
+
+        self.torch = torch
+        w = inputs["workload"]
+        self.workload = w
+        fp8 = w.cache_dtype == "fp8_e4m3"
+        self.shape = MlaShape.make(
+            batch=w.batch, num_heads=w.heads, q_len=w.q_len, d_latent=w.d_latent, d_nope=w.d_nope,
+            d_rope=w.d_rope, d_v=w.d_v, block_size=w.block_size, max_blocks_per_seq=w.max_blocks_per_seq,
+            softmax_scale=float(inputs["softmax_scale"]), cache_dtype=MLA_FP8_E4M3 if fp8 else MLA_BF16,
+            out_dtype=MLA_FP32 if w.out_dtype == "fp32" else MLA_BF16)
+        bf16 = torch.bfloat16
+        self.q_nope = _dev_bits(torch, inputs["q_nope"], device, bf16)
+        self.q_rope = _dev_bits(torch, inputs["q_rope"], device, bf16)
+        self.w_uk = _dev_bits(torch, inputs["w_uk"], device, bf16)
+        self.w_uv = _dev_bits(torch, inputs["w_uv"], device, bf16)
+        self.cache = _dev_bits(torch, inputs["cache"], device, bf16)
+        self.kv_scale = None if inputs["kv_scale"] is None else torch.from_numpy(inputs["kv_scale"]).to(device)
+        self.block_table = torch.from_numpy(inputs["block_table"]).to(device)
+        self.seq_lens = torch.from_numpy(inputs["seq_lens"]).to(device)
+        self.elem = 1 if fp8 else 2
+        self.token_stride = w.record_elems * self.elem
+        self.block_stride = w.block_size * self.token_stride
+        self.num_parts = num_parts if num_parts is not None else mla_decode_num_parts(self.shape)
+        B, S, H, DC = w.batch, w.q_len, w.heads, w.d_latent
+        R = S * H
+        f32 = torch.float32
+        self.q_lat = torch.empty((B, S, H, DC), dtype=bf16, device=device)
+        self.o_part = torch.empty((self.num_parts, R, DC), dtype=f32, device=device)
+        self.lse_part = torch.empty((self.num_parts, R), dtype=f32, device=device)
+        self.o_lat = torch.empty((B, S, H, DC), dtype=f32, device=device)
+        self.lse = torch.empty((B, S, H), dtype=f32, device=device)
+        self.out = torch.empty((B, S, H, w.d_v), dtype=f32 if w.out_dtype == "fp32" else bf16, device=device)
+
+    def absorb(self, stream=None):
+        mla_absorb_q(self.shape, self.q_nope, self.w_uk, self.q_lat, stream)
+
+    def decode(self, stream=None, cache=None, kv_scale=None):
+        cache = self.cache if cache is None else cache
+        kv_scale = self.kv_scale if kv_scale is None else kv_scale
+        base = cache.data_ptr()
+        mla_decode_paged(self.shape, self.q_lat, self.q_rope, base, base + self.workload.d_latent * self.elem,
+                         self.token_stride, self.block_stride, kv_scale, self.block_table, self.seq_lens,
+                         self.num_parts, self.o_part, self.lse_part, stream)
+
+    def combine(self, stream=None):
+        mla_combine_lse(self.shape, self.num_parts, self.o_part, self.lse_part, self.seq_lens, self.o_lat, self.lse,
+                        stream)
+
+    def up(self, stream=None):
+        mla_up_v(self.shape, self.o_lat, self.w_uv, self.out, stream)
+
+    def run(self, stream=None, cache=None, kv_scale=None):
+        """The whole step: absorb, split-K decode, LSE combine, up-projection."""
+        self.absorb(stream)
+        self.decode(stream, cache, kv_scale)
+        self.combine(stream)
+        self.up(stream)
+        return self.out

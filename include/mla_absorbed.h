@@ -1,0 +1,187 @@
+/*
+ * mla_absorbed.h -- C ABI of the MI355X (gfx950) absorbed Multi-Head Latent
+ * Attention decode library (libmla_absorbed.so).
+ *
+ * One decode step of one attention layer is four calls, all enqueued in order
+ * on the caller's HIP stream:
+ *
+ *   mla_absorb_q      q_lat = q_nope . W_UK[h]              (per head)
+ *   mla_decode_paged  split-K attention of [q_lat; q_rope] over the paged
+ *                     latent cache, one normalised partial + lse per split
+ *   mla_combine_lse   log-sum-exp merge of the splits -> o_lat, lse
+ *   mla_up_v          out = o_lat . W_UV[h]                  (per head)
+ *
+ * What the method is, and where the pages say it:
+ *  - Only one low-rank latent c_KV per token is cached, next to one decoupled
+ *    RoPE key that every head shares (TPLA abstract, taxoreview pages for
+ *    dblp:408/6122 and dblp:256/5536-3; TransMLA review page on pith.science,
+ *    core_discovery).
+ *  - The RoPE-free key up-projection W_UK is folded into the query ("absorb"),
+ *    so attention runs in the latent space and the cache is never expanded
+ *    (TransMLA abstracts on the taxoreview pages; TransMLA review page,
+ *    key_machinery; the Eq. (26) interaction matrix in
+ *    referee_report.major_comments[0]).
+ *  - With the absorb, all heads read the same cache record: the MQA form of
+ *    MLA (GQLA abstract, "GQA-to-MLA" Daily Papers listing).
+ *  - The value up-projection W_UV is applied after attention (early TransMLA
+ *    abstract on that listing).
+ *  - Decode is bound by memory traffic (TPLA and CLOVER abstracts; the OI/CF
+ *    abstract on the Daily Papers listing), and the softmax is computed online
+ *    (BLASST abstract on that listing) so that splits of the token axis can be
+ *    merged exactly by their log-sum-exp.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers, owned by the caller; the library
+ *    never allocates, frees or synchronises, and keeps no per-call state.
+ *    Every call only enqueues work on `stream` (0 = the null stream).
+ *  - Tensors are dense row-major in the shapes given, bf16 as raw IEEE
+ *    bfloat16, fp8 as OCP E4M3 (e4m3fn: bias 7, max 448, no infinities).
+ *  - The shape structure is read on the host during the call only.
+ *  - Errors detectable on the host (null pointers, bad sizes, misalignment,
+ *    shapes without a kernel) return a status before anything is enqueued;
+ *    a failed launch returns MLA_ERR_HIP.  Device-side faults surface at the
+ *    caller's next synchronisation.  mla_last_error() gives a message for the
+ *    calling thread's most recent failure.  Calls are thread-safe.
+ *  - Queries: the q_len = S_q tokens of a step are the LAST S_q positions of
+ *    each sequence; seq_lens[b] counts cached tokens including them.  Query s
+ *    sees positions t <= seq_lens[b] - S_q + s (causal among themselves).  A
+ *    query row that sees no position (seq_lens[b] == 0 for an idle batch slot)
+ *    yields out = 0 and lse = -inf.
+ *  - lse is the natural-log log-sum-exp of the scaled scores.
+ */
+#ifndef MLA_ABSORBED_H
+#define MLA_ABSORBED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad stride or alignment  */
+  MLA_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for                 */
+  MLA_ERR_HIP = 3          /* a HIP runtime call (device query or launch) failed         */
+} mla_status_t;
+
+typedef enum { MLA_BF16 = 0, MLA_FP8_E4M3 = 1, MLA_FP32 = 2 } mla_dtype_t;
+
+/* Tokens per decode tile; the split plan below is counted in tiles. */
+#define MLA_TILE_TOKENS 32
+
+typedef struct {
+  int32_t batch;              /* B >= 1                                          */
+  int32_t num_heads;          /* H >= 1                                          */
+  int32_t q_len;              /* S_q, 1..8                                       */
+  int32_t d_nope;             /* query/key RoPE-free width; 128                  */
+  int32_t d_rope;             /* decoupled RoPE width; 64                        */
+  int32_t d_latent;           /* latent rank d_c; 512 or 256                     */
+  int32_t d_v;                /* value width; 128                                */
+  int32_t block_size;         /* tokens per cache page; 64                       */
+  int32_t max_blocks_per_seq; /* row stride (entries) of block_table, >= 1       */
+  float softmax_scale;        /* multiplies q.k; usually 1/sqrt(d_nope + d_rope) */
+  mla_dtype_t cache_dtype;    /* MLA_BF16 or MLA_FP8_E4M3                        */
+  mla_dtype_t out_dtype;      /* MLA_BF16 or MLA_FP32 (dtype of `out`)           */
+} mla_shape_t;
+
+/*
+ * mla_absorb_q -- fold W_UK into the query.
+ *   q_lat[b,s,h,:] = q_nope[b,s,h,:] . W_UK[h]        (fp32 accumulation, bf16 RNE result)
+ *   q_nope  bf16 [B, S_q, H, d_nope]
+ *   w_uk    bf16 [H, d_nope, d_latent]     (k_nope of head h = W_UK[h] . c)
+ *   q_lat   bf16 [B, S_q, H, d_latent]     (written)
+ * Pointers 16-byte aligned.
+ */
+mla_status_t mla_absorb_q(const mla_shape_t* shape, const void* q_nope, const void* w_uk, void* q_lat,
+                          hipStream_t stream);
+
+/*
+ * mla_decode_num_parts -- host query: how many partial slots mla_decode_paged
+ * should use on the current device (o_part / lse_part are sized by it).  The
+ * value is (token parts) + B - 1, where the token-part count fills the
+ * device's compute units.  Any value >= B may be passed to the decode and
+ * combine calls instead; it only changes how the token axis is split.
+ */
+mla_status_t mla_decode_num_parts(const mla_shape_t* shape, int32_t* num_parts);
+
+/*
+ * mla_decode_paged -- split-K attention over the paged latent cache.
+ *
+ * Cache: page p, slot j (0 <= j < block_size) holds one token's record.
+ *   latent  of that token at  (const char*)c_kv   + p*block_stride + j*token_stride
+ *   RoPE key of that token at (const char*)k_rope + p*block_stride + j*token_stride
+ *   element type: bf16 (MLA_BF16) or e4m3 (MLA_FP8_E4M3), d_latent resp. d_rope values.
+ * The two parts must share the record: 0 < k_rope - c_kv, the latent ends at
+ * or before the RoPE key, and the RoPE key ends within token_stride.  The
+ * native layout is the interleaved record [c_KV | k_rope] of 576 values
+ * (k_rope = c_kv + d_latent elements, token_stride = 576 * elem,
+ * block_stride = block_size * token_stride).  c_kv, k_rope, token_stride and
+ * block_stride must be multiples of 16 bytes.
+ * kv_scale (fp8 only, else NULL): fp32 [pages][block_size], the dequantisation
+ *   scale of each token, applied to its whole record.
+ * block_table int32 [B, max_blocks_per_seq]: logical block i of sequence b is
+ *   page block_table[b][i]; only entries i < ceil(seq_lens[b] / block_size) are read.
+ * seq_lens int32 [B]: tokens in each sequence (0 = idle slot, else >= S_q).
+ *   Cache slots at positions >= seq_lens[b] are never used in a way that can
+ *   change results (they may hold NaN).
+ * q_lat bf16 [B, S_q, H, d_latent] (from mla_absorb_q), q_rope bf16 [B, S_q, H, d_rope].
+ *
+ * Split plan (so that callers and tests can reproduce it; R = S_q * H rows,
+ * row r = s*H + h):
+ *   n_b = ceil(L_b / MLA_TILE_TOKENS), cu_0 = 0, cu_{b+1} = cu_b + n_b, N = cu_B
+ *   G = num_parts - B + 1 token parts, W = ceil(N / G) tiles per part
+ *   part g covers global tiles [g*W, min((g+1)*W, N)); for each sequence b it
+ *   touches it writes slot (b + g): the partial over positions
+ *   [max(cu_b, g*W) - cu_b, min(cu_{b+1}, (g+1)*W) - cu_b) * MLA_TILE_TOKENS,
+ *   clipped to what each query may see.
+ * o_part   fp32 [num_parts, R, d_latent]: sum_t p_t c_t, normalised within the split
+ * lse_part fp32 [num_parts, R]: the split's log-sum-exp (-inf if it sees nothing)
+ * Slots that no (sequence, part) pair maps to are left untouched.
+ */
+mla_status_t mla_decode_paged(const mla_shape_t* shape, const void* q_lat, const void* q_rope,
+                              const void* c_kv, const void* k_rope, int64_t token_stride,
+                              int64_t block_stride, const float* kv_scale, const int32_t* block_table,
+                              const int32_t* seq_lens, int32_t num_parts, float* o_part,
+                              float* lse_part, hipStream_t stream);
+
+/*
+ * mla_combine_lse -- merge the splits written by mla_decode_paged (same
+ * shape, num_parts and seq_lens):
+ *   lse[b,r]   = log sum_k exp(lse_part[k,r])
+ *   o_lat[b,r] = sum_k exp(lse_part[k,r] - lse[b,r]) o_part[k,r]
+ * over sequence b's slots; splits with lse = -inf weigh nothing; a row with
+ * no visible position gets o_lat = 0 and lse = -inf.
+ *   o_lat fp32 [B, S_q, H, d_latent], lse fp32 [B, S_q, H] (written)
+ */
+mla_status_t mla_combine_lse(const mla_shape_t* shape, int32_t num_parts, const float* o_part,
+                             const float* lse_part, const int32_t* seq_lens, float* o_lat, float* lse,
+                             hipStream_t stream);
+
+/*
+ * mla_up_v -- value up-projection of the latent output.
+ *   out[b,s,h,:] = o_lat[b,s,h,:] . W_UV[h]           (fp32 accumulation)
+ *   o_lat fp32 [B, S_q, H, d_latent]
+ *   w_uv  bf16 [H, d_latent, d_v]
+ *   out   [B, S_q, H, d_v] in shape->out_dtype (bf16 RNE or fp32) (written)
+ * For a latent-split shard (d_latent = 256 of a wider latent) the fp32 out
+ * together with the lse from mla_combine_lse is that shard's result for an
+ * external merge.
+ */
+mla_status_t mla_up_v(const mla_shape_t* shape, const float* o_lat, const void* w_uv, void* out,
+                      hipStream_t stream);
+
+/* Static description of a status code. */
+const char* mla_status_string(mla_status_t status);
+
+/* Message for the calling thread's most recent non-OK status ("" if none). */
+const char* mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_ABSORBED_H */

@@ -92,10 +92,11 @@ def reconstruct_kv(C: np.ndarray, KR: np.ndarray, w_uk: np.ndarray, w_uv: np.nda
     """Explicit per-head keys and values for heads ``w_uk.shape[0]``:
     K[h, t] = [W_UK[h] c_t ; k_rope_t]  (d_n + d_r),  V[h, t] = c_t^T W_UV[h]  (d_v)."""
     H, dn, dc = w_uk.shape
+    dv = w_uv.shape[2]
     L = C.shape[0]
     k_nope = (C @ w_uk.reshape(H * dn, dc).T).reshape(L, H, dn).transpose(1, 0, 2)
     k = np.concatenate([k_nope, np.broadcast_to(KR, (H,) + KR.shape)], axis=2)
-    v = (C @ w_uv.transpose(1, 0, 2).reshape(dc, -1)).reshape(L, H, -1).transpose(1, 0, 2)
+    v = (C @ w_uv.transpose(1, 0, 2).reshape(dc, H * dv)).reshape(L, H, dv).transpose(1, 0, 2)
     return k, v
 
 

@@ -1,0 +1,123 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+and rejects bad arguments on the host before touching the device."""
+import ctypes
+import math
+import os
+import subprocess
+
+import pytest
+
+import head_latent_attention_absorbed_amd as mla
+from head_latent_attention_absorbed_amd import MlaShape, split_plan
+
+
+def _lib():
+    if not os.path.exists(mla.library_path):
+        pytest.fail("libmla_absorbed.so is not built (run __graft_entry__.build())")
+    return mla.library()
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib()
+    declared = mla.exported_symbols()
+    assert set(declared) >= {"mla_absorb_q", "mla_decode_num_parts", "mla_decode_paged", "mla_combine_lse",
+                             "mla_up_v", "mla_status_string", "mla_last_error"}
+    out = subprocess.run(["nm", "-D", "--defined-only", mla.library_path], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared:
+        assert name in exported, f"{name} declared in the header but not exported"
+        assert hasattr(lib, name)
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(MlaShape) == 12 * 4
+    assert MlaShape.softmax_scale.offset == 36
+
+
+def _shape(**kw):
+    base = dict(batch=2, num_heads=16, q_len=1, d_latent=512, max_blocks_per_seq=4, softmax_scale=192 ** -0.5)
+    base.update(kw)
+    return MlaShape.make(**base)
+
+
+FAKE = 1 << 40  # a 16-byte aligned address; never dereferenced by failing calls
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(num_heads=-1), mla.MLA_ERR_INVALID_ARG),
+    (dict(softmax_scale=math.inf), mla.MLA_ERR_INVALID_ARG),
+    (dict(cache_dtype=7), mla.MLA_ERR_INVALID_ARG),
+    (dict(out_dtype=mla.MLA_FP8_E4M3), mla.MLA_ERR_INVALID_ARG),
+    (dict(d_latent=384), mla.MLA_ERR_UNSUPPORTED),
+    (dict(d_rope=32), mla.MLA_ERR_UNSUPPORTED),
+    (dict(block_size=48), mla.MLA_ERR_UNSUPPORTED),
+    (dict(q_len=9), mla.MLA_ERR_UNSUPPORTED),
+    (dict(batch=4096), mla.MLA_ERR_UNSUPPORTED),
+])
+def test_shape_validation(kw, status):
+    lib = _lib()
+    sh = _shape(**kw)
+    st = lib.mla_absorb_q(ctypes.byref(sh), FAKE, FAKE, FAKE, None)
+    assert st == status, mla.mla_last_error()
+    assert mla.mla_last_error() != ""
+
+
+def test_null_and_alignment_checks():
+    lib = _lib()
+    sh = _shape()
+    assert lib.mla_absorb_q(None, FAKE, FAKE, FAKE, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(ctypes.byref(sh), None, FAKE, FAKE, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(ctypes.byref(sh), FAKE + 2, FAKE, FAKE, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_up_v(ctypes.byref(sh), FAKE, None, FAKE, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_combine_lse(ctypes.byref(sh), 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == mla.MLA_ERR_INVALID_ARG
+
+
+def _decode(sh, **kw):
+    lib = _lib()
+    a = dict(q_lat=FAKE, q_rope=FAKE, c_kv=FAKE, k_rope=FAKE + 1024, token_stride=1152, block_stride=64 * 1152,
+             kv_scale=None, block_table=FAKE, seq_lens=FAKE, num_parts=8, o_part=FAKE, lse_part=FAKE)
+    a.update(kw)
+    return lib.mla_decode_paged(ctypes.byref(sh), a["q_lat"], a["q_rope"], a["c_kv"], a["k_rope"],
+                                a["token_stride"], a["block_stride"], a["kv_scale"], a["block_table"],
+                                a["seq_lens"], a["num_parts"], a["o_part"], a["lse_part"], None)
+
+
+def test_decode_argument_checks():
+    sh = _shape()
+    assert _decode(sh, block_table=None) == mla.MLA_ERR_INVALID_ARG
+    assert _decode(sh, kv_scale=FAKE) == mla.MLA_ERR_INVALID_ARG                 # scale with a bf16 cache
+    assert _decode(_shape(cache_dtype=mla.MLA_FP8_E4M3), k_rope=FAKE + 512, token_stride=576,
+                   block_stride=64 * 576) == mla.MLA_ERR_INVALID_ARG             # fp8 needs kv_scale
+    assert _decode(sh, token_stride=1000) == mla.MLA_ERR_INVALID_ARG             # not a multiple of 16
+    assert _decode(sh, block_stride=32 * 1152) == mla.MLA_ERR_INVALID_ARG        # page smaller than 64 records
+    assert _decode(sh, k_rope=FAKE + 512) == mla.MLA_ERR_INVALID_ARG             # RoPE key overlaps the latent
+    assert _decode(sh, k_rope=FAKE + 1152) == mla.MLA_ERR_INVALID_ARG            # RoPE key past the record
+    assert _decode(sh, num_parts=1) == mla.MLA_ERR_INVALID_ARG                   # fewer parts than sequences
+    assert _decode(sh, q_lat=FAKE + 8) == mla.MLA_ERR_INVALID_ARG                # misaligned
+
+
+def test_status_strings():
+    _lib()
+    assert mla.mla_status_string(0) == "MLA_OK"
+    for st in (1, 2, 3):
+        assert mla.mla_status_string(st).startswith("MLA_ERR")
+
+
+def test_split_plan_covers_every_tile_once():
+    lens = [0, 1, 31, 32, 33, 700, 0, 64]
+    for parts in (8, 9, 12, 40, 300):
+        plan = split_plan(lens, parts)
+        covered = {b: [] for b in range(len(lens))}
+        slots = set()
+        for slot, b, t0, t1 in plan:
+            assert slot not in slots and 0 <= slot < parts
+            slots.add(slot)
+            covered[b].append((t0, t1))
+        for b, L in enumerate(lens):
+            segs = sorted(covered[b])
+            pos = 0
+            for t0, t1 in segs:
+                assert t0 == pos and t1 > t0
+                pos = t1
+            assert pos == L

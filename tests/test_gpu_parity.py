@@ -1,0 +1,143 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Small cases span several tiles, ragged tails, idle batch slots, the causal
+multi-token tail, both latent widths, the e4m3 cache and several split
+counts; they compare every output element and every intermediate (absorbed
+query, each split partial, merged latent output, final output).  The full
+workloads run in the launch configuration the bench times and are compared on
+sampled sequences and heads, which the oracle computes one by one.
+"""
+import math
+import sys
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import get_workload, make_inputs, small_workload
+from gpu_helpers import compare, run_step, to_np, tolerances
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_all(inputs, st, check_partials=True):
+    w = inputs["workload"]
+    tol_abs, tol_rel = tolerances(w)
+    ref = oracle.decode(inputs)
+    # absorbed query (bf16 result of an fp32 accumulation)
+    compare("q_lat", to_np(st.q_lat), ref["q_lat"], tol_abs, tol_rel)
+    # merged latent output and lse
+    compare("o_lat", to_np(st.o_lat), ref["o_lat"], tol_abs, tol_rel)
+    compare("lse", to_np(st.lse), ref["lse"], tol_abs, tol_rel, finite_only=True)
+    compare("out", to_np(st.out), ref["out"], tol_abs, tol_rel)
+    if check_partials:
+        from head_latent_attention_absorbed_amd import split_plan
+        plan = split_plan(inputs["seq_lens"], st.num_parts)
+        o_part, lse_part = to_np(st.o_part), to_np(st.lse_part)
+        R = w.q_len * w.heads
+        values = oracle.cache_values(inputs)
+        used = set()
+        for slot, b, t0, t1 in plan:
+            o_ref, lse_ref = oracle.partial(inputs, b, t0, t1, values=values)
+            compare(f"o_part[{slot}] b={b} [{t0},{t1})", o_part[slot].reshape(w.q_len, w.heads, -1), o_ref,
+                    tol_abs, tol_rel)
+            compare(f"lse_part[{slot}]", lse_part[slot].reshape(w.q_len, w.heads), lse_ref, tol_abs, tol_rel,
+                    finite_only=True)
+            used.add(slot)
+        # slots outside the plan are never written (they still hold the NaN poison)
+        for slot in range(st.num_parts):
+            if slot not in used:
+                assert np.all(np.isnan(lse_part[slot])), f"slot {slot} written outside the plan"
+    return ref
+
+
+def _announce(name, inputs, st=None):
+    w = inputs["workload"]
+    print(f"[case] {name}: B={w.batch} H={w.heads} S_q={w.q_len} d_c={w.d_latent} cache={w.cache_dtype} "
+          f"lens={list(map(int, inputs['seq_lens']))[:8]} parts={getattr(st, 'num_parts', None)}", flush=True)
+
+
+SMALL_CASES = {
+    # the tiny workload exactly as specified
+    "tiny": get_workload("tiny"),
+    # DeepSeek-V3-like heads over ragged lengths (one token, one partial tile, multi-page)
+    "h128_ragged": small_workload("deepseek_v3", batch=3, seq_len=(1, 900), max_seq_len=1024,
+                                  forced_lens=(1, 77, 515), spare_blocks=3),
+    # 32 heads (one wave per work-group)
+    "h32": small_workload("gqa7b", batch=3, seq_len=(1, 700), max_seq_len=768, forced_lens=(129, 64, 33)),
+    # latent-split shard: d_c = 256, fp32 output
+    "dc256": small_workload("tpla_shard", batch=2, seq_len=(40, 400), max_seq_len=512, forced_lens=(40, 300)),
+    # 4-token causal tail over an e4m3 cache, 256 rows (two row groups)
+    "fp8_sq4_h64": small_workload("kimi_k2_fp8", batch=3, seq_len=(4, 300), max_seq_len=384,
+                                  forced_lens=(4, 170, 33)),
+    # 4-token tail, 16 heads (64 rows: two waves), bf16 cache
+    "bf16_sq4_h16": replace(small_workload("kimi_k2_fp8", batch=2, heads=16, seq_len=(5, 200), max_seq_len=256,
+                                           forced_lens=(5, 97)), cache_dtype="bf16"),
+    # an idle batch slot (seq_len 0) next to live ones
+    "idle_slot": small_workload("deepseek_v3", batch=3, seq_len=(50, 300), max_seq_len=320, forced_lens=(0, 65, 0)),
+    # fp8 with 32 rows (one wave) and d_c = 512
+    "fp8_h32": replace(small_workload("gqa7b", batch=2, seq_len=(3, 200), max_seq_len=256, forced_lens=(3, 161)),
+                       cache_dtype="fp8_e4m3"),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_CASES))
+def test_small_parity_default_split(name):
+    inputs = make_inputs(SMALL_CASES[name])
+    _announce(name, inputs)
+    st = run_step(inputs)
+    _check_all(inputs, st)
+
+
+@pytest.mark.parametrize("name", ["h128_ragged", "dc256", "fp8_sq4_h64", "h32"])
+@pytest.mark.parametrize("extra_parts", [0, 1, 5])
+def test_small_parity_few_splits(name, extra_parts):
+    """Few token parts: each part runs many tiles and spans sequence boundaries."""
+    inputs = make_inputs(SMALL_CASES[name])
+    B = inputs["workload"].batch
+    _announce(f"{name}+{extra_parts}", inputs)
+    st = run_step(inputs, num_parts=B + extra_parts)
+    _check_all(inputs, st)
+
+
+def test_bitwise_deterministic():
+    inputs = make_inputs(SMALL_CASES["h128_ragged"])
+    outs = []
+    for _ in range(3):
+        st = run_step(inputs)
+        outs.append((to_np(st.out), to_np(st.lse), to_np(st.o_part)))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b, equal_nan=True)
+
+
+FULL = ["tiny", "deepseek_v3", "gqa7b", "tpla_shard", "kimi_k2_fp8"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload_sampled(name):
+    """Each named workload at full size, in the launch configuration the bench
+    times; every output is checked finite and sampled (sequence, head) pairs are
+    compared with the oracle."""
+    w = get_workload(name)
+    inputs = make_inputs(w)
+    st = run_step(inputs)
+    _announce(name, inputs, st)
+    out, lse, o_lat = to_np(st.out), to_np(st.lse), to_np(st.o_lat)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    tol_abs, tol_rel = tolerances(w)
+    rng = np.random.default_rng(7)
+    bs = sorted(set([0, w.batch - 1] + rng.integers(0, w.batch, size=2).tolist()))
+    heads = sorted(set([0, w.heads - 1] + rng.integers(0, w.heads, size=4).tolist()))
+    values = oracle.cache_values(inputs)
+    got, ref = [], []
+    got_l, ref_l = [], []
+    for b in bs:
+        o_ref, l_ref, _ = oracle.decode_one(inputs, b, heads, values=values)
+        got.append(out[b][:, heads])
+        ref.append(o_ref)
+        got_l.append(lse[b][:, heads])
+        ref_l.append(l_ref)
+    compare(f"{name} out (sampled)", np.stack(got), np.stack(ref), tol_abs, tol_rel, scaled_abs=False)
+    compare(f"{name} lse (sampled)", np.stack(got_l), np.stack(ref_l), tol_abs, tol_rel)

@@ -377,6 +377,20 @@ def test_p14_causal_tail():
     check_causal_tail(oracle)
 
 
+# ------------------------------------------------------------------ idle batch slot
+
+def test_idle_slot_reads_nothing():
+    """A sequence of length 0 sees no position: output 0 and lse -inf, and the
+    other sequences of the batch are unaffected."""
+    w = tiny(batch=3, forced_lens=(0, 7, 0), q_len=2, seq_len=(5, 9))
+    inp = make_inputs(w)
+    res = oracle.decode(inp)
+    for b in (0, 2):
+        assert np.all(res["out"][b] == 0) and np.all(np.isneginf(res["lse"][b]))
+    one = oracle.decode(inp, batches=[1])
+    assert np.array_equal(one["out"][0], res["out"][1])
+
+
 # ------------------------------------------------------------------ P15 record size
 
 def test_p15_record_size_against_printed_figures():
