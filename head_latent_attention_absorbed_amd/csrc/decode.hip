@@ -21,6 +21,12 @@
 // register-staged e4m3->bf16 decode for fp8).  The token axis of the whole
 // batch is cut into G equal parts; each (part, sequence) pair writes one
 // normalised partial and its log-sum-exp.
+//
+// LDS tile layout (granule-major): row g (512 bytes) holds 16-byte granule g
+// (8 bf16 values) of all 32 tokens, token t at slot t ^ (4 * (g & 1)).  One
+// DMA instruction fills two rows; the K-operand reads of eight lanes cover one
+// contiguous 128-byte run, and the sixteen lanes of a transposing V read hit
+// 32 distinct banks.
 #include "mla_device.h"
 #include "mla_kernels.h"
 
@@ -29,6 +35,7 @@ namespace {
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRebase = 8.0f;  // log2 of the largest unnormalised weight kept between re-bases
+constexpr int kRow = kTile * 16;  // bytes of one granule row of a tile
 
 __device__ __forceinline__ void block_sync() {
   // Work-group barrier for LDS hand-offs: waits for this wave's LDS traffic,
@@ -66,92 +73,89 @@ template <int DC>
 struct Geo {
   static constexpr int GC = DC * 2 / 16;         // latent granules per token (bf16)
   static constexpr int GR = 64 * 2 / 16;         // RoPE granules per token (d_rope = 64)
-  static constexpr int GPT = GC + GR;            // granules per token in LDS
-  static constexpr int TILE_BYTES = kTile * GPT * 16;
+  static constexpr int GPT = GC + GR;            // granule rows per tile
+  static constexpr int TILE_BYTES = GPT * kRow;
   static constexpr int KS = (DC + 64) / 16;      // k-steps of the score product
   static constexpr int NB = DC / 32;             // 32-column blocks of O^T
 };
 
-// bf16 tile: direct DMA of the 16-byte granules into the swizzled LDS layout.
-// Slot s of the tile (LDS byte 16*s) holds granule (s % GPT) ^ swz(t) of token
-// t = s / GPT; a lane's NI slots are fixed, so their byte offsets inside a
-// 32-token run of a page are computed once.  A tile always copies all 32
-// slots of its run (they lie inside one allocated page); rows past the
-// sequence length are zeroed in LDS afterwards (zero_tail), so stale or NaN
-// slot contents never reach the P.V product.
+// A lane id the compiler cannot see through, so that lane-derived constants
+// are recomputed where they are used instead of being kept live (and spilled)
+// across the whole kernel.
+__device__ __forceinline__ int opaque_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// The token a lane moves in every tile-load instruction: slot lane % 32 of
+// row 2m + lane / 32 holds token (lane % 32) ^ (4 * (lane / 32)).
+__device__ __forceinline__ int load_token(int lane) { return (lane & 31) ^ ((lane >> 5) << 2); }
+
+// Byte offset of granule row pair (g0, g0+1) inside a cache record (GB-byte
+// granules: 16 for bf16, 8 for e4m3).  g0 is even, so a pair never straddles
+// the latent and the RoPE key.
+template <int DC, int GB>
+__device__ __forceinline__ int64_t granule_offset(const DecodeParams& p, int g0) {
+  return g0 < Geo<DC>::GC ? (int64_t)g0 * GB : p.rope_off + (int64_t)(g0 - Geo<DC>::GC) * GB;
+}
+
+// Issue this wave's DMA loads of one tile.  `run` is the address of the
+// tile's first token (page base + slot offset); `lane_off` is this lane's
+// load_token times the token stride, plus 16 bytes on the odd row of a pair.
 template <int DC, int NW>
-struct DmaPlan {
-  using Gm = Geo<DC>;
-  static constexpr int NI = kTile * Gm::GPT / (kWave * NW);
-  uint32_t off[NI];
-
-  __device__ __forceinline__ void init(const DecodeParams& p, int w, int lane) {
+__device__ __forceinline__ void issue_tile_dma(const DecodeParams& p, const char* run, uint32_t lane_off,
+                                               uint32_t buf_lds, int w) {
+  constexpr int NI = Geo<DC>::GPT / (2 * NW);
 #pragma unroll
-    for (int q = 0; q < NI; ++q) {
-      const int s = (q * NW + w) * kWave + lane;
-      const int t = s / Gm::GPT;
-      const int gr = (s % Gm::GPT) ^ swz(t);
-      off[q] = (uint32_t)t * (uint32_t)p.token_stride +
-               (gr < Gm::GC ? (uint32_t)gr * 16u : (uint32_t)p.rope_off + (uint32_t)(gr - Gm::GC) * 16u);
-    }
+  for (int q = 0; q < NI; ++q) {
+    const int g0 = 2 * (q * NW + w);
+    lds_dma16(run + granule_offset<DC, 16>(p, g0), lane_off, uniform(buf_lds + (q * NW + w) * 1024));
   }
-  // Issue this wave's NI loads of tile j of sequence b into the LDS buffer at buf_lds.
-  __device__ __forceinline__ void issue(const DecodeParams& p, const int32_t* __restrict__ block_table, int b, int j,
-                                        uint32_t buf_lds, int w) const {
-    b = uniform(b);
-    j = uniform(j);
-    const int pos0 = j * kTile;
-    const int page = block_table[(int64_t)b * p.bt_stride + pos0 / p.block_size];
-    const char* base = p.c_kv + (int64_t)page * p.block_stride + (int64_t)(pos0 % p.block_size) * p.token_stride;
-#pragma unroll
-    for (int q = 0; q < NI; ++q) lds_dma16(base, off[q], uniform(buf_lds + (q * NW + w) * 1024));
-  }
-};
+}
 
-// Zero the LDS rows of tokens nv..31 of a tile (the last, partial tile of a sequence).
+// Zero the slots of tokens nv..31 of a tile (the last, partial tile of a
+// sequence): their DMA'd contents are whatever the page held past the length.
 template <int DC, int NW>
 __device__ __forceinline__ void zero_tail(char* tb, int nv, int tid) {
-  constexpr int ROW = Geo<DC>::GPT * 16;
-  for (int o = nv * ROW + tid * 16; o < kTile * ROW; o += NW * kWave * 16) *(uint4*)(tb + o) = uint4{0, 0, 0, 0};
+  for (int i = tid; i < Geo<DC>::GPT * kTile; i += NW * kWave) {
+    const int g = i >> 5, slot = i & 31;
+    if ((slot ^ ((g & 1) << 2)) >= nv) *(uint4*)(tb + g * kRow + slot * 16) = uint4{0, 0, 0, 0};
+  }
 }
 
 // fp8 tile: 8 e4m3 bytes per bf16 granule, loaded into registers, decoded
-// exactly (every e4m3 value is a bf16 value) and written to the same layout.
+// exactly (every e4m3 value is a bf16 value) and written to the same layout;
+// tokens past the length are written as zeros.
 template <int DC, int NW>
 struct Fp8Stage {
-  using Gm = Geo<DC>;
-  static constexpr int NI = kTile * Gm::GPT / (kWave * NW);  // granules per lane
-  static constexpr int CH = NI < 9 ? NI : 9;                 // granules kept in flight
+  static constexpr int NI = Geo<DC>::GPT / (2 * NW);  // granules per lane
+  static constexpr int CH = NI < 9 ? NI : 9;          // granules kept in flight
   uint2 v[CH];
-  float sc;
 
-  __device__ __forceinline__ void load_chunk(const DecodeParams& p, const char* pbase, int nv, int c0, int w,
-                                             int lane) {
+  __device__ __forceinline__ void load_chunk(const DecodeParams& p, const char* run, uint32_t lane_off8, int c0,
+                                             int w) {
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
       const int qq = c0 + q;
       if (qq < NI) {
-        const int s = (qq * NW + w) * kWave + lane;
-        const int t = s / Gm::GPT;
-        const int gr = (s % Gm::GPT) ^ swz(t);
-        const int ts = min(t, nv - 1);
-        const int64_t off = (int64_t)ts * p.token_stride + (gr < Gm::GC ? gr * 8 : p.rope_off + (gr - Gm::GC) * 8);
-        v[q] = *(const uint2*)(pbase + off);
+        const int g0 = 2 * (qq * NW + w);
+        v[q] = *(const uint2*)(run + granule_offset<DC, 8>(p, g0) + lane_off8);
       }
     }
   }
-  __device__ __forceinline__ void store_chunk(char* buf, int c0, int w, int lane) {
+  __device__ __forceinline__ void store_chunk(char* buf, int c0, int w, int lane, bool valid) {
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
       const int qq = c0 + q;
       if (qq < NI) {
-        const int s = (qq * NW + w) * kWave + lane;
         bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[q].x, 1.0f, false);
         bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[q].x, 1.0f, true);
         bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[q].y, 1.0f, false);
         bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[q].y, 1.0f, true);
         bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-        *(bf16x8*)(buf + s * 16) = r;
+        if (!valid) r = bf16x8{};
+        *(bf16x8*)(buf + (qq * NW + w) * 1024 + lane * 16) = r;
       }
     }
   }
@@ -161,19 +165,33 @@ struct Fp8Stage {
 template <int DC, bool FP8>
 __device__ __forceinline__ void tile_step(const char* tb, const float* tsc, const bf16x8 (&qf)[Geo<DC>::KS],
                                           f32x16 (&O)[Geo<DC>::NB], float& m_run, float& l_run, int pos0, int limit,
-                                          float slog2, const int (&koff)[4], int voff0, int voff1, int half) {
+                                          float slog2) {
   using Gm = Geo<DC>;
-  // ---- S^T = K . Q^T  (32 tokens x 32 rows)
-  f32x16 sacc = f32x16{};
+  constexpr int PD = 4;  // k-steps of K fragments read ahead of their MFMA
+  const int lane = opaque_lane();
+  const int half = lane >> 5, col = lane & 31;
+
+  // ---- S^T = K . Q^T  (32 tokens x 32 rows); A = token `col`, granule 2ks + half,
+  // in two independent accumulator chains (even / odd k-steps).
+  const char* kb = tb + half * kRow + ((col ^ (half << 2)) << 4);
+  bf16x8 kf[Gm::KS];
+#pragma unroll
+  for (int ks = 0; ks < PD; ++ks) kf[ks] = *(const bf16x8*)(kb + ks * 2 * kRow);
+  f32x16 sacc0 = f32x16{}, sacc1 = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < Gm::KS; ++ks) {
-    const bf16x8 a = *(const bf16x8*)(tb + koff[ks & 3] + 128 * (ks >> 2));
-    sacc = mfma32(a, qf[ks], sacc);
-    // Bound the scheduler's read-ahead (registers are the scarce resource).
-    if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    if (ks + PD < Gm::KS) kf[ks + PD] = *(const bf16x8*)(kb + (ks + PD) * 2 * kRow);
+    if (ks & 1) sacc1 = mfma32(kf[ks], qf[ks], sacc1); else sacc0 = mfma32(kf[ks], qf[ks], sacc0);
   }
+#pragma unroll
+  for (int ks = 0; ks < Gm::KS - PD; ++ks) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read of k-step ks + PD
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA of k-step ks
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, PD, 0);
+  const f32x16 sacc = sacc0 + sacc1;
 
-  // ---- online softmax; this lane holds row (lane % 32), tokens 8(i/4) + 4*half + i%4
+  // ---- online softmax; this lane holds row `col`, tokens 8(i/4) + 4*half + i%4
   float tsv[16];
   if constexpr (FP8) {
 #pragma unroll
@@ -183,17 +201,23 @@ __device__ __forceinline__ void tile_step(const char* tb, const float* tsc, cons
       for (int c = 0; c < 4; ++c) tsv[4 * a4 + c] = s4[c];
     }
   }
+  // Per-token masking only where some position of the tile is not visible to
+  // some row (the last tile of a sequence, or the causal tail).
+  const bool full = __all(pos0 + kTile <= limit);
   float z[16];
   float mt = -__builtin_inff();
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int tau = 8 * (i >> 2) + 4 * half + (i & 3);
     float zi = sacc[i] * slog2;
     if constexpr (FP8) zi *= tsv[i];
-    z[i] = (pos0 + tau < limit) ? zi : -__builtin_inff();
-    mt = fmaxf(mt, z[i]);
+    if (!full) {
+      const int tau = 8 * (i >> 2) + 4 * half + (i & 3);
+      zi = (pos0 + tau < limit) ? zi : -__builtin_inff();
+    }
+    z[i] = zi;
+    mt = fmaxf(mt, zi);
   }
-  mt = wave_max_pair(mt);
+  mt = pair_max(mt);
   if (__any(mt > m_run + kRebase)) {
     const float m_new = fmaxf(m_run, mt);
     const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -217,27 +241,50 @@ __device__ __forceinline__ void tile_step(const char* tb, const float* tsc, cons
   float pv[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float pi = (z[i] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(z[i] - m_run);
+    // A row that has seen no visible position yet keeps m = -inf with all its
+    // z = -inf; exp2(-inf - -inf) would be NaN, so masked entries give 0.
+    float pi = __builtin_amdgcn_exp2f(z[i] - m_run);
+    if (!full) pi = (z[i] == -__builtin_inff()) ? 0.0f : pi;
     l_run += pi;
     if constexpr (FP8) pv[i] = pi * tsv[i]; else pv[i] = pi;
   }
   const bf16x8 pf0 = pack_bf16x8(pv);
   const bf16x8 pf1 = pack_bf16x8(pv + 8);
 
-  // ---- O^T += V^T . P^T
+  // ---- O^T += V^T . P^T; the four transposed reads of block nb+1 are issued
+  // before the two MFMAs of block nb.  Source lane (group G = lane/16, i = lane%16)
+  // reads token 16 j2 + 8 h + 4 (G/2) + i/4, columns 32 nb + 16 (G%2) + 4 (i%4) .. +3.
+  const int i16 = lane & 15, grp = lane >> 4;
+  const int jj = i16 >> 2, qq = i16 & 3, ch = grp & 1;
+  const int godd = qq >> 1;
+  const char* vb = tb + (2 * ch + godd) * kRow + (((4 * half + jj) ^ (godd << 2)) << 4) + ((qq & 1) << 3);
+  struct VF { s16x4 x0, x1, y0, y1; };
+  auto vread = [&](int nb) {
+    const char* a = vb + nb * 4 * kRow;
+    VF f;
+    f.x0 = lds_read_tr16(a);
+    f.x1 = lds_read_tr16(a + 8 * 16);
+    f.y0 = lds_read_tr16(a + 16 * 16);
+    f.y1 = lds_read_tr16(a + 24 * 16);
+    return f;
+  };
+  VF cur = vread(0);
 #pragma unroll
   for (int nb = 0; nb < Gm::NB; ++nb) {
-    const char* vb = tb + 128 * (nb >> 1) + ((nb & 1) ? voff1 : voff0);
-    const s16x4 x0 = lds_read_tr16(vb);
-    const s16x4 x1 = lds_read_tr16(vb + 8 * Gm::GPT * 16);
-    const s16x8 a0 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    VF nxt;
+    if (nb + 1 < Gm::NB) nxt = vread(nb + 1);
+    const s16x8 a0 = {cur.x0[0], cur.x0[1], cur.x0[2], cur.x0[3], cur.x1[0], cur.x1[1], cur.x1[2], cur.x1[3]};
+    const s16x8 a1 = {cur.y0[0], cur.y0[1], cur.y0[2], cur.y0[3], cur.y1[0], cur.y1[1], cur.y1[2], cur.y1[3]};
     O[nb] = mfma32((bf16x8)a0, pf0, O[nb]);
-    const s16x4 y0 = lds_read_tr16(vb + 16 * Gm::GPT * 16);
-    const s16x4 y1 = lds_read_tr16(vb + 24 * Gm::GPT * 16);
-    const s16x8 a1 = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
     O[nb] = mfma32((bf16x8)a1, pf1, O[nb]);
-    if (nb & 1) __builtin_amdgcn_sched_barrier(0);
+    cur = nxt;
   }
+#pragma unroll
+  for (int nb = 0; nb < Gm::NB - 1; ++nb) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);  // transposed reads of block nb + 1
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);  // MFMAs of block nb
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
 }
 
 template <int DC, bool FP8, int NW, int NBUF>
@@ -246,8 +293,8 @@ __global__ void __launch_bounds__(NW * kWave)
                   const float* __restrict__ kv_scale) {
   using Gm = Geo<DC>;
   constexpr int TB = Gm::TILE_BYTES;
-  constexpr int NI = kTile * Gm::GPT / (kWave * NW);
-  static_assert(kTile * Gm::GPT % (kWave * NW) == 0, "tile must split evenly over the waves");
+  constexpr int NI = Gm::GPT / (2 * NW);
+  static_assert(Gm::GPT % (2 * NW) == 0, "tile rows must split evenly over the waves");
   static_assert(FP8 ? NBUF == 2 : (NI * (NBUF - 2) <= 63), "DMA groups must fit vmcnt");
 
   __shared__ __attribute__((aligned(1024))) char tiles[NBUF * TB];
@@ -272,65 +319,57 @@ __global__ void __launch_bounds__(NW * kWave)
   if (k0 >= k1) return;
 
   const int row = rg * (32 * NW) + 32 * w + col;  // this lane's query row (S^T column)
-
-  // Lane-constant LDS offsets of the score A-operand (token `col`, granule 2ks+half).
-  const int swz_k = swz(col);
-  int koff[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) koff[m] = col * Gm::GPT * 16 + (((2 * m + half) ^ swz_k) * 16);
-  // ... and of the transposing V^T reads.
-  const int i16 = lane & 15, grp = lane >> 4;
-  const int jj = i16 >> 2, qq = i16 & 3, ch = grp & 1;
-  const int sv = (jj << 1) | half;
-  const int e = 2 * ch + (qq >> 1);
-  const int vbase = (4 * half + jj) * Gm::GPT * 16 + (qq & 1) * 8;
-  const int voff0 = vbase + ((e ^ sv) * 16);
-  const int voff1 = vbase + (((4 + e) ^ sv) * 16);
-
   const uint32_t tiles_lds = lds_offset(tiles);
 
-  // ---- tile loader state: next tile to load (kl) and its sequence (bl)
+  // ---- tile loader: next tile to load (kl, sequence bl) and its source run,
+  // looked up one tile ahead so the scalar loads are off the critical path.
   int kl = k0;
   int bl = uniform(seq_of_tile(cu, p.B, k0));
-  Fp8Stage<DC, NW> stage;
-
-  auto page_base = [&](int b, int j, int& nv) -> const char* {
+  auto run_of = [&](int b, int j) -> const char* {
+    b = uniform(b);
+    j = uniform(j);
     const int pos0 = j * kTile;
-    nv = min(kTile, seq_lens[b] - pos0);
-    const int page = block_table[(int64_t)b * p.bt_stride + pos0 / p.block_size];
-    return p.c_kv + (int64_t)page * p.block_stride + (int64_t)(pos0 % p.block_size) * p.token_stride;
+    const int page = block_table[(int64_t)b * p.bt_stride + (pos0 >> p.block_shift)];
+    return p.c_kv + (int64_t)page * p.block_stride + (int64_t)(pos0 & (p.block_size - 1)) * p.token_stride;
   };
+  auto advance = [&]() {
+    ++kl;
+    while (bl < p.B - 1 && kl >= uniform(cu[bl + 1])) ++bl;
+  };
+  const char* src = run_of(bl, kl - uniform(cu[bl]));
+
+  Fp8Stage<DC, NW> stage;
   auto stage_scales = [&](int b, int j, int sbuf) {
     if (w == 0 && lane < kTile) {
       const int pos0 = j * kTile;
-      const int nv = min(kTile, seq_lens[b] - pos0);
-      const int pos = pos0 + min(lane, nv - 1);
-      const int page = block_table[(int64_t)b * p.bt_stride + pos / p.block_size];
-      tscale[sbuf * kTile + lane] = kv_scale[(int64_t)page * p.block_size + pos % p.block_size];
+      const int nv = seq_lens[b] - pos0;
+      const int page = block_table[(int64_t)b * p.bt_stride + (pos0 >> p.block_shift)];
+      const float s = kv_scale[(int64_t)page * p.block_size + (pos0 & (p.block_size - 1)) + lane];
+      tscale[sbuf * kTile + lane] = lane < nv ? s : 0.0f;
     }
   };
 
-  DmaPlan<DC, NW> dma;
   if constexpr (!FP8) {
-    dma.init(p, w, lane);
+    const uint32_t lane_off = (uint32_t)load_token(lane) * (uint32_t)p.token_stride + 16u * half;
 #pragma unroll
     for (int i = 0; i < NBUF - 1; ++i) {
       if (kl < k1) {
-        dma.issue(p, block_table, bl, kl - uniform(cu[bl]), tiles_lds + ((kl - k0) % NBUF) * TB, w);
-        ++kl;
-        while (bl < p.B - 1 && kl >= uniform(cu[bl + 1])) ++bl;
+        issue_tile_dma<DC, NW>(p, src, lane_off, tiles_lds + ((kl - k0) % NBUF) * TB, w);
+        advance();
+        if (kl < k1) src = run_of(bl, kl - uniform(cu[bl]));
       }
     }
   } else {
-    int nv;
-    const char* pb = page_base(bl, kl - uniform(cu[bl]), nv);
+    const uint32_t lane_off8 = (uint32_t)load_token(lane) * (uint32_t)p.token_stride + 8u * half;
+    const int jl = kl - uniform(cu[bl]);
+    const bool valid = load_token(lane) < seq_lens[bl] - jl * kTile;
     for (int c0 = 0; c0 < Fp8Stage<DC, NW>::NI; c0 += Fp8Stage<DC, NW>::CH) {
-      stage.load_chunk(p, pb, nv, c0, w, lane);
-      stage.store_chunk(tiles, c0, w, lane);
+      stage.load_chunk(p, src, lane_off8, c0, w);
+      stage.store_chunk(tiles, c0, w, lane, valid);
     }
-    stage_scales(bl, kl - uniform(cu[bl]), 0);
-    ++kl;
-    while (bl < p.B - 1 && kl >= uniform(cu[bl + 1])) ++bl;
+    stage_scales(bl, jl, 0);
+    advance();
+    if (kl < k1) src = run_of(bl, kl - uniform(cu[bl]));
     block_sync();
   }
 
@@ -374,41 +413,45 @@ __global__ void __launch_bounds__(NW * kWave)
           block_sync();
         }
         if (kl < k1) {
-          dma.issue(p, block_table, bl, kl - uniform(cu[bl]), tiles_lds + ((kl - k0) % NBUF) * TB, w);
-          ++kl;
-          while (bl < p.B - 1 && kl >= uniform(cu[bl + 1])) ++bl;
+          const int ol = opaque_lane();
+          const uint32_t lane_off = (uint32_t)load_token(ol) * (uint32_t)p.token_stride + 16u * (ol >> 5);
+          issue_tile_dma<DC, NW>(p, src, lane_off, tiles_lds + ((kl - k0) % NBUF) * TB, w);
+          advance();
+          if (kl < k1) src = run_of(bl, kl - uniform(cu[bl]));
         }
       } else {
         if (kl < k1) {
-          int nv;
-          const char* pb = page_base(bl, kl - uniform(cu[bl]), nv);
-          stage.load_chunk(p, pb, nv, 0, w, lane);
+          const int ol = opaque_lane();
+          const uint32_t lane_off8 = (uint32_t)load_token(ol) * (uint32_t)p.token_stride + 8u * (ol >> 5);
+          stage.load_chunk(p, src, lane_off8, 0, w);
         }
       }
 
       tile_step<DC, FP8>(tiles + buf * TB, tscale + buf * kTile, qf, O, m_run, l_run, (k - cub) * kTile, limit,
-                         p.scale_log2, koff, voff0, voff1, half);
+                         p.scale_log2);
 
       if constexpr (FP8) {
         if (kl < k1) {
           const int nbuf = (kl - k0) % NBUF;
-          int nv;
-          const char* pb = page_base(bl, kl - uniform(cu[bl]), nv);
-          stage.store_chunk(tiles + nbuf * TB, 0, w, lane);
+          const int jl = kl - uniform(cu[bl]);
+          const int ol = opaque_lane();
+          const uint32_t lane_off8 = (uint32_t)load_token(ol) * (uint32_t)p.token_stride + 8u * (ol >> 5);
+          const bool valid = load_token(ol) < seq_lens[bl] - jl * kTile;
+          stage.store_chunk(tiles + nbuf * TB, 0, w, ol, valid);
           for (int c0 = Fp8Stage<DC, NW>::CH; c0 < Fp8Stage<DC, NW>::NI; c0 += Fp8Stage<DC, NW>::CH) {
-            stage.load_chunk(p, pb, nv, c0, w, lane);
-            stage.store_chunk(tiles + nbuf * TB, c0, w, lane);
+            stage.load_chunk(p, src, lane_off8, c0, w);
+            stage.store_chunk(tiles + nbuf * TB, c0, w, ol, valid);
           }
-          stage_scales(bl, kl - uniform(cu[bl]), nbuf);
-          ++kl;
-          while (bl < p.B - 1 && kl >= uniform(cu[bl + 1])) ++bl;
+          stage_scales(bl, jl, nbuf);
+          advance();
+          if (kl < k1) src = run_of(bl, kl - uniform(cu[bl]));
         }
         block_sync();
       }
     }
 
     // ---- normalise and write this (sequence, part) partial
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -__builtin_inff();
     const int64_t slot = (int64_t)bc + g;

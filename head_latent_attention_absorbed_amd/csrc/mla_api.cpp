@@ -72,8 +72,8 @@ mla_status_t check_shape(const mla_shape_t* s) {
   if (s->d_nope % 64 != 0 || s->d_nope > 512)
     return fail(MLA_ERR_UNSUPPORTED, "d_nope %d (multiple of 64 up to 512)", s->d_nope);
   if (s->d_v % 64 != 0) return fail(MLA_ERR_UNSUPPORTED, "d_v %d (multiple of 64)", s->d_v);
-  if (s->block_size % MLA_TILE_TOKENS != 0)
-    return fail(MLA_ERR_UNSUPPORTED, "block_size %d (multiple of %d)", s->block_size, MLA_TILE_TOKENS);
+  if (s->block_size < MLA_TILE_TOKENS || (s->block_size & (s->block_size - 1)) != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "block_size %d (a power of two >= %d)", s->block_size, MLA_TILE_TOKENS);
   if ((int64_t)s->batch * s->q_len > (1 << 20)) return fail(MLA_ERR_UNSUPPORTED, "batch * q_len too large");
   return MLA_OK;
 }
@@ -147,7 +147,7 @@ mla_status_t mla_decode_paged(const mla_shape_t* shape, const void* q_lat, const
   const int elem = fp8 ? 1 : 2;
   const int64_t rope_off = static_cast<const char*>(k_rope) - static_cast<const char*>(c_kv);
   if (token_stride <= 0 || token_stride % 16 || block_stride % 16 ||
-      block_stride < (int64_t)shape->block_size * token_stride)
+      block_stride < (int64_t)shape->block_size * token_stride || (int64_t)shape->block_size * token_stride > INT32_MAX)
     return fail(MLA_ERR_INVALID_ARG,
                 "mla_decode_paged: token_stride/block_stride must be positive multiples of 16 with "
                 "block_stride >= block_size * token_stride");
@@ -175,6 +175,7 @@ mla_status_t mla_decode_paged(const mla_shape_t* shape, const void* q_lat, const
   p.RG = mla::decode_row_groups(p.R);
   p.G = num_parts - shape->batch + 1;
   p.block_size = shape->block_size;
+  p.block_shift = __builtin_ctz((unsigned)shape->block_size);
   p.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
   p.o_part = o_part;
   p.lse_part = lse_part;

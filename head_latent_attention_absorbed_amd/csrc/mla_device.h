@@ -16,6 +16,8 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
 constexpr int kWave = 64;
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 constexpr int kTile = 32;  // tokens per decode tile (the M extent of one 32x32 MFMA)
 
 // D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).
@@ -41,7 +43,13 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // (wave-uniform).  Issued from inline asm so that the compiler does not put a
 // full vmcnt(0) wait in front of every LDS read; completion is tracked by
 // hand with vm_wait<N>().  M0 is saved and restored around the load.
-__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds) {
+__device__ __forceinline__ void lds_dma16(const void* base_any, uint32_t voff, uint32_t lds) {
+  // Make the base provably wave-uniform.  readfirstlane returns int: widen
+  // each half through uint32_t so the low half is zero-, not sign-, extended.
+  const uint64_t b = reinterpret_cast<uint64_t>(base_any);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -60,7 +68,7 @@ __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
   bf16x8 r;
@@ -69,9 +77,17 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
   return r;
 }
 
-__device__ __forceinline__ float wave_max_pair(float x) {
-  // max over lanes l and l ^ 32
-  return fmaxf(x, __shfl_xor(x, 32));
+// Reductions over the lane pair (l, l ^ 32) without going through LDS:
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second, so with x in both, the two results hold x[l % 32]
+// and x[l % 32 + 32] in every lane (in some order).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // XOR swizzle of the 16-byte granules of one cache record in LDS: token t's

@@ -23,7 +23,8 @@ struct DecodeParams {
   int32_t B, H, S, R;        // batch, heads, query tokens, rows = S * H
   int32_t RG;                // row groups (work-groups sharing one token range)
   int32_t G;                 // token parts
-  int32_t block_size;
+  int32_t block_size;        // tokens per page: 32 * 2^k
+  int32_t block_shift;       // log2(block_size)
   float scale_log2;          // softmax_scale * log2(e)
   float* o_part;             // fp32 [parts, R, DC]
   float* lse_part;           // fp32 [parts, R]

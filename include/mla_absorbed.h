@@ -81,7 +81,7 @@ typedef struct {
   int32_t d_rope;             /* decoupled RoPE width; 64                        */
   int32_t d_latent;           /* latent rank d_c; 512 or 256                     */
   int32_t d_v;                /* value width; 128                                */
-  int32_t block_size;         /* tokens per cache page; 64                       */
+  int32_t block_size;         /* tokens per cache page: 32 * 2^k (64)          */
   int32_t max_blocks_per_seq; /* row stride (entries) of block_table, >= 1       */
   float softmax_scale;        /* multiplies q.k; usually 1/sqrt(d_nope + d_rope) */
   mla_dtype_t cache_dtype;    /* MLA_BF16 or MLA_FP8_E4M3                        */
