@@ -161,11 +161,14 @@ struct Fp8Stage {
   }
 };
 
-// One 32-token tile of one wave: scores, online-softmax update, P.V.
+// Scores of one 32-token tile and the online-softmax update, without
+// branches: returns P (the B operand of the P.V product) and the factor
+// alpha by which the accumulators must be multiplied before P.V of this tile
+// is added (1 unless the row maximum grew by more than 2^kRebase).
 template <int DC, bool FP8>
-__device__ __forceinline__ void tile_step(const char* tb, const float* tsc, const bf16x8 (&qf)[Geo<DC>::KS],
-                                          f32x16 (&O)[Geo<DC>::NB], float& m_run, float& l_run, int pos0, int limit,
-                                          float slog2) {
+__device__ __forceinline__ void score_tile(const char* tb, const float* tsc, const bf16x8 (&qf)[Geo<DC>::KS],
+                                           float& m_run, float& l_run, int pos0, int limit, float slog2,
+                                           bf16x8& pf0, bf16x8& pf1, float& alpha) {
   using Gm = Geo<DC>;
   constexpr int PD = 4;  // k-steps of K fragments read ahead of their MFMA
   const int lane = opaque_lane();
@@ -183,6 +186,9 @@ __device__ __forceinline__ void tile_step(const char* tb, const float* tsc, cons
     if (ks + PD < Gm::KS) kf[ks + PD] = *(const bf16x8*)(kb + (ks + PD) * 2 * kRow);
     if (ks & 1) sacc1 = mfma32(kf[ks], qf[ks], sacc1); else sacc0 = mfma32(kf[ks], qf[ks], sacc0);
   }
+  // Order: the PD leading fragment reads, then (read ks + PD, MFMA ks), then
+  // the last PD MFMAs -- each MFMA's operand was requested PD MFMAs earlier.
+  __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
 #pragma unroll
   for (int ks = 0; ks < Gm::KS - PD; ++ks) {
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read of k-step ks + PD
@@ -190,8 +196,11 @@ __device__ __forceinline__ void tile_step(const char* tb, const float* tsc, cons
   }
   __builtin_amdgcn_sched_group_barrier(0x008, PD, 0);
   const f32x16 sacc = sacc0 + sacc1;
+  // The score product is its own scheduling region: nothing that follows
+  // (the softmax, or the lagged P.V of the previous tile) is hoisted into it.
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- online softmax; this lane holds row `col`, tokens 8(i/4) + 4*half + i%4
+  // ---- this lane holds row `col`, tokens 8(i/4) + 4*half + i%4
   float tsv[16];
   if constexpr (FP8) {
 #pragma unroll
@@ -201,59 +210,45 @@ __device__ __forceinline__ void tile_step(const char* tb, const float* tsc, cons
       for (int c = 0; c < 4; ++c) tsv[4 * a4 + c] = s4[c];
     }
   }
-  // Per-token masking only where some position of the tile is not visible to
-  // some row (the last tile of a sequence, or the causal tail).
-  const bool full = __all(pos0 + kTile <= limit);
   float z[16];
   float mt = -__builtin_inff();
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
+    const int tau = 8 * (i >> 2) + 4 * half + (i & 3);
     float zi = sacc[i] * slog2;
     if constexpr (FP8) zi *= tsv[i];
-    if (!full) {
-      const int tau = 8 * (i >> 2) + 4 * half + (i & 3);
-      zi = (pos0 + tau < limit) ? zi : -__builtin_inff();
-    }
+    zi = (pos0 + tau < limit) ? zi : -__builtin_inff();
     z[i] = zi;
     mt = fmaxf(mt, zi);
   }
   mt = pair_max(mt);
-  if (__any(mt > m_run + kRebase)) {
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= alpha;
-    // Element-wise through an AGPR-constrained block: the accumulators stay
-    // in AGPRs and the rescale needs a single temporary VGPR.
-#pragma unroll
-    for (int nb = 0; nb < Gm::NB; ++nb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = O[nb][i];
-        float tmp;
-        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32_e32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                     : "+a"(x), "=&v"(tmp)
-                     : "v"(alpha));
-        O[nb][i] = x;
-      }
-    }
-    m_run = m_new;
-  }
+  const bool rebase = mt > m_run + kRebase;
+  const float m_new = rebase ? mt : m_run;
+  alpha = rebase ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // exp2(-inf) = 0 on the first visible tile
+  l_run *= alpha;
+  m_run = m_new;
   float pv[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     // A row that has seen no visible position yet keeps m = -inf with all its
     // z = -inf; exp2(-inf - -inf) would be NaN, so masked entries give 0.
-    float pi = __builtin_amdgcn_exp2f(z[i] - m_run);
-    if (!full) pi = (z[i] == -__builtin_inff()) ? 0.0f : pi;
+    const float pi = (z[i] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(z[i] - m_new);
     l_run += pi;
     if constexpr (FP8) pv[i] = pi * tsv[i]; else pv[i] = pi;
   }
-  const bf16x8 pf0 = pack_bf16x8(pv);
-  const bf16x8 pf1 = pack_bf16x8(pv + 8);
+  pf0 = pack_bf16x8(pv);
+  pf1 = pack_bf16x8(pv + 8);
+}
 
-  // ---- O^T += V^T . P^T; the four transposed reads of block nb+1 are issued
-  // before the two MFMAs of block nb.  Source lane (group G = lane/16, i = lane%16)
-  // reads token 16 j2 + 8 h + 4 (G/2) + i/4, columns 32 nb + 16 (G%2) + 4 (i%4) .. +3.
+// O^T += V^T . P^T for one tile; the four transposed reads of block nb+1 are
+// issued before the two MFMAs of block nb.  Source lane (group G = lane/16,
+// i = lane%16) reads token 16 j2 + 8 h + 4 (G/2) + i/4 and columns
+// 32 nb + 16 (G%2) + 4 (i%4) .. +3.
+template <int DC, int VALU_PER_BLOCK>
+__device__ __forceinline__ void pv_tile(const char* tb, bf16x8 pf0, bf16x8 pf1, f32x16 (&O)[Geo<DC>::NB]) {
+  using Gm = Geo<DC>;
+  const int lane = opaque_lane();
+  const int half = lane >> 5;
   const int i16 = lane & 15, grp = lane >> 4;
   const int jj = i16 >> 2, qq = i16 & 3, ch = grp & 1;
   const int godd = qq >> 1;
@@ -279,29 +274,62 @@ __device__ __forceinline__ void tile_step(const char* tb, const float* tsc, cons
     O[nb] = mfma32((bf16x8)a1, pf1, O[nb]);
     cur = nxt;
   }
+  // Order: the four reads of block 0, then per block (reads of block nb + 1,
+  // MFMAs of block nb[, some independent VALU work of the caller]).
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
-  for (int nb = 0; nb < Gm::NB - 1; ++nb) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);  // transposed reads of block nb + 1
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);  // MFMAs of block nb
+  for (int nb = 0; nb < Gm::NB; ++nb) {
+    if (nb + 1 < Gm::NB) __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+    if (VALU_PER_BLOCK > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER_BLOCK, 1);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
 }
 
-template <int DC, bool FP8, int NW, int NBUF>
+// Multiply the accumulators by alpha (rare: the row maximum grew by more than
+// 2^kRebase).  Element-wise through AGPR-constrained blocks, so the
+// accumulators stay in AGPRs and one temporary VGPR suffices; the leading
+// wait states cover an MFMA that may just have written them (the compiler's
+// hazard check does not look inside inline asm).
+template <int DC>
+__device__ __forceinline__ void rescale(f32x16 (&O)[Geo<DC>::NB], float alpha) {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int nb = 0; nb < Geo<DC>::NB; ++nb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float x = O[nb][i];
+      float tmp;
+      asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32_e32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                   : "+a"(x), "=&v"(tmp)
+                   : "v"(alpha));
+      O[nb][i] = x;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// LAG: P.V of tile k runs while the softmax of tile k+1 is computed (one
+// basic block, so MFMA and VALU work interleave); needs one extra ring buffer.
+template <int DC, bool FP8, int NW, int NBUF, bool LAG>
 __global__ void __launch_bounds__(NW * kWave)
     decode_kernel(DecodeParams p, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ block_table,
                   const float* __restrict__ kv_scale) {
   using Gm = Geo<DC>;
   constexpr int TB = Gm::TILE_BYTES;
   constexpr int NI = Gm::GPT / (2 * NW);
+  constexpr int AHEAD = NBUF - 1 - (LAG ? 1 : 0);  // tiles in flight ahead of the one computed
   static_assert(Gm::GPT % (2 * NW) == 0, "tile rows must split evenly over the waves");
-  static_assert(FP8 ? NBUF == 2 : (NI * (NBUF - 2) <= 63), "DMA groups must fit vmcnt");
+  static_assert(AHEAD >= 1, "ring too small");
+  static_assert(FP8 || NI * (AHEAD - 1) <= 63, "DMA groups must fit vmcnt");
+  static_assert(!FP8 || AHEAD == 1, "fp8 tiles are staged one ahead");
 
   __shared__ __attribute__((aligned(1024))) char tiles[NBUF * TB];
   __shared__ __attribute__((aligned(16))) float tscale[FP8 ? NBUF * kTile : 4];
   __shared__ int cu[kMaxBatch + 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = uniform(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
 
   // XCD-aware placement: consecutive work items (the row groups of one token
@@ -321,8 +349,7 @@ __global__ void __launch_bounds__(NW * kWave)
   const int row = rg * (32 * NW) + 32 * w + col;  // this lane's query row (S^T column)
   const uint32_t tiles_lds = lds_offset(tiles);
 
-  // ---- tile loader: next tile to load (kl, sequence bl) and its source run,
-  // looked up one tile ahead so the scalar loads are off the critical path.
+  // ---- tile loader: next tile to load (kl, sequence bl) and its source run.
   int kl = k0;
   int bl = uniform(seq_of_tile(cu, p.B, k0));
   auto run_of = [&](int b, int j) -> const char* {
@@ -337,6 +364,13 @@ __global__ void __launch_bounds__(NW * kWave)
     while (bl < p.B - 1 && kl >= uniform(cu[bl + 1])) ++bl;
   };
   const char* src = run_of(bl, kl - uniform(cu[bl]));
+  auto dma_next = [&]() {  // bf16: start the copy of tile kl into its ring slot
+    const int ol = opaque_lane();
+    const uint32_t lane_off = (uint32_t)load_token(ol) * (uint32_t)p.token_stride + 16u * (ol >> 5);
+    issue_tile_dma<DC, NW>(p, src, lane_off, tiles_lds + ((kl - k0) % NBUF) * TB, w);
+    advance();
+    if (kl < k1) src = run_of(bl, kl - uniform(cu[bl]));
+  };
 
   Fp8Stage<DC, NW> stage;
   auto stage_scales = [&](int b, int j, int sbuf) {
@@ -348,30 +382,59 @@ __global__ void __launch_bounds__(NW * kWave)
       tscale[sbuf * kTile + lane] = lane < nv ? s : 0.0f;
     }
   };
-
-  if constexpr (!FP8) {
-    const uint32_t lane_off = (uint32_t)load_token(lane) * (uint32_t)p.token_stride + 16u * half;
-#pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i) {
-      if (kl < k1) {
-        issue_tile_dma<DC, NW>(p, src, lane_off, tiles_lds + ((kl - k0) % NBUF) * TB, w);
-        advance();
-        if (kl < k1) src = run_of(bl, kl - uniform(cu[bl]));
-      }
-    }
-  } else {
-    const uint32_t lane_off8 = (uint32_t)load_token(lane) * (uint32_t)p.token_stride + 8u * half;
+  auto stage_finish = [&]() {  // fp8: decode the loaded tile kl into its ring slot
+    const int nbuf = (kl - k0) % NBUF;
     const int jl = kl - uniform(cu[bl]);
-    const bool valid = load_token(lane) < seq_lens[bl] - jl * kTile;
-    for (int c0 = 0; c0 < Fp8Stage<DC, NW>::NI; c0 += Fp8Stage<DC, NW>::CH) {
+    const int ol = opaque_lane();
+    const uint32_t lane_off8 = (uint32_t)load_token(ol) * (uint32_t)p.token_stride + 8u * (ol >> 5);
+    const bool valid = load_token(ol) < seq_lens[bl] - jl * kTile;
+    stage.store_chunk(tiles + nbuf * TB, 0, w, ol, valid);
+    for (int c0 = Fp8Stage<DC, NW>::CH; c0 < Fp8Stage<DC, NW>::NI; c0 += Fp8Stage<DC, NW>::CH) {
       stage.load_chunk(p, src, lane_off8, c0, w);
-      stage.store_chunk(tiles, c0, w, lane, valid);
+      stage.store_chunk(tiles + nbuf * TB, c0, w, ol, valid);
     }
-    stage_scales(bl, jl, 0);
+    stage_scales(bl, jl, nbuf);
     advance();
     if (kl < k1) src = run_of(bl, kl - uniform(cu[bl]));
+  };
+  auto stage_start = [&]() {
+    const int ol = opaque_lane();
+    const uint32_t lane_off8 = (uint32_t)load_token(ol) * (uint32_t)p.token_stride + 8u * (ol >> 5);
+    stage.load_chunk(p, src, lane_off8, 0, w);
+  };
+
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i)
+      if (kl < k1) dma_next();
+  } else {
+    stage_start();
+    stage_finish();
     block_sync();
   }
+
+  // Before computing tile k: its data is in LDS and visible to all waves, and
+  // the next copy is started (bf16) or its loads are issued (fp8).
+  auto tile_begin = [&](int k, int cub, int L) {
+    const int buf = (k - k0) % NBUF;
+    if constexpr (!FP8) {
+      wait_dma_groups<NI, AHEAD - 1>(kl - 1 - k);
+      block_sync();
+      if ((k - cub + 1) * kTile > L) {  // last tile of the sequence, partially filled
+        zero_tail<DC, NW>(tiles + buf * TB, L - (k - cub) * kTile, tid);
+        block_sync();
+      }
+      if (kl < k1) dma_next();
+    } else {
+      if (kl < k1) stage_start();
+    }
+  };
+  auto tile_end = [&]() {
+    if constexpr (FP8) {
+      if (kl < k1) stage_finish();
+      block_sync();
+    }
+  };
 
   // ---- segments: maximal runs of this part's tiles inside one sequence
   int k = k0;
@@ -402,51 +465,39 @@ __global__ void __launch_bounds__(NW * kWave)
 #pragma unroll
     for (int nb = 0; nb < Gm::NB; ++nb) O[nb] = f32x16{};
     float m_run = -__builtin_inff(), l_run = 0.0f;
+    bf16x8 pf0, pf1;
+    float alpha;
 
-    for (; k < kend; ++k) {
-      const int buf = (k - k0) % NBUF;
-      if constexpr (!FP8) {
-        wait_dma_groups<NI, NBUF - 2>(kl - 1 - k);
-        block_sync();
-        if ((k - cub + 1) * kTile > L) {  // last tile of the sequence, partially filled
-          zero_tail<DC, NW>(tiles + buf * TB, L - (k - cub) * kTile, tid);
-          block_sync();
-        }
-        if (kl < k1) {
-          const int ol = opaque_lane();
-          const uint32_t lane_off = (uint32_t)load_token(ol) * (uint32_t)p.token_stride + 16u * (ol >> 5);
-          issue_tile_dma<DC, NW>(p, src, lane_off, tiles_lds + ((kl - k0) % NBUF) * TB, w);
-          advance();
-          if (kl < k1) src = run_of(bl, kl - uniform(cu[bl]));
-        }
-      } else {
-        if (kl < k1) {
-          const int ol = opaque_lane();
-          const uint32_t lane_off8 = (uint32_t)load_token(ol) * (uint32_t)p.token_stride + 8u * (ol >> 5);
-          stage.load_chunk(p, src, lane_off8, 0, w);
-        }
+    if constexpr (LAG) {
+      // first tile: scores only (the accumulators are still zero, so no rescale)
+      tile_begin(k, cub, L);
+      score_tile<DC, FP8>(tiles + ((k - k0) % NBUF) * TB, tscale + ((k - k0) % NBUF) * kTile, qf, m_run, l_run,
+                          (k - cub) * kTile, limit, p.scale_log2, pf0, pf1, alpha);
+      tile_end();
+      for (++k; k < kend; ++k) {
+        tile_begin(k, cub, L);
+        const int buf = (k - k0) % NBUF;
+        bf16x8 nf0, nf1;
+        score_tile<DC, FP8>(tiles + buf * TB, tscale + buf * kTile, qf, m_run, l_run, (k - cub) * kTile, limit,
+                            p.scale_log2, nf0, nf1, alpha);
+        // P.V of tile k-1 interleaved with the softmax VALU work of tile k.
+        pv_tile<DC, 128 / Geo<DC>::NB>(tiles + ((k - 1 - k0) % NBUF) * TB, pf0, pf1, O);
+        __builtin_amdgcn_sched_barrier(0);
+        if (__any(alpha != 1.0f)) rescale<DC>(O, alpha);
+        pf0 = nf0;
+        pf1 = nf1;
+        tile_end();
       }
-
-      tile_step<DC, FP8>(tiles + buf * TB, tscale + buf * kTile, qf, O, m_run, l_run, (k - cub) * kTile, limit,
-                         p.scale_log2);
-
-      if constexpr (FP8) {
-        if (kl < k1) {
-          const int nbuf = (kl - k0) % NBUF;
-          const int jl = kl - uniform(cu[bl]);
-          const int ol = opaque_lane();
-          const uint32_t lane_off8 = (uint32_t)load_token(ol) * (uint32_t)p.token_stride + 8u * (ol >> 5);
-          const bool valid = load_token(ol) < seq_lens[bl] - jl * kTile;
-          stage.store_chunk(tiles + nbuf * TB, 0, w, ol, valid);
-          for (int c0 = Fp8Stage<DC, NW>::CH; c0 < Fp8Stage<DC, NW>::NI; c0 += Fp8Stage<DC, NW>::CH) {
-            stage.load_chunk(p, src, lane_off8, c0, w);
-            stage.store_chunk(tiles + nbuf * TB, c0, w, ol, valid);
-          }
-          stage_scales(bl, jl, nbuf);
-          advance();
-          if (kl < k1) src = run_of(bl, kl - uniform(cu[bl]));
-        }
-        block_sync();
+      pv_tile<DC, 0>(tiles + ((k - 1 - k0) % NBUF) * TB, pf0, pf1, O);
+    } else {
+      for (; k < kend; ++k) {
+        tile_begin(k, cub, L);
+        const int buf = (k - k0) % NBUF;
+        score_tile<DC, FP8>(tiles + buf * TB, tscale + buf * kTile, qf, m_run, l_run, (k - cub) * kTile, limit,
+                            p.scale_log2, pf0, pf1, alpha);
+        if (__any(alpha != 1.0f)) rescale<DC>(O, alpha);
+        pv_tile<DC, 0>(tiles + buf * TB, pf0, pf1, O);
+        tile_end();
       }
     }
 
@@ -474,24 +525,27 @@ __global__ void __launch_bounds__(NW * kWave)
   }
 }
 
-template <int DC, bool FP8, int NW, int NBUF>
+template <int DC, bool FP8, int NW, int NBUF, bool LAG>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   const int grid = p.G * p.RG;
-  hipLaunchKernelGGL((decode_kernel<DC, FP8, NW, NBUF>), dim3(grid), dim3(NW * kWave), 0, stream, p, p.seq_lens,
-                     p.block_table, p.kv_scale);
+  hipLaunchKernelGGL((decode_kernel<DC, FP8, NW, NBUF, LAG>), dim3(grid), dim3(NW * kWave), 0, stream, p,
+                     p.seq_lens, p.block_table, p.kv_scale);
   return hipGetLastError();
 }
 
+// Four-wave groups (128 query rows) run one work-group per CU on a 4-tile
+// ring (bf16; 2 for the staged fp8 path).  One- and two-wave groups run two
+// work-groups per CU on a 2-tile ring.
 template <int DC, bool FP8>
 hipError_t launch_dc(const DecodeParams& p, int nw, hipStream_t stream) {
   if constexpr (FP8) {
-    if (nw == 4) return launch_one<DC, FP8, 4, 2>(p, stream);
-    if (nw == 2) return launch_one<DC, FP8, 2, 2>(p, stream);
-    return launch_one<DC, FP8, 1, 2>(p, stream);
+    if (nw == 4) return launch_one<DC, FP8, 4, 2, false>(p, stream);
+    if (nw == 2) return launch_one<DC, FP8, 2, 2, false>(p, stream);
+    return launch_one<DC, FP8, 1, 2, false>(p, stream);
   } else {
-    if (nw == 4) return launch_one<DC, FP8, 4, 4>(p, stream);
-    if (nw == 2) return launch_one<DC, FP8, 2, 2>(p, stream);
-    return launch_one<DC, FP8, 1, 2>(p, stream);
+    if (nw == 4) return launch_one<DC, FP8, 4, 4, false>(p, stream);
+    if (nw == 2) return launch_one<DC, FP8, 2, 2, false>(p, stream);
+    return launch_one<DC, FP8, 1, 2, false>(p, stream);
   }
 }
 
