@@ -83,6 +83,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="input replicas rotated across steps (0 = auto)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--partial", default="fp16", choices=("fp16", "fp32"), help="element type of the split partials")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -109,7 +110,7 @@ def main():
     per_rep = alg["step_bytes"]
     nrep = args.replicas or max(3, math.ceil(3 * INFINITY_CACHE_BYTES / max(per_rep, 1)) + 1)
     nrep = min(nrep, 64)
-    steps = [DecodeStep(inputs) for _ in range(nrep)]
+    steps = [DecodeStep(inputs, partial=args.partial) for _ in range(nrep)]
     stream = torch.cuda.current_stream()
     log(f"workload {w.name}: tokens={alg['tokens']} cache={alg['cache_bytes'] / 1e6:.1f} MB "
         f"replicas={nrep} num_parts={steps[0].num_parts}")
@@ -170,7 +171,7 @@ def main():
             "d_nope": w.d_nope, "d_v": w.d_v, "block_size": w.block_size, "cache": w.cache_dtype,
             "seq_lens": f"uniform[{w.seq_len[0]},{w.seq_len[1]}] seed {w.seed}",
             "tokens": alg["tokens"], "cache_bytes": alg["cache_bytes"], "input_replicas": nrep,
-            "num_parts": steps[0].num_parts,
+            "num_parts": steps[0].num_parts, "partials": args.partial,
         },
         "per_call_us_median": {k: round(v, 2) for k, v in med.items()},
         "decode_combine_tbs": round(alg["cache_bytes"] / ((med["decode"] + med["combine"]) * 1e-6) / 1e12, 4),

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     MLA_ERR_HIP,
     MLA_BF16,
     MLA_FP8_E4M3,
+    MLA_FP16,
     MLA_FP32,
     MLA_TILE_TOKENS,
     MlaError,

@@ -13,6 +13,7 @@ MLA_ERR_HIP = 3
 MLA_BF16 = 0
 MLA_FP8_E4M3 = 1
 MLA_FP32 = 2
+MLA_FP16 = 3
 
 MLA_TILE_TOKENS = 32
 
@@ -36,13 +37,15 @@ class MlaShape(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("cache_dtype", ctypes.c_int),
         ("out_dtype", ctypes.c_int),
+        ("partial_dtype", ctypes.c_int),
     ]
 
     @classmethod
     def make(cls, *, batch, num_heads, q_len, d_latent, max_blocks_per_seq, softmax_scale,
-             cache_dtype=MLA_BF16, out_dtype=MLA_BF16, d_nope=128, d_rope=64, d_v=128, block_size=64):
+             cache_dtype=MLA_BF16, out_dtype=MLA_BF16, partial_dtype=MLA_FP32, d_nope=128, d_rope=64, d_v=128,
+             block_size=64):
         return cls(batch, num_heads, q_len, d_nope, d_rope, d_latent, d_v, block_size, max_blocks_per_seq,
-                   softmax_scale, cache_dtype, out_dtype)
+                   softmax_scale, cache_dtype, out_dtype, partial_dtype)
 
 
 class MlaError(RuntimeError):

@@ -5,15 +5,59 @@
 // on the "GQA-to-MLA" Daily Papers listing builds on): with per-split
 // normalised outputs o_k and log-sum-exps lse_k,
 //   lse = log sum_k e^{lse_k},  o = sum_k e^{lse_k - lse} o_k.
-// One wave per (sequence, query row); each lane owns DC/64 latent columns.
 #include "mla_device.h"
 #include "mla_kernels.h"
 
 namespace mla {
 namespace {
 
-template <int DC>
+template <int E, bool HALF>
+struct PartRow;  // E consecutive columns of one partial row, loaded as one or two 16-byte words
+
+template <>
+struct PartRow<8, true> {
+  uint4 v;
+  __device__ void load(const void* base, int64_t off) { v = *(const uint4*)((const _Float16*)base + off); }
+  __device__ float at(int i) const {
+    const uint32_t w = i < 2 ? v.x : i < 4 ? v.y : i < 6 ? v.z : v.w;
+    return (float)__builtin_bit_cast(f16x2, w)[i & 1];
+  }
+};
+template <>
+struct PartRow<4, true> {
+  uint2 v;
+  __device__ void load(const void* base, int64_t off) { v = *(const uint2*)((const _Float16*)base + off); }
+  __device__ float at(int i) const { return (float)__builtin_bit_cast(f16x2, i < 2 ? v.x : v.y)[i & 1]; }
+};
+template <>
+struct PartRow<8, false> {
+  f32x4 a, b;
+  __device__ void load(const void* base, int64_t off) {
+    a = *(const f32x4*)((const float*)base + off);
+    b = *(const f32x4*)((const float*)base + off + 4);
+  }
+  __device__ float at(int i) const { return i < 4 ? a[i] : b[i - 4]; }
+};
+template <>
+struct PartRow<4, false> {
+  f32x4 a;
+  __device__ void load(const void* base, int64_t off) { a = *(const f32x4*)((const float*)base + off); }
+  __device__ float at(int i) const { return a[i]; }
+};
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// One wave per (sequence, query row); lane i owns columns E*i .. E*i + E-1.
+// The splits are visited U at a time with all U loads issued before the
+// first is used (indices past the last split repeat it with weight 0).
+template <int DC, bool HALF>
 __global__ void __launch_bounds__(256) combine_kernel(CombineParams p, const int32_t* __restrict__ seq_lens) {
+  constexpr int E = DC / 64;
+  constexpr int U = 8;
   __shared__ int cu[kMaxBatch + 1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.x;
@@ -22,53 +66,61 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineParams p, const int
   const int row = blockIdx.y * 4 + w;
   if (row >= p.R) return;
 
-  constexpr int V4 = DC / 256;  // float4 groups per lane
-  float* out = p.o_lat + ((int64_t)b * p.R + row) * DC + 4 * lane;
-  float* lse_out = p.lse + (int64_t)b * p.R + row;
+  float* out = p.o_lat + ((int64_t)b * p.R + row) * DC + E * lane;
   const int N = cu[p.B], cb = cu[b], ce = cu[b + 1];
-
-  float m = -__builtin_inff();
   int g0 = 0, g1 = -1;
   if (ce > cb) {
     const int Wt = (N + p.G - 1) / p.G;
     g0 = cb / Wt;
     g1 = (ce - 1) / Wt;
-    for (int g = g0; g <= g1; ++g) m = fmaxf(m, p.lse_part[((int64_t)b + g) * p.R + row]);
   }
-  if (m == -__builtin_inff()) {
+  float m = -__builtin_inff();
+  for (int g = g0 + lane; g <= g1; g += kWave) m = fmaxf(m, p.lse_part[((int64_t)b + g) * p.R + row]);
+  m = wave_max(m);
+  if (m == -__builtin_inff()) {  // the row sees no position
 #pragma unroll
-    for (int i = 0; i < V4; ++i) *(f32x4*)(out + 256 * i) = f32x4{};
-    if (lane == 0) *lse_out = -__builtin_inff();
+    for (int i = 0; i < E; i += 4) *(f32x4*)(out + i) = f32x4{};
+    if (lane == 0) p.lse[(int64_t)b * p.R + row] = -__builtin_inff();
     return;
   }
-  f32x4 acc[V4];
+  float acc[E];
 #pragma unroll
-  for (int i = 0; i < V4; ++i) acc[i] = f32x4{};
+  for (int i = 0; i < E; ++i) acc[i] = 0.0f;
   float tot = 0.0f;
-  for (int g = g0; g <= g1; ++g) {
-    const int64_t slot = (int64_t)b + g;
-    const float lk = p.lse_part[slot * p.R + row];
-    if (lk == -__builtin_inff()) continue;
-    const float wk = expf(lk - m);
-    tot += wk;
-    const float* src = p.o_part + (slot * p.R + row) * DC + 4 * lane;
+  for (int gb = g0; gb <= g1; gb += U) {
+    PartRow<E, HALF> part[U];
+    float wk[U];
 #pragma unroll
-    for (int i = 0; i < V4; ++i) acc[i] += wk * *(const f32x4*)(src + 256 * i);
+    for (int j = 0; j < U; ++j) {
+      const int64_t slot = (int64_t)b + min(gb + j, g1);
+      part[j].load(p.o_part, (slot * p.R + row) * DC + E * lane);
+      wk[j] = p.lse_part[slot * p.R + row];
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const float wj = (gb + j <= g1) ? __expf(wk[j] - m) : 0.0f;  // exp(-inf) = 0 for empty splits
+      tot += wj;
+#pragma unroll
+      for (int i = 0; i < E; ++i) acc[i] += wj * part[j].at(i);
+    }
   }
   const float inv = 1.0f / tot;
 #pragma unroll
-  for (int i = 0; i < V4; ++i) *(f32x4*)(out + 256 * i) = acc[i] * inv;
-  if (lane == 0) *lse_out = m + logf(tot);
+  for (int i = 0; i < E; i += 4) *(f32x4*)(out + i) = f32x4{acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv};
+  if (lane == 0) p.lse[(int64_t)b * p.R + row] = m + __logf(tot);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   dim3 grid(p.B, (p.R + 3) / 4);
-  if (p.DC == 512)
-    hipLaunchKernelGGL(combine_kernel<512>, grid, dim3(256), 0, stream, p, p.seq_lens);
-  else
-    hipLaunchKernelGGL(combine_kernel<256>, grid, dim3(256), 0, stream, p, p.seq_lens);
+  if (p.DC == 512) {
+    if (p.o_half) hipLaunchKernelGGL((combine_kernel<512, true>), grid, dim3(256), 0, stream, p, p.seq_lens);
+    else hipLaunchKernelGGL((combine_kernel<512, false>), grid, dim3(256), 0, stream, p, p.seq_lens);
+  } else {
+    if (p.o_half) hipLaunchKernelGGL((combine_kernel<256, true>), grid, dim3(256), 0, stream, p, p.seq_lens);
+    else hipLaunchKernelGGL((combine_kernel<256, false>), grid, dim3(256), 0, stream, p, p.seq_lens);
+  }
   return hipGetLastError();
 }
 

@@ -490,7 +490,10 @@ __global__ void __launch_bounds__(NW * kWave)
       }
       pv_tile<DC, 0>(tiles + ((k - 1 - k0) % NBUF) * TB, pf0, pf1, O);
     } else {
-      for (; k < kend; ++k) {
+      // A segment holds at least one tile; with the loop written bottom-tested
+      // the accumulators leave it only as MFMA results, so the epilogue reads
+      // them block by block instead of copying all of them out at once.
+      do {
         tile_begin(k, cub, L);
         const int buf = (k - k0) % NBUF;
         score_tile<DC, FP8>(tiles + buf * TB, tscale + buf * kTile, qf, m_run, l_run, (k - cub) * kTile, limit,
@@ -498,7 +501,8 @@ __global__ void __launch_bounds__(NW * kWave)
         if (__any(alpha != 1.0f)) rescale<DC>(O, alpha);
         pv_tile<DC, 0>(tiles + buf * TB, pf0, pf1, O);
         tile_end();
-      }
+        ++k;
+      } while (k < kend);
     }
 
     // ---- normalise and write this (sequence, part) partial
@@ -507,18 +511,46 @@ __global__ void __launch_bounds__(NW * kWave)
     const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -__builtin_inff();
     const int64_t slot = (int64_t)bc + g;
     if (row < p.R) {
-      float* dst = p.o_part + (slot * p.R + row) * DC + 4 * half;
-#pragma unroll
-      for (int nb = 0; nb < Gm::NB; ++nb) {
-#pragma unroll
-        for (int ig = 0; ig < 4; ++ig) {
-          const f32x4 v = {O[nb][4 * ig] * inv, O[nb][4 * ig + 1] * inv, O[nb][4 * ig + 2] * inv,
-                           O[nb][4 * ig + 3] * inv};
-          *(f32x4*)(dst + 32 * nb + 8 * ig) = v;
-        }
-        __builtin_amdgcn_sched_barrier(0);  // one accumulator block at a time
-      }
+      // The lse goes first: vector stores count in vmcnt, so any wait the
+      // compiler places before a later store (a spilled address being
+      // reloaded) would otherwise also wait for the whole partial to be written.
       if (half == 0) p.lse_part[slot * p.R + row] = lse;
+      if (p.o_half) {
+        // fp16 partial.  Lane pair (l, l + 32) swaps packed halves so that each
+        // lane stores 8 consecutive columns: with column quarters q0..q3 of an
+        // 8-column group split 4 + 4 over the pair, the swap gives the lower
+        // lane the odd group and the upper lane the even one.
+        _Float16* dst = (_Float16*)p.o_part + (slot * p.R + row) * DC + 8 * (1 - half);
+#pragma unroll
+        for (int nb = 0; nb < Gm::NB; ++nb) {
+          uint32_t h[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const f16x2 v = {(_Float16)(O[nb][2 * j] * inv), (_Float16)(O[nb][2 * j + 1] * inv)};
+            h[j] = __builtin_bit_cast(uint32_t, v);
+          }
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {  // 8-column groups (2pr, 2pr + 1)
+            const auto r0 = __builtin_amdgcn_permlane32_swap(h[4 * pr + 2], h[4 * pr], false, false);
+            const auto r1 = __builtin_amdgcn_permlane32_swap(h[4 * pr + 3], h[4 * pr + 1], false, false);
+            const uint4 v = {r0[0], r1[0], r0[1], r1[1]};
+            *(uint4*)(dst + 32 * nb + 16 * pr) = v;
+          }
+          __builtin_amdgcn_sched_barrier(0);  // one accumulator block at a time
+        }
+      } else {
+        float* dst = (float*)p.o_part + (slot * p.R + row) * DC + 4 * half;
+#pragma unroll
+        for (int nb = 0; nb < Gm::NB; ++nb) {
+#pragma unroll
+          for (int ig = 0; ig < 4; ++ig) {
+            const f32x4 v = {O[nb][4 * ig] * inv, O[nb][4 * ig + 1] * inv, O[nb][4 * ig + 2] * inv,
+                             O[nb][4 * ig + 3] * inv};
+            *(f32x4*)(dst + 32 * nb + 8 * ig) = v;
+          }
+          __builtin_amdgcn_sched_barrier(0);  // one accumulator block at a time
+        }
+      }
     }
     ++bc;
     while (bc < p.B - 1 && uniform(cu[bc + 1]) == uniform(cu[bc])) ++bc;

@@ -64,6 +64,8 @@ mla_status_t check_shape(const mla_shape_t* s) {
     return fail(MLA_ERR_INVALID_ARG, "cache_dtype must be MLA_BF16 or MLA_FP8_E4M3");
   if (s->out_dtype != MLA_BF16 && s->out_dtype != MLA_FP32)
     return fail(MLA_ERR_INVALID_ARG, "out_dtype must be MLA_BF16 or MLA_FP32");
+  if (s->partial_dtype != MLA_FP32 && s->partial_dtype != MLA_FP16)
+    return fail(MLA_ERR_INVALID_ARG, "partial_dtype must be MLA_FP32 or MLA_FP16");
   if (s->batch > mla::kMaxBatch) return fail(MLA_ERR_UNSUPPORTED, "batch %d > %d", s->batch, mla::kMaxBatch);
   if (s->q_len > 8) return fail(MLA_ERR_UNSUPPORTED, "q_len %d > 8", s->q_len);
   if (s->d_latent != 512 && s->d_latent != 256)
@@ -133,7 +135,7 @@ mla_status_t mla_decode_num_parts(const mla_shape_t* shape, int32_t* num_parts) 
 
 mla_status_t mla_decode_paged(const mla_shape_t* shape, const void* q_lat, const void* q_rope, const void* c_kv,
                               const void* k_rope, int64_t token_stride, int64_t block_stride, const float* kv_scale,
-                              const int32_t* block_table, const int32_t* seq_lens, int32_t num_parts, float* o_part,
+                              const int32_t* block_table, const int32_t* seq_lens, int32_t num_parts, void* o_part,
                               float* lse_part, hipStream_t stream) {
   mla_status_t st = check_shape(shape);
   if (st != MLA_OK) return st;
@@ -178,12 +180,13 @@ mla_status_t mla_decode_paged(const mla_shape_t* shape, const void* q_lat, const
   p.block_shift = __builtin_ctz((unsigned)shape->block_size);
   p.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
   p.o_part = o_part;
+  p.o_half = shape->partial_dtype == MLA_FP16;
   p.lse_part = lse_part;
   if ((int64_t)p.G * p.RG > (int64_t)1 << 30) return fail(MLA_ERR_UNSUPPORTED, "too many decode work-groups");
   return hip_status(mla::launch_decode(p, shape->d_latent, fp8, stream), "mla_decode_paged launch");
 }
 
-mla_status_t mla_combine_lse(const mla_shape_t* shape, int32_t num_parts, const float* o_part, const float* lse_part,
+mla_status_t mla_combine_lse(const mla_shape_t* shape, int32_t num_parts, const void* o_part, const float* lse_part,
                              const int32_t* seq_lens, float* o_lat, float* lse, hipStream_t stream) {
   mla_status_t st = check_shape(shape);
   if (st != MLA_OK) return st;
@@ -195,6 +198,7 @@ mla_status_t mla_combine_lse(const mla_shape_t* shape, int32_t num_parts, const 
     return fail(MLA_ERR_INVALID_ARG, "mla_combine_lse: num_parts %d < batch %d", num_parts, shape->batch);
   mla::CombineParams p{};
   p.o_part = o_part;
+  p.o_half = shape->partial_dtype == MLA_FP16;
   p.lse_part = lse_part;
   p.seq_lens = seq_lens;
   p.B = shape->batch;

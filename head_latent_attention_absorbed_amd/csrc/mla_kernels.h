@@ -26,7 +26,8 @@ struct DecodeParams {
   int32_t block_size;        // tokens per page: 32 * 2^k
   int32_t block_shift;       // log2(block_size)
   float scale_log2;          // softmax_scale * log2(e)
-  float* o_part;             // fp32 [parts, R, DC]
+  void* o_part;              // fp32 or fp16 [parts, R, DC]
+  int32_t o_half;            // o_part holds fp16
   float* lse_part;           // fp32 [parts, R]
 };
 
@@ -39,7 +40,8 @@ int decode_wgs_per_cu(int R, int d_latent);
 hipError_t launch_decode(const DecodeParams& p, int d_latent, bool fp8, hipStream_t stream);
 
 struct CombineParams {
-  const float* o_part;
+  const void* o_part;        // fp32 or fp16 [parts, R, DC]
+  int32_t o_half;
   const float* lse_part;
   const int32_t* seq_lens;
   int32_t B, R, G, DC;

@@ -9,7 +9,7 @@ from __future__ import annotations
 import numpy as np
 
 from .binding import (
-    MLA_BF16, MLA_FP8_E4M3, MLA_FP32, MLA_TILE_TOKENS, MlaShape,
+    MLA_BF16, MLA_FP8_E4M3, MLA_FP16, MLA_FP32, MLA_TILE_TOKENS, MlaShape,
     mla_absorb_q, mla_decode_num_parts, mla_decode_paged, mla_combine_lse, mla_up_v,
 )
 
@@ -47,9 +47,13 @@ def _dev_bits(torch, arr: np.ndarray, device, dtype):
 
 
 class DecodeStep:
-    def __init__(self, inputs: dict, device: str = "cuda", num_parts: int | None = None):
+    def __init__(self, inputs: dict, device: str = "cuda", num_parts: int | None = None, partial: str = "fp16"):
+        """``partial`` is the element type of the split partials o_part:
+        "fp16" (half the bytes) or "fp32"."""
         import torch
 
+        if partial not in ("fp16", "fp32"):
+            raise ValueError(f"partial must be 'fp16' or 'fp32', not {partial!r}")
         self.torch = torch
         w = inputs["workload"]
         self.workload = w
@@ -58,7 +62,8 @@ class DecodeStep:
             batch=w.batch, num_heads=w.heads, q_len=w.q_len, d_latent=w.d_latent, d_nope=w.d_nope,
             d_rope=w.d_rope, d_v=w.d_v, block_size=w.block_size, max_blocks_per_seq=w.max_blocks_per_seq,
             softmax_scale=float(inputs["softmax_scale"]), cache_dtype=MLA_FP8_E4M3 if fp8 else MLA_BF16,
-            out_dtype=MLA_FP32 if w.out_dtype == "fp32" else MLA_BF16)
+            out_dtype=MLA_FP32 if w.out_dtype == "fp32" else MLA_BF16,
+            partial_dtype=MLA_FP16 if partial == "fp16" else MLA_FP32)
         bf16 = torch.bfloat16
         self.q_nope = _dev_bits(torch, inputs["q_nope"], device, bf16)
         self.q_rope = _dev_bits(torch, inputs["q_rope"], device, bf16)
@@ -76,7 +81,8 @@ class DecodeStep:
         R = S * H
         f32 = torch.float32
         self.q_lat = torch.empty((B, S, H, DC), dtype=bf16, device=device)
-        self.o_part = torch.empty((self.num_parts, R, DC), dtype=f32, device=device)
+        self.o_part = torch.empty((self.num_parts, R, DC), dtype=torch.float16 if partial == "fp16" else f32,
+                                  device=device)
         self.lse_part = torch.empty((self.num_parts, R), dtype=f32, device=device)
         self.o_lat = torch.empty((B, S, H, DC), dtype=f32, device=device)
         self.lse = torch.empty((B, S, H), dtype=f32, device=device)

@@ -68,7 +68,7 @@ typedef enum {
   MLA_ERR_HIP = 3          /* a HIP runtime call (device query or launch) failed         */
 } mla_status_t;
 
-typedef enum { MLA_BF16 = 0, MLA_FP8_E4M3 = 1, MLA_FP32 = 2 } mla_dtype_t;
+typedef enum { MLA_BF16 = 0, MLA_FP8_E4M3 = 1, MLA_FP32 = 2, MLA_FP16 = 3 } mla_dtype_t;
 
 /* Tokens per decode tile; the split plan below is counted in tiles. */
 #define MLA_TILE_TOKENS 32
@@ -86,6 +86,7 @@ typedef struct {
   float softmax_scale;        /* multiplies q.k; usually 1/sqrt(d_nope + d_rope) */
   mla_dtype_t cache_dtype;    /* MLA_BF16 or MLA_FP8_E4M3                        */
   mla_dtype_t out_dtype;      /* MLA_BF16 or MLA_FP32 (dtype of `out`)           */
+  mla_dtype_t partial_dtype;  /* MLA_FP32 or MLA_FP16 (dtype of `o_part`)        */
 } mla_shape_t;
 
 /*
@@ -138,26 +139,30 @@ mla_status_t mla_decode_num_parts(const mla_shape_t* shape, int32_t* num_parts);
  *   touches it writes slot (b + g): the partial over positions
  *   [max(cu_b, g*W) - cu_b, min(cu_{b+1}, (g+1)*W) - cu_b) * MLA_TILE_TOKENS,
  *   clipped to what each query may see.
- * o_part   fp32 [num_parts, R, d_latent]: sum_t p_t c_t, normalised within the split
+ * o_part   [num_parts, R, d_latent] in shape->partial_dtype: sum_t p_t c_t,
+ *          normalised within the split (a convex combination of latent rows).
+ *          MLA_FP16 (round to nearest even) halves the bytes written here and
+ *          read back by mla_combine_lse; it needs |latent value| < 65504 (the
+ *          scaled value for an e4m3 cache), else the row becomes +-inf/NaN.
  * lse_part fp32 [num_parts, R]: the split's log-sum-exp (-inf if it sees nothing)
  * Slots that no (sequence, part) pair maps to are left untouched.
  */
 mla_status_t mla_decode_paged(const mla_shape_t* shape, const void* q_lat, const void* q_rope,
                               const void* c_kv, const void* k_rope, int64_t token_stride,
                               int64_t block_stride, const float* kv_scale, const int32_t* block_table,
-                              const int32_t* seq_lens, int32_t num_parts, float* o_part,
+                              const int32_t* seq_lens, int32_t num_parts, void* o_part,
                               float* lse_part, hipStream_t stream);
 
 /*
  * mla_combine_lse -- merge the splits written by mla_decode_paged (same
- * shape, num_parts and seq_lens):
+ * shape, including partial_dtype, num_parts and seq_lens):
  *   lse[b,r]   = log sum_k exp(lse_part[k,r])
  *   o_lat[b,r] = sum_k exp(lse_part[k,r] - lse[b,r]) o_part[k,r]
  * over sequence b's slots; splits with lse = -inf weigh nothing; a row with
  * no visible position gets o_lat = 0 and lse = -inf.
  *   o_lat fp32 [B, S_q, H, d_latent], lse fp32 [B, S_q, H] (written)
  */
-mla_status_t mla_combine_lse(const mla_shape_t* shape, int32_t num_parts, const float* o_part,
+mla_status_t mla_combine_lse(const mla_shape_t* shape, int32_t num_parts, const void* o_part,
                              const float* lse_part, const int32_t* seq_lens, float* o_lat, float* lse,
                              hipStream_t stream);
 

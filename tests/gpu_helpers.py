@@ -50,11 +50,11 @@ def compare(name, got, ref, tol_abs, tol_rel, finite_only=False, scaled_abs=True
     return max_abs, rel
 
 
-def run_step(inputs, num_parts=None, poison=True):
+def run_step(inputs, num_parts=None, poison=True, partial="fp16"):
     import torch
     from head_latent_attention_absorbed_amd import DecodeStep
 
-    st = DecodeStep(inputs, num_parts=num_parts)
+    st = DecodeStep(inputs, num_parts=num_parts, partial=partial)
     if poison:
         for t in (st.q_lat, st.o_part, st.lse_part, st.o_lat, st.lse, st.out):
             t.fill_(float("nan"))

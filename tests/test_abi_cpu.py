@@ -29,9 +29,26 @@ def test_exports_every_declared_symbol():
         assert hasattr(lib, name)
 
 
-def test_struct_layout_matches_header():
-    assert ctypes.sizeof(MlaShape) == 12 * 4
-    assert MlaShape.softmax_scale.offset == 36
+def test_struct_layout_matches_header(tmp_path):
+    """Compile a C program against the header and compare sizeof/offsetof of
+    mla_shape_t with the ctypes mirror field by field."""
+    names = [f[0] for f in MlaShape._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text(
+        "#include <stdio.h>\n#include <stddef.h>\n#include \"mla_absorbed.h\"\n"
+        "int main(void) {\n  printf(\"%zu\\n\", sizeof(mla_shape_t));\n"
+        + "".join(f'  printf("%zu\\n", offsetof(mla_shape_t, {n}));\n' for n in names)
+        + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    from head_latent_attention_absorbed_amd import binding
+    inc = os.path.dirname(binding.header_path)
+    r = subprocess.run(["gcc", "-std=c11", "-D__HIP_PLATFORM_AMD__", f"-I{inc}", "-I/opt/rocm/include", str(src),
+                        "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(MlaShape)
+    for n, off in zip(names, vals[1:]):
+        assert getattr(MlaShape, n).offset == off, n
 
 
 def _shape(**kw):
@@ -49,6 +66,7 @@ FAKE = 1 << 40  # a 16-byte aligned address; never dereferenced by failing calls
     (dict(softmax_scale=math.inf), mla.MLA_ERR_INVALID_ARG),
     (dict(cache_dtype=7), mla.MLA_ERR_INVALID_ARG),
     (dict(out_dtype=mla.MLA_FP8_E4M3), mla.MLA_ERR_INVALID_ARG),
+    (dict(partial_dtype=mla.MLA_BF16), mla.MLA_ERR_INVALID_ARG),
     (dict(d_latent=384), mla.MLA_ERR_UNSUPPORTED),
     (dict(d_rope=32), mla.MLA_ERR_UNSUPPORTED),
     (dict(block_size=48), mla.MLA_ERR_UNSUPPORTED),

@@ -90,6 +90,16 @@ def test_small_parity_default_split(name):
     _check_all(inputs, st)
 
 
+@pytest.mark.parametrize("name", ["tiny", "h128_ragged", "dc256", "fp8_sq4_h64", "idle_slot", "h32"])
+def test_small_parity_fp32_partials(name):
+    """The same step with fp32 split partials (o_part) instead of fp16."""
+    inputs = make_inputs(SMALL_CASES[name])
+    _announce(f"{name}/fp32-partials", inputs)
+    st = run_step(inputs, partial="fp32")
+    assert str(st.o_part.dtype) == "torch.float32"
+    _check_all(inputs, st)
+
+
 @pytest.mark.parametrize("name", ["h128_ragged", "dc256", "fp8_sq4_h64", "h32"])
 @pytest.mark.parametrize("extra_parts", [0, 1, 5])
 def test_small_parity_few_splits(name, extra_parts):
