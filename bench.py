@@ -13,6 +13,7 @@ Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload deepsee
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -52,6 +53,54 @@ def algorithmic(w, seq_lens):
                 step_flops=attn_flops + proj_flops, record_bytes=rec, tokens=sum(L))
 
 
+KERNEL_SOURCES = ("decode.hip", "mla_device.h", "mla_kernels.h")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the sources the decode kernel is built from."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "head_latent_attention_absorbed_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by a copy kernel's reading), or None
+    when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(mb: int, reps: int = 3):
+    """A plain device copy of known size (read mb MB, write mb MB), launched
+    after the timed region so that a counter run sees a kernel whose HBM bytes
+    are known; its FETCH_SIZE / WRITE_SIZE readings calibrate the decode's."""
+    import torch
+
+    n = mb * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.add(src, 0.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy probe: {reps} x add(out=) over {mb} MiB fp32 (read {n * 4} B, write {n * 4} B per launch)")
+
+
 def cpu_baseline(inputs, budget_s: float):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload:
     whole sequences, all heads, until about ``budget_s`` seconds of CPU work."""
@@ -84,6 +133,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--partial", default="fp16", choices=("fp16", "fp32"), help="element type of the split partials")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after timing, run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -183,13 +234,15 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name) if args.partial == "fp16" else None,
             "algorithmic_bytes_per_launch": alg["decode_bytes"],
             "avg_launch_us": round(dec_us, 2),
             "mfma_frac": round(alg["attn_flops"] / (dec_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         },
         "wall_s": round(wall, 3),
     }
+    if args.copy_probe_mb > 0:
+        copy_probe(args.copy_probe_mb)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(inputs, args.cpu_budget)
         try:
