@@ -27,6 +27,8 @@
 // DMA instruction fills two rows; the K-operand reads of eight lanes cover one
 // contiguous 128-byte run, and the sixteen lanes of a transposing V read hit
 // 32 distinct banks.
+#include <type_traits>
+
 #include "mla_device.h"
 #include "mla_kernels.h"
 
@@ -36,6 +38,9 @@ namespace {
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRebase = 8.0f;  // log2 of the largest unnormalised weight kept between re-bases
 constexpr int kRow = kTile * 16;  // bytes of one granule row of a tile
+constexpr int kTab = 128;  // tiles per LDS source-table fill
+constexpr int kPvAhead = 2;     // V blocks read ahead of their MFMAs
+constexpr int kScoreAhead = 4;  // K fragments read ahead of their MFMAs
 
 __device__ __forceinline__ void block_sync() {
   // Work-group barrier for LDS hand-offs: waits for this wave's LDS traffic,
@@ -114,6 +119,26 @@ __device__ __forceinline__ void issue_tile_dma(const DecodeParams& p, const char
   }
 }
 
+// The same copy, one instruction at a time, so that the instructions can be
+// spread over the MFMA stream of the score product instead of being issued in
+// one burst (a burst stalls the wave while the texture unit accepts it).
+template <int DC, int NW>
+struct TileDma {
+  static constexpr int NI = Geo<DC>::GPT / (2 * NW);
+  const char* run;
+  int64_t rope_off;
+  uint32_t lane_off, buf_lds;
+  int w;
+  __device__ __forceinline__ void issue(int q) const {
+    const int g0 = 2 * (q * NW + w);
+    const int64_t off = g0 < Geo<DC>::GC ? (int64_t)g0 * 16 : rope_off + (int64_t)(g0 - Geo<DC>::GC) * 16;
+    lds_dma16(run + off, lane_off, uniform(buf_lds + (q * NW + w) * 1024));
+  }
+};
+struct NoDma {
+  __device__ __forceinline__ void issue(int) const {}
+};
+
 // Zero the slots of tokens nv..31 of a tile (the last, partial tile of a
 // sequence): their DMA'd contents are whatever the page held past the length.
 template <int DC, int NW>
@@ -161,16 +186,30 @@ struct Fp8Stage {
   }
 };
 
+// Score MFMAs with VGPR accumulators.  The hardware forwards an MFMA result
+// to the accumulator input of the next MFMA of the same chain; a VALU read of
+// the result needs wait states that the compiler cannot see through inline
+// asm, so every chain ends with mfma_v_drain before its values are used.
+__device__ __forceinline__ void mfma_v_first(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_drain(f32x16& x, f32x16& y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+}
+
 // Scores of one 32-token tile and the online-softmax update, without
 // branches: returns P (the B operand of the P.V product) and the factor
 // alpha by which the accumulators must be multiplied before P.V of this tile
 // is added (1 unless the row maximum grew by more than 2^kRebase).
-template <int DC, bool FP8>
+template <int DC, bool FP8, int NDMA, class Dma>
 __device__ __forceinline__ void score_tile(const char* tb, const float* tsc, const bf16x8 (&qf)[Geo<DC>::KS],
                                            float& m_run, float& l_run, int pos0, int limit, float slog2,
-                                           bf16x8& pf0, bf16x8& pf1, float& alpha) {
+                                           bf16x8& pf0, bf16x8& pf1, float& alpha, const Dma& dma) {
   using Gm = Geo<DC>;
-  constexpr int PD = 4;  // k-steps of K fragments read ahead of their MFMA
+  constexpr int PD = kScoreAhead;  // k-steps of K fragments read ahead of their MFMA
   const int lane = opaque_lane();
   const int half = lane >> 5, col = lane & 31;
 
@@ -180,21 +219,22 @@ __device__ __forceinline__ void score_tile(const char* tb, const float* tsc, con
   bf16x8 kf[Gm::KS];
 #pragma unroll
   for (int ks = 0; ks < PD; ++ks) kf[ks] = *(const bf16x8*)(kb + ks * 2 * kRow);
-  f32x16 sacc0 = f32x16{}, sacc1 = f32x16{};
+  // The score accumulators are kept in VGPRs (inline-asm MFMAs): the
+  // accumulator registers are all taken by O^T, and left to itself the
+  // compiler would park part of O^T in VGPRs around every tile.  Program
+  // order is the issue order: read ks + PD, then the MFMA of k-step ks.
+  f32x16 sacc0, sacc1;
+  static_assert(NDMA == 0 || Gm::KS % NDMA == 0, "DMA instructions must divide the k-steps");
 #pragma unroll
   for (int ks = 0; ks < Gm::KS; ++ks) {
     if (ks + PD < Gm::KS) kf[ks + PD] = *(const bf16x8*)(kb + (ks + PD) * 2 * kRow);
-    if (ks & 1) sacc1 = mfma32(kf[ks], qf[ks], sacc1); else sacc0 = mfma32(kf[ks], qf[ks], sacc0);
+    if constexpr (NDMA > 0) {
+      if (ks % (Gm::KS / NDMA) == 0) dma.issue(ks / (Gm::KS / NDMA));  // next tile's copy, spread out
+    }
+    if (ks < 2) mfma_v_first(ks ? sacc1 : sacc0, kf[ks], qf[ks]);
+    else mfma_v_acc((ks & 1) ? sacc1 : sacc0, kf[ks], qf[ks]);
   }
-  // Order: the PD leading fragment reads, then (read ks + PD, MFMA ks), then
-  // the last PD MFMAs -- each MFMA's operand was requested PD MFMAs earlier.
-  __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
-#pragma unroll
-  for (int ks = 0; ks < Gm::KS - PD; ++ks) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read of k-step ks + PD
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA of k-step ks
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, PD, 0);
+  mfma_v_drain(sacc0, sacc1);
   const f32x16 sacc = sacc0 + sacc1;
   // The score product is its own scheduling region: nothing that follows
   // (the softmax, or the lagged P.V of the previous tile) is hoisted into it.
@@ -240,11 +280,11 @@ __device__ __forceinline__ void score_tile(const char* tb, const float* tsc, con
   pf1 = pack_bf16x8(pv + 8);
 }
 
-// O^T += V^T . P^T for one tile; the four transposed reads of block nb+1 are
-// issued before the two MFMAs of block nb.  Source lane (group G = lane/16,
+// O^T += V^T . P^T for one tile; the four transposed reads of block nb + AH
+// are issued before the two MFMAs of block nb.  Source lane (group G = lane/16,
 // i = lane%16) reads token 16 j2 + 8 h + 4 (G/2) + i/4 and columns
 // 32 nb + 16 (G%2) + 4 (i%4) .. +3.
-template <int DC, int VALU_PER_BLOCK>
+template <int DC, int AH, bool FIRST>
 __device__ __forceinline__ void pv_tile(const char* tb, bf16x8 pf0, bf16x8 pf1, f32x16 (&O)[Geo<DC>::NB]) {
   using Gm = Geo<DC>;
   const int lane = opaque_lane();
@@ -263,25 +303,25 @@ __device__ __forceinline__ void pv_tile(const char* tb, bf16x8 pf0, bf16x8 pf1, 
     f.y1 = lds_read_tr16(a + 24 * 16);
     return f;
   };
-  VF cur = vread(0);
+  VF vf[Gm::NB];
+#pragma unroll
+  for (int nb = 0; nb < AH; ++nb) vf[nb] = vread(nb);
 #pragma unroll
   for (int nb = 0; nb < Gm::NB; ++nb) {
-    VF nxt;
-    if (nb + 1 < Gm::NB) nxt = vread(nb + 1);
+    if (nb + AH < Gm::NB) vf[nb + AH] = vread(nb + AH);
+    const VF& cur = vf[nb];
     const s16x8 a0 = {cur.x0[0], cur.x0[1], cur.x0[2], cur.x0[3], cur.x1[0], cur.x1[1], cur.x1[2], cur.x1[3]};
     const s16x8 a1 = {cur.y0[0], cur.y0[1], cur.y0[2], cur.y0[3], cur.y1[0], cur.y1[1], cur.y1[2], cur.y1[3]};
-    O[nb] = mfma32((bf16x8)a0, pf0, O[nb]);
+    O[nb] = mfma32((bf16x8)a0, pf0, FIRST ? f32x16{} : O[nb]);  // the first tile starts the sums
     O[nb] = mfma32((bf16x8)a1, pf1, O[nb]);
-    cur = nxt;
   }
-  // Order: the four reads of block 0, then per block (reads of block nb + 1,
-  // MFMAs of block nb[, some independent VALU work of the caller]).
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+  // Order: the reads of the first AH blocks, then per block (reads of block
+  // nb + AH, MFMAs of block nb).
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 * AH, 1);
 #pragma unroll
   for (int nb = 0; nb < Gm::NB; ++nb) {
-    if (nb + 1 < Gm::NB) __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+    if (nb + AH < Gm::NB) __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-    if (VALU_PER_BLOCK > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER_BLOCK, 1);
   }
 }
 
@@ -309,16 +349,57 @@ __device__ __forceinline__ void rescale(f32x16 (&O)[Geo<DC>::NB], float alpha) {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// LAG: P.V of tile k runs while the softmax of tile k+1 is computed (one
-// basic block, so MFMA and VALU work interleave); needs one extra ring buffer.
-template <int DC, bool FP8, int NW, int NBUF, bool LAG>
+// Write NBK accumulator blocks (32 latent columns each, starting at element
+// offset `base` of o_part) scaled by inv, as fp16 or fp32.
+template <int NBK>
+__device__ __forceinline__ void store_partial(const DecodeParams& p, const f32x16* O, float inv, int64_t base,
+                                              int half) {
+  if (p.o_half) {
+    // Lane pair (l, l + 32) swaps packed halves so that each lane stores 8
+    // consecutive columns: with column quarters q0..q3 of an 8-column group
+    // split 4 + 4 over the pair, the swap gives the lower lane the odd group
+    // and the upper lane the even one.
+    _Float16* dst = (_Float16*)p.o_part + base + 8 * (1 - half);
+#pragma unroll
+    for (int nb = 0; nb < NBK; ++nb) {
+      uint32_t h[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f16x2 v = {(_Float16)(O[nb][2 * j] * inv), (_Float16)(O[nb][2 * j + 1] * inv)};
+        h[j] = __builtin_bit_cast(uint32_t, v);
+      }
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {  // 8-column groups (2pr, 2pr + 1)
+        const auto r0 = __builtin_amdgcn_permlane32_swap(h[4 * pr + 2], h[4 * pr], false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(h[4 * pr + 3], h[4 * pr + 1], false, false);
+        const uint4 v = {r0[0], r1[0], r0[1], r1[1]};
+        *(uint4*)(dst + 32 * nb + 16 * pr) = v;
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one accumulator block at a time
+    }
+  } else {
+    float* dst = (float*)p.o_part + base + 4 * half;
+#pragma unroll
+    for (int nb = 0; nb < NBK; ++nb) {
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        const f32x4 v = {O[nb][4 * ig] * inv, O[nb][4 * ig + 1] * inv, O[nb][4 * ig + 2] * inv,
+                         O[nb][4 * ig + 3] * inv};
+        *(f32x4*)(dst + 32 * nb + 8 * ig) = v;
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one accumulator block at a time
+    }
+  }
+}
+
+template <int DC, bool FP8, int NW, int NBUF>
 __global__ void __launch_bounds__(NW * kWave)
     decode_kernel(DecodeParams p, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ block_table,
                   const float* __restrict__ kv_scale) {
   using Gm = Geo<DC>;
   constexpr int TB = Gm::TILE_BYTES;
   constexpr int NI = Gm::GPT / (2 * NW);
-  constexpr int AHEAD = NBUF - 1 - (LAG ? 1 : 0);  // tiles in flight ahead of the one computed
+  constexpr int AHEAD = NBUF - 1;  // tiles in flight ahead of the one computed
   static_assert(Gm::GPT % (2 * NW) == 0, "tile rows must split evenly over the waves");
   static_assert(AHEAD >= 1, "ring too small");
   static_assert(FP8 || NI * (AHEAD - 1) <= 63, "DMA groups must fit vmcnt");
@@ -327,6 +408,7 @@ __global__ void __launch_bounds__(NW * kWave)
   __shared__ __attribute__((aligned(1024))) char tiles[NBUF * TB];
   __shared__ __attribute__((aligned(16))) float tscale[FP8 ? NBUF * kTile : 4];
   __shared__ int cu[kMaxBatch + 1];
+  __shared__ int4 tab[kTab];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = uniform(tid >> 6);
@@ -349,53 +431,67 @@ __global__ void __launch_bounds__(NW * kWave)
   const int row = rg * (32 * NW) + 32 * w + col;  // this lane's query row (S^T column)
   const uint32_t tiles_lds = lds_offset(tiles);
 
-  // ---- tile loader: next tile to load (kl, sequence bl) and its source run.
+  // ---- tile source table: page, position and valid-token count of each tile
+  // this part loads, kTab tiles at a time in LDS, so that starting a tile's
+  // copy needs no memory round trip (a block-table read in the loop would).
+  int tab0 = k0;
+  auto fill_tab = [&](int from) {  // all threads; followed by block_sync()
+    for (int i = tid; i < kTab; i += NW * kWave) {
+      const int kk = from + i;
+      if (kk < k1) {
+        const int b = seq_of_tile(cu, p.B, kk);
+        const int pos0 = (kk - cu[b]) * kTile;
+        const int page = block_table[(int64_t)b * p.bt_stride + (pos0 >> p.block_shift)];
+        tab[i] = int4{page, pos0, min(seq_lens[b] - pos0, kTile), 0};
+      }
+    }
+  };
+  fill_tab(k0);
+  block_sync();
+
+  // ---- tile loader: next tile to load (kl) and its source.
   int kl = k0;
-  int bl = uniform(seq_of_tile(cu, p.B, k0));
-  auto run_of = [&](int b, int j) -> const char* {
-    b = uniform(b);
-    j = uniform(j);
-    const int pos0 = j * kTile;
-    const int page = block_table[(int64_t)b * p.bt_stride + (pos0 >> p.block_shift)];
-    return p.c_kv + (int64_t)page * p.block_stride + (int64_t)(pos0 & (p.block_size - 1)) * p.token_stride;
+  int spage = 0, spos = 0, snv = 0;
+  const char* src = p.c_kv;
+  auto locate = [&]() {  // source of tile kl < k1 (called by all waves together)
+    if (kl - tab0 == kTab) {
+      block_sync();
+      tab0 = kl;
+      fill_tab(kl);
+      block_sync();
+    }
+    const int4 e = tab[kl - tab0];
+    spage = uniform(e.x);
+    spos = uniform(e.y);
+    snv = uniform(e.z);
+    src = p.c_kv + (int64_t)spage * p.block_stride + (int64_t)(spos & (p.block_size - 1)) * p.token_stride;
   };
-  auto advance = [&]() {
-    ++kl;
-    while (bl < p.B - 1 && kl >= uniform(cu[bl + 1])) ++bl;
-  };
-  const char* src = run_of(bl, kl - uniform(cu[bl]));
+  locate();
   auto dma_next = [&]() {  // bf16: start the copy of tile kl into its ring slot
     const int ol = opaque_lane();
     const uint32_t lane_off = (uint32_t)load_token(ol) * (uint32_t)p.token_stride + 16u * (ol >> 5);
     issue_tile_dma<DC, NW>(p, src, lane_off, tiles_lds + ((kl - k0) % NBUF) * TB, w);
-    advance();
-    if (kl < k1) src = run_of(bl, kl - uniform(cu[bl]));
+    ++kl;
+    if (kl < k1) locate();
   };
 
   Fp8Stage<DC, NW> stage;
-  auto stage_scales = [&](int b, int j, int sbuf) {
-    if (w == 0 && lane < kTile) {
-      const int pos0 = j * kTile;
-      const int nv = seq_lens[b] - pos0;
-      const int page = block_table[(int64_t)b * p.bt_stride + (pos0 >> p.block_shift)];
-      const float s = kv_scale[(int64_t)page * p.block_size + (pos0 & (p.block_size - 1)) + lane];
-      tscale[sbuf * kTile + lane] = lane < nv ? s : 0.0f;
-    }
-  };
   auto stage_finish = [&]() {  // fp8: decode the loaded tile kl into its ring slot
     const int nbuf = (kl - k0) % NBUF;
-    const int jl = kl - uniform(cu[bl]);
     const int ol = opaque_lane();
     const uint32_t lane_off8 = (uint32_t)load_token(ol) * (uint32_t)p.token_stride + 8u * (ol >> 5);
-    const bool valid = load_token(ol) < seq_lens[bl] - jl * kTile;
+    const bool valid = load_token(ol) < snv;
     stage.store_chunk(tiles + nbuf * TB, 0, w, ol, valid);
     for (int c0 = Fp8Stage<DC, NW>::CH; c0 < Fp8Stage<DC, NW>::NI; c0 += Fp8Stage<DC, NW>::CH) {
       stage.load_chunk(p, src, lane_off8, c0, w);
       stage.store_chunk(tiles + nbuf * TB, c0, w, ol, valid);
     }
-    stage_scales(bl, jl, nbuf);
-    advance();
-    if (kl < k1) src = run_of(bl, kl - uniform(cu[bl]));
+    if (w == 0 && lane < kTile) {
+      const float sc = kv_scale[(int64_t)spage * p.block_size + (spos & (p.block_size - 1)) + lane];
+      tscale[nbuf * kTile + lane] = lane < snv ? sc : 0.0f;
+    }
+    ++kl;
+    if (kl < k1) locate();
   };
   auto stage_start = [&]() {
     const int ol = opaque_lane();
@@ -424,7 +520,6 @@ __global__ void __launch_bounds__(NW * kWave)
         zero_tail<DC, NW>(tiles + buf * TB, L - (k - cub) * kTile, tid);
         block_sync();
       }
-      if (kl < k1) dma_next();
     } else {
       if (kl < k1) stage_start();
     }
@@ -447,8 +542,10 @@ __global__ void __launch_bounds__(NW * kWave)
 
     bf16x8 qf[Gm::KS];
     if (row < p.R) {
-      const bf16x8* ql = (const bf16x8*)(p.q_lat + ((int64_t)bc * p.R + row) * DC + 8 * half);
-      const bf16x8* qr = (const bf16x8*)(p.q_rope + ((int64_t)bc * p.R + row) * 64 + 8 * half);
+      const int ln = opaque_lane();
+      const int qrow = rg * (32 * NW) + 32 * w + (ln & 31);
+      const bf16x8* ql = (const bf16x8*)(p.q_lat + ((int64_t)bc * p.R + qrow) * DC + 8 * (ln >> 5));
+      const bf16x8* qr = (const bf16x8*)(p.q_rope + ((int64_t)bc * p.R + qrow) * 64 + 8 * (ln >> 5));
 #pragma unroll
       for (int ks = 0; ks < DC / 16; ++ks) qf[ks] = ql[2 * ks];
 #pragma unroll
@@ -462,105 +559,67 @@ __global__ void __launch_bounds__(NW * kWave)
       for (int ks = 0; ks < Gm::KS; ++ks) qf[ks] = bf16x8{};
     }
     f32x16 O[Gm::NB];
-#pragma unroll
-    for (int nb = 0; nb < Gm::NB; ++nb) O[nb] = f32x16{};
     float m_run = -__builtin_inff(), l_run = 0.0f;
     bf16x8 pf0, pf1;
     float alpha;
 
-    if constexpr (LAG) {
-      // first tile: scores only (the accumulators are still zero, so no rescale)
+    // One tile.  The first tile of a segment starts the accumulators with its
+    // P.V (a zero accumulator input), so O needs no initialisation and no
+    // rescale there (alpha is 0 or 1 on a first tile, and O would be 0).
+    auto one_tile = [&](auto first_tag) {
+      constexpr bool FIRST = decltype(first_tag)::value;
       tile_begin(k, cub, L);
-      score_tile<DC, FP8>(tiles + ((k - k0) % NBUF) * TB, tscale + ((k - k0) % NBUF) * kTile, qf, m_run, l_run,
-                          (k - cub) * kTile, limit, p.scale_log2, pf0, pf1, alpha);
-      tile_end();
-      for (++k; k < kend; ++k) {
-        tile_begin(k, cub, L);
-        const int buf = (k - k0) % NBUF;
-        bf16x8 nf0, nf1;
-        score_tile<DC, FP8>(tiles + buf * TB, tscale + buf * kTile, qf, m_run, l_run, (k - cub) * kTile, limit,
-                            p.scale_log2, nf0, nf1, alpha);
-        // P.V of tile k-1 interleaved with the softmax VALU work of tile k.
-        pv_tile<DC, 128 / Geo<DC>::NB>(tiles + ((k - 1 - k0) % NBUF) * TB, pf0, pf1, O);
-        __builtin_amdgcn_sched_barrier(0);
-        if (__any(alpha != 1.0f)) rescale<DC>(O, alpha);
-        pf0 = nf0;
-        pf1 = nf1;
-        tile_end();
+      const int buf = (k - k0) % NBUF;
+      if (!FP8 && kl < k1) {
+        // the copy of tile kl (AHEAD tiles on) is issued inside the score product
+        const int ol = opaque_lane();
+        const TileDma<DC, NW> dma{src, p.rope_off,
+                                  (uint32_t)load_token(ol) * (uint32_t)p.token_stride + 16u * (ol >> 5),
+                                  tiles_lds + (uint32_t)(((kl - k0) % NBUF) * TB), w};
+        score_tile<DC, FP8, TileDma<DC, NW>::NI>(tiles + buf * TB, tscale + buf * kTile, qf, m_run, l_run,
+                                                 (k - cub) * kTile, limit, p.scale_log2, pf0, pf1, alpha, dma);
+        ++kl;
+        if (kl < k1) locate();
+      } else {
+        score_tile<DC, FP8, 0>(tiles + buf * TB, tscale + buf * kTile, qf, m_run, l_run, (k - cub) * kTile, limit,
+                               p.scale_log2, pf0, pf1, alpha, NoDma{});
       }
-      pv_tile<DC, 0>(tiles + ((k - 1 - k0) % NBUF) * TB, pf0, pf1, O);
-    } else {
-      // A segment holds at least one tile; with the loop written bottom-tested
-      // the accumulators leave it only as MFMA results, so the epilogue reads
-      // them block by block instead of copying all of them out at once.
-      do {
-        tile_begin(k, cub, L);
-        const int buf = (k - k0) % NBUF;
-        score_tile<DC, FP8>(tiles + buf * TB, tscale + buf * kTile, qf, m_run, l_run, (k - cub) * kTile, limit,
-                            p.scale_log2, pf0, pf1, alpha);
+      if constexpr (!FIRST) {
         if (__any(alpha != 1.0f)) rescale<DC>(O, alpha);
-        pv_tile<DC, 0>(tiles + buf * TB, pf0, pf1, O);
-        tile_end();
-        ++k;
-      } while (k < kend);
-    }
+      }
+      pv_tile<DC, kPvAhead, FIRST>(tiles + buf * TB, pf0, pf1, O);
+      tile_end();
+      ++k;
+    };
+    one_tile(std::true_type{});
+    while (k < kend) one_tile(std::false_type{});
 
     // ---- normalise and write this (sequence, part) partial
     const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -__builtin_inff();
     const int64_t slot = (int64_t)bc + g;
-    if (row < p.R) {
-      // The lse goes first: vector stores count in vmcnt, so any wait the
-      // compiler places before a later store (a spilled address being
-      // reloaded) would otherwise also wait for the whole partial to be written.
-      if (half == 0) p.lse_part[slot * p.R + row] = lse;
-      if (p.o_half) {
-        // fp16 partial.  Lane pair (l, l + 32) swaps packed halves so that each
-        // lane stores 8 consecutive columns: with column quarters q0..q3 of an
-        // 8-column group split 4 + 4 over the pair, the swap gives the lower
-        // lane the odd group and the upper lane the even one.
-        _Float16* dst = (_Float16*)p.o_part + (slot * p.R + row) * DC + 8 * (1 - half);
-#pragma unroll
-        for (int nb = 0; nb < Gm::NB; ++nb) {
-          uint32_t h[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const f16x2 v = {(_Float16)(O[nb][2 * j] * inv), (_Float16)(O[nb][2 * j + 1] * inv)};
-            h[j] = __builtin_bit_cast(uint32_t, v);
-          }
-#pragma unroll
-          for (int pr = 0; pr < 2; ++pr) {  // 8-column groups (2pr, 2pr + 1)
-            const auto r0 = __builtin_amdgcn_permlane32_swap(h[4 * pr + 2], h[4 * pr], false, false);
-            const auto r1 = __builtin_amdgcn_permlane32_swap(h[4 * pr + 3], h[4 * pr + 1], false, false);
-            const uint4 v = {r0[0], r1[0], r0[1], r1[1]};
-            *(uint4*)(dst + 32 * nb + 16 * pr) = v;
-          }
-          __builtin_amdgcn_sched_barrier(0);  // one accumulator block at a time
-        }
-      } else {
-        float* dst = (float*)p.o_part + (slot * p.R + row) * DC + 4 * half;
-#pragma unroll
-        for (int nb = 0; nb < Gm::NB; ++nb) {
-#pragma unroll
-          for (int ig = 0; ig < 4; ++ig) {
-            const f32x4 v = {O[nb][4 * ig] * inv, O[nb][4 * ig + 1] * inv, O[nb][4 * ig + 2] * inv,
-                             O[nb][4 * ig + 3] * inv};
-            *(f32x4*)(dst + 32 * nb + 8 * ig) = v;
-          }
-          __builtin_amdgcn_sched_barrier(0);  // one accumulator block at a time
-        }
-      }
+    // The lse goes first: vector stores count in vmcnt, so any wait the
+    // compiler places before a later store (a spilled address being reloaded)
+    // would otherwise also wait for the whole partial to be written.
+    {
+      // lane-derived indices recomputed here rather than kept live (and
+      // spilled) across the tile loop
+      const int ln = opaque_lane();
+      const int lhalf = ln >> 5, lcol = ln & 31;
+      const int lrow = rg * (32 * NW) + 32 * w + lcol;
+      if (lrow < p.R && lhalf == 0) p.lse_part[slot * p.R + lrow] = lse;
+      if (lrow < p.R) store_partial<Gm::NB>(p, O, inv, (slot * p.R + lrow) * DC, lhalf);
     }
     ++bc;
     while (bc < p.B - 1 && uniform(cu[bc + 1]) == uniform(cu[bc])) ++bc;
   }
 }
 
-template <int DC, bool FP8, int NW, int NBUF, bool LAG>
+template <int DC, bool FP8, int NW, int NBUF>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   const int grid = p.G * p.RG;
-  hipLaunchKernelGGL((decode_kernel<DC, FP8, NW, NBUF, LAG>), dim3(grid), dim3(NW * kWave), 0, stream, p,
+  hipLaunchKernelGGL((decode_kernel<DC, FP8, NW, NBUF>), dim3(grid), dim3(NW * kWave), 0, stream, p,
                      p.seq_lens, p.block_table, p.kv_scale);
   return hipGetLastError();
 }
@@ -571,13 +630,13 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
 template <int DC, bool FP8>
 hipError_t launch_dc(const DecodeParams& p, int nw, hipStream_t stream) {
   if constexpr (FP8) {
-    if (nw == 4) return launch_one<DC, FP8, 4, 2, false>(p, stream);
-    if (nw == 2) return launch_one<DC, FP8, 2, 2, false>(p, stream);
-    return launch_one<DC, FP8, 1, 2, false>(p, stream);
+    if (nw == 4) return launch_one<DC, FP8, 4, 2>(p, stream);
+    if (nw == 2) return launch_one<DC, FP8, 2, 2>(p, stream);
+    return launch_one<DC, FP8, 1, 2>(p, stream);
   } else {
-    if (nw == 4) return launch_one<DC, FP8, 4, 4, false>(p, stream);
-    if (nw == 2) return launch_one<DC, FP8, 2, 2, false>(p, stream);
-    return launch_one<DC, FP8, 1, 2, false>(p, stream);
+    if (nw == 4) return launch_one<DC, FP8, 4, 4>(p, stream);
+    if (nw == 2) return launch_one<DC, FP8, 2, 2>(p, stream);
+    return launch_one<DC, FP8, 1, 2>(p, stream);
   }
 }
 
