@@ -45,19 +45,20 @@ struct PartRow<4, false> {
   __device__ float at(int i) const { return a[i]; }
 };
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+// The value of x in lane j (j wave-uniform).
+__device__ __forceinline__ float lane_value(float x, int j) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), j));
 }
 
 // One wave per (sequence, query row); lane i owns columns E*i .. E*i + E-1.
-// The splits are visited U at a time with all U loads issued before the
-// first is used (indices past the last split repeat it with weight 0).
+// The splits are visited U at a time: lane j requests the lse of split j of
+// the batch while every lane requests its columns of all U partial rows, so
+// one memory latency covers the whole batch (indices past the last split
+// repeat it with weight 0).
 template <int DC, bool HALF>
 __global__ void __launch_bounds__(256) combine_kernel(CombineParams p, const int32_t* __restrict__ seq_lens) {
   constexpr int E = DC / 64;
-  constexpr int U = 8;
+  constexpr int U = 16;
   __shared__ int cu[kMaxBatch + 1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.x;
@@ -74,35 +75,46 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineParams p, const int
     g0 = cb / Wt;
     g1 = (ce - 1) / Wt;
   }
-  float m = -__builtin_inff();
-  for (int g = g0 + lane; g <= g1; g += kWave) m = fmaxf(m, p.lse_part[((int64_t)b + g) * p.R + row]);
-  m = wave_max(m);
+  float acc[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) acc[i] = 0.0f;
+  float m = -__builtin_inff(), tot = 0.0f;
+  for (int gb = g0; gb <= g1; gb += U) {
+    const int n = min(U, g1 - gb + 1);
+    const float lk = lane < n ? p.lse_part[((int64_t)b + gb + lane) * p.R + row] : -__builtin_inff();
+    PartRow<E, HALF> part[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int64_t slot = (int64_t)b + gb + min(j, n - 1);
+      part[j].load(p.o_part, (slot * p.R + row) * DC + E * lane);
+    }
+    // Keep every load above this point: the lse is waited for while the
+    // partial rows are still in flight.
+    asm volatile("" ::: "memory");
+    // Running maximum over the batches; earlier sums are rescaled when it grows.
+    float mb = m;
+#pragma unroll
+    for (int j = 0; j < U; ++j) mb = fmaxf(mb, lane_value(lk, j));
+    if (mb == -__builtin_inff()) continue;  // nothing visible so far
+    const float r = __expf(m - mb);          // 0 when m = -inf
+    tot *= r;
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[i] *= r;
+    m = mb;
+    const float wl = __expf(lk - m);         // this lane's split weight (0 for -inf)
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const float wj = lane_value(wl, j);  // 0 past the batch's last split
+      tot += wj;
+#pragma unroll
+      for (int i = 0; i < E; ++i) acc[i] += wj * part[j].at(i);
+    }
+  }
   if (m == -__builtin_inff()) {  // the row sees no position
 #pragma unroll
     for (int i = 0; i < E; i += 4) *(f32x4*)(out + i) = f32x4{};
     if (lane == 0) p.lse[(int64_t)b * p.R + row] = -__builtin_inff();
     return;
-  }
-  float acc[E];
-#pragma unroll
-  for (int i = 0; i < E; ++i) acc[i] = 0.0f;
-  float tot = 0.0f;
-  for (int gb = g0; gb <= g1; gb += U) {
-    PartRow<E, HALF> part[U];
-    float wk[U];
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int64_t slot = (int64_t)b + min(gb + j, g1);
-      part[j].load(p.o_part, (slot * p.R + row) * DC + E * lane);
-      wk[j] = p.lse_part[slot * p.R + row];
-    }
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const float wj = (gb + j <= g1) ? __expf(wk[j] - m) : 0.0f;  // exp(-inf) = 0 for empty splits
-      tot += wj;
-#pragma unroll
-      for (int i = 0; i < E; ++i) acc[i] += wj * part[j].at(i);
-    }
   }
   const float inv = 1.0f / tot;
 #pragma unroll

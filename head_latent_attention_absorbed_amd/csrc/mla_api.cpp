@@ -108,6 +108,9 @@ mla_status_t mla_absorb_q(const mla_shape_t* shape, const void* q_nope, const vo
   if (!q_nope || !w_uk || !q_lat) return fail(MLA_ERR_INVALID_ARG, "mla_absorb_q: NULL tensor");
   if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_lat))
     return fail(MLA_ERR_INVALID_ARG, "mla_absorb_q: tensors must be 16-byte aligned");
+  if (!mla::head_gemm_supported(shape->d_nope, shape->d_latent))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_absorb_q: no kernel for d_nope %d, d_latent %d", shape->d_nope,
+                shape->d_latent);
   mla::HeadGemmParams p{};
   p.a = q_nope;
   p.w = static_cast<const uint16_t*>(w_uk);
@@ -217,6 +220,8 @@ mla_status_t mla_up_v(const mla_shape_t* shape, const float* o_lat, const void* 
   if (!o_lat || !w_uv || !out) return fail(MLA_ERR_INVALID_ARG, "mla_up_v: NULL tensor");
   if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out))
     return fail(MLA_ERR_INVALID_ARG, "mla_up_v: tensors must be 16-byte aligned");
+  if (!mla::head_gemm_supported(shape->d_latent, shape->d_v))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_up_v: no kernel for d_latent %d, d_v %d", shape->d_latent, shape->d_v);
   mla::HeadGemmParams p{};
   p.a = o_lat;
   p.w = static_cast<const uint16_t*>(w_uv);

@@ -59,6 +59,8 @@ struct HeadGemmParams {
   int32_t M, H, K, N;
 };
 
+// Whether a kernel exists for reduction depth K and N output columns per head.
+bool head_gemm_supported(int K, int N);
 hipError_t launch_head_gemm(const HeadGemmParams& p, bool a_fp32, bool c_fp32, hipStream_t stream);
 
 }  // namespace mla
