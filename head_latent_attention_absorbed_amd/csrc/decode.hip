@@ -196,25 +196,20 @@ __device__ __forceinline__ void mfma_v_first(f32x16& acc, bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void mfma_v_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void mfma_v_drain(f32x16& x, f32x16& y) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+__device__ __forceinline__ void mfma_v_drain(f32x16& x) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
 }
 
-// Scores of one 32-token tile and the online-softmax update, without
-// branches: returns P (the B operand of the P.V product) and the factor
-// alpha by which the accumulators must be multiplied before P.V of this tile
-// is added (1 unless the row maximum grew by more than 2^kRebase).
-template <int DC, bool FP8, int NDMA, class Dma>
-__device__ __forceinline__ void score_tile(const char* tb, const float* tsc, const bf16x8 (&qf)[Geo<DC>::KS],
-                                           float& m_run, float& l_run, int pos0, int limit, float slog2,
-                                           bf16x8& pf0, bf16x8& pf1, float& alpha, const Dma& dma) {
+// S^T = K . Q^T of one 32-token tile (32 tokens x this wave's 32 rows):
+// A = token `col`, granule 2ks + half, from LDS; B = the query fragments.
+// NDMA > 0 spreads that many instructions of the next tile's copy over
+// the MFMA stream.
+template <int DC, int NDMA, class Dma>
+__device__ __forceinline__ f32x16 score_mfma(const char* tb, const bf16x8 (&qf)[Geo<DC>::KS], const Dma& dma) {
   using Gm = Geo<DC>;
   constexpr int PD = kScoreAhead;  // k-steps of K fragments read ahead of their MFMA
   const int lane = opaque_lane();
   const int half = lane >> 5, col = lane & 31;
-
-  // ---- S^T = K . Q^T  (32 tokens x 32 rows); A = token `col`, granule 2ks + half,
-  // in two independent accumulator chains (even / odd k-steps).
   const char* kb = tb + half * kRow + ((col ^ (half << 2)) << 4);
   bf16x8 kf[Gm::KS];
 #pragma unroll
@@ -223,7 +218,9 @@ __device__ __forceinline__ void score_tile(const char* tb, const float* tsc, con
   // accumulator registers are all taken by O^T, and left to itself the
   // compiler would park part of O^T in VGPRs around every tile.  Program
   // order is the issue order: read ks + PD, then the MFMA of k-step ks.
-  f32x16 sacc0, sacc1;
+  // Dependent MFMAs on one accumulator issue back to back (the hardware
+  // forwards the accumulation), so one chain suffices.
+  f32x16 sacc;
   static_assert(NDMA == 0 || Gm::KS % NDMA == 0, "DMA instructions must divide the k-steps");
 #pragma unroll
   for (int ks = 0; ks < Gm::KS; ++ks) {
@@ -231,53 +228,157 @@ __device__ __forceinline__ void score_tile(const char* tb, const float* tsc, con
     if constexpr (NDMA > 0) {
       if (ks % (Gm::KS / NDMA) == 0) dma.issue(ks / (Gm::KS / NDMA));  // next tile's copy, spread out
     }
-    if (ks < 2) mfma_v_first(ks ? sacc1 : sacc0, kf[ks], qf[ks]);
-    else mfma_v_acc((ks & 1) ? sacc1 : sacc0, kf[ks], qf[ks]);
+    if (ks == 0) mfma_v_first(sacc, kf[ks], qf[ks]);
+    else mfma_v_acc(sacc, kf[ks], qf[ks]);
   }
-  mfma_v_drain(sacc0, sacc1);
-  const f32x16 sacc = sacc0 + sacc1;
+  mfma_v_drain(sacc);
   // The score product is its own scheduling region: nothing that follows
   // (the softmax, or the lagged P.V of the previous tile) is hoisted into it.
   __builtin_amdgcn_sched_barrier(0);
+  return sacc;
+}
 
-  // ---- this lane holds row `col`, tokens 8(i/4) + 4*half + i%4
+// Online-softmax update of one tile's scores, in kSoftmaxSteps steps that
+// can be spread over the MFMAs of the previous tile's P.V (step() with
+// increasing j; all() runs them back to back).  Produces P (the B operand of
+// the P.V product, pf0 | pf1) and the factor alpha by which the accumulators
+// must be multiplied before this tile's P.V is added (1 unless the row
+// maximum grew by more than 2^kRebase).  Lane (col, half) holds row `col`,
+// tokens 8(i/4) + 4 half + i%4 of the tile in value i.
+//
+// `full` (bf16 only, wave-uniform) says every position of the tile is visible
+// to every row: then the maximum is taken over the raw scores (the scale is
+// positive) and each weight is exp2(s * scale - m) with one fused
+// multiply-add, with no masking and no guard (m is finite), in 10 steps.
+constexpr int kSoftmaxSteps = 13;
+template <bool FP8>
+struct Softmax {
+  f32x16 v;          // raw scores, then scaled masked scores, then weights (in place)
+  const float* tsc;  // fp8: the tile's per-token scales (LDS)
+  int pos0, limit;   // tile position in the sequence, first masked position of this row
+  float slog2;       // softmax scale * log2(e)
+  float& m_run;
+  float& l_run;
+  bool full = false;
   float tsv[16];
-  if constexpr (FP8) {
+  float mt, m_new, alpha;
+  bf16x8 pf0, pf1;
+
+  __device__ __forceinline__ void step(int j) {
+    if (!FP8 && full) {
+      fast_step(j);
+      return;
+    }
+    const int half = opaque_lane() >> 5;
+    if (j < 4) {  // scaled, masked scores, four at a time
+      if constexpr (FP8) {
+        const f32x4 s4 = *(const f32x4*)(tsc + 8 * j + 4 * half);
 #pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      const f32x4 s4 = *(const f32x4*)(tsc + 8 * a4 + 4 * half);
+        for (int c = 0; c < 4; ++c) tsv[4 * j + c] = s4[c];
+      }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) tsv[4 * a4 + c] = s4[c];
+      for (int c = 0; c < 4; ++c) {
+        const int i = 4 * j + c;
+        const int tau = 8 * (i >> 2) + 4 * half + (i & 3);
+        float zi = v[i] * slog2;
+        if constexpr (FP8) zi *= tsv[i];
+        v[i] = (pos0 + tau < limit) ? zi : -__builtin_inff();
+      }
+    } else if (j == 4) {
+      mt = v[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, v[i]);
+    } else if (j == 5) {
+      mt = pair_max(mt);
+      const bool rebase = mt > m_run + kRebase;
+      m_new = rebase ? mt : m_run;
+      alpha = rebase ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // exp2(-inf) = 0 on the first visible tile
+      l_run *= alpha;
+      m_run = m_new;
+    } else if (j < 10) {  // weights, four at a time
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int i = 4 * (j - 6) + c;
+        // A row that has seen no visible position yet keeps m = -inf with all
+        // its scores at -inf; exp2(-inf - -inf) would be NaN, so masked
+        // entries give 0.
+        v[i] = (v[i] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(v[i] - m_new);
+      }
+    } else if (j == 10) {
+      float t = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) t += v[i];
+      l_run += t;
+      if constexpr (FP8) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] *= tsv[i];
+      }
+    } else if (j == 11) {
+      float w8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w8[i] = v[i];
+      pf0 = pack_bf16x8(w8);
+    } else if (j == 12) {
+      float w8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w8[i] = v[8 + i];
+      pf1 = pack_bf16x8(w8);
     }
   }
-  float z[16];
-  float mt = -__builtin_inff();
+  __device__ __forceinline__ void fast_step(int j) {
+    if (j == 0) {
+      mt = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int tau = 8 * (i >> 2) + 4 * half + (i & 3);
-    float zi = sacc[i] * slog2;
-    if constexpr (FP8) zi *= tsv[i];
-    zi = (pos0 + tau < limit) ? zi : -__builtin_inff();
-    z[i] = zi;
-    mt = fmaxf(mt, zi);
-  }
-  mt = pair_max(mt);
-  const bool rebase = mt > m_run + kRebase;
-  const float m_new = rebase ? mt : m_run;
-  alpha = rebase ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // exp2(-inf) = 0 on the first visible tile
-  l_run *= alpha;
-  m_run = m_new;
-  float pv[16];
+      for (int i = 4; i < 8; ++i) mt = fmaxf(mt, v[i]);
+    } else if (j == 1) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    // A row that has seen no visible position yet keeps m = -inf with all its
-    // z = -inf; exp2(-inf - -inf) would be NaN, so masked entries give 0.
-    const float pi = (z[i] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(z[i] - m_new);
-    l_run += pi;
-    if constexpr (FP8) pv[i] = pi * tsv[i]; else pv[i] = pi;
+      for (int i = 8; i < 16; ++i) mt = fmaxf(mt, v[i]);
+    } else if (j == 2) {
+      mt = pair_max(mt) * slog2;
+      const bool rebase = mt > m_run + kRebase;
+      m_new = rebase ? mt : m_run;
+      alpha = rebase ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // exp2(-inf) = 0 on the first visible tile
+      l_run *= alpha;
+      m_run = m_new;
+    } else if (j < 7) {  // weights, four at a time
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int i = 4 * (j - 3) + c;
+        v[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], slog2, -m_new));
+      }
+    } else if (j == 7) {
+      float t0 = v[0] + v[1], t1 = v[2] + v[3], t2 = v[4] + v[5], t3 = v[6] + v[7];
+      float t4 = v[8] + v[9], t5 = v[10] + v[11], t6 = v[12] + v[13], t7 = v[14] + v[15];
+      l_run += ((t0 + t1) + (t2 + t3)) + ((t4 + t5) + (t6 + t7));
+    } else if (j == 8) {
+      float w8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w8[i] = v[i];
+      pf0 = pack_bf16x8(w8);
+    } else if (j == 9) {
+      float w8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w8[i] = v[8 + i];
+      pf1 = pack_bf16x8(w8);
+    }
   }
-  pf0 = pack_bf16x8(pv);
-  pf1 = pack_bf16x8(pv + 8);
+  __device__ __forceinline__ void all() {
+#pragma unroll
+    for (int j = 0; j < kSoftmaxSteps; ++j) step(j);
+  }
+};
+
+// Scores of one tile and the whole softmax update (the unpipelined order).
+template <int DC, bool FP8, int NDMA, class Dma>
+__device__ __forceinline__ void score_tile(const char* tb, const float* tsc, const bf16x8 (&qf)[Geo<DC>::KS],
+                                           float& m_run, float& l_run, int pos0, int limit, bool full, float slog2,
+                                           bf16x8& pf0, bf16x8& pf1, float& alpha, const Dma& dma) {
+  Softmax<FP8> sm{score_mfma<DC, NDMA>(tb, qf, dma), tsc, pos0, limit, slog2, m_run, l_run};
+  sm.full = full;
+  sm.all();
+  pf0 = sm.pf0;
+  pf1 = sm.pf1;
+  alpha = sm.alpha;
 }
 
 // O^T += V^T . P^T for one tile; the four transposed reads of block nb + AH
@@ -392,6 +493,52 @@ __device__ __forceinline__ void store_partial(const DecodeParams& p, const f32x1
   }
 }
 
+// Pitch of one row of a staged fp16 partial: the row plus 16 bytes, so that
+// the rows of one LDS write instruction start in different banks.
+template <int DC>
+constexpr int stage_pitch() { return DC * 2 + 16; }
+
+// The same write as store_partial<NB> for fp16 partials, through LDS: the
+// wave puts its 32 normalised rows into `stage` (row = lane % 32), then
+// writes them back out with every store instruction covering whole rows
+// (DC * 2 contiguous bytes), instead of 32 rows x 32 bytes per instruction.
+// `stage` is this wave's own region; nothing else may use it meanwhile.
+template <int DC>
+__device__ __forceinline__ void store_partial_staged(const DecodeParams& p, const f32x16* O, float inv, int64_t slot,
+                                                     int rowbase, char* stage) {
+  constexpr int NB = DC / 32;
+  constexpr int PITCH = stage_pitch<DC>();
+  const int lane = opaque_lane();
+  const int half = lane >> 5, col = lane & 31;
+  char* mine = stage + col * PITCH + 16 * (1 - half);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    uint32_t h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const f16x2 v = {(_Float16)(O[nb][2 * j] * inv), (_Float16)(O[nb][2 * j + 1] * inv)};
+      h[j] = __builtin_bit_cast(uint32_t, v);
+    }
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {  // 8-column groups (2pr, 2pr + 1), as in store_partial
+      const auto r0 = __builtin_amdgcn_permlane32_swap(h[4 * pr + 2], h[4 * pr], false, false);
+      const auto r1 = __builtin_amdgcn_permlane32_swap(h[4 * pr + 3], h[4 * pr + 1], false, false);
+      *(uint4*)(mine + 64 * nb + 32 * pr) = uint4{r0[0], r1[0], r0[1], r1[1]};
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one accumulator block at a time
+  }
+  // A wave's LDS accesses complete in order, so the reads below see the writes.
+  constexpr int LPR = DC / 8;       // lanes per row (16 bytes each)
+  constexpr int RPI = kWave / LPR;  // rows per store instruction
+  const int sub = lane / LPR, gi = lane % LPR;
+#pragma unroll 4
+  for (int r0 = 0; r0 < 32; r0 += RPI) {
+    const int r = r0 + sub;
+    const uint4 x = *(const uint4*)(stage + r * PITCH + 16 * gi);
+    if (rowbase + r < p.R) *(uint4*)((_Float16*)p.o_part + (slot * p.R + rowbase + r) * DC + 8 * gi) = x;
+  }
+}
+
 template <int DC, bool FP8, int NW, int NBUF>
 __global__ void __launch_bounds__(NW * kWave)
     decode_kernel(DecodeParams p, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ block_table,
@@ -402,7 +549,7 @@ __global__ void __launch_bounds__(NW * kWave)
   constexpr int AHEAD = NBUF - 1;  // tiles in flight ahead of the one computed
   static_assert(Gm::GPT % (2 * NW) == 0, "tile rows must split evenly over the waves");
   static_assert(AHEAD >= 1, "ring too small");
-  static_assert(FP8 || NI * (AHEAD - 1) <= 63, "DMA groups must fit vmcnt");
+  static_assert(FP8 || NI * AHEAD <= 63, "DMA groups must fit vmcnt");
   static_assert(!FP8 || AHEAD == 1, "fp8 tiles are staged one ahead");
 
   __shared__ __attribute__((aligned(1024))) char tiles[NBUF * TB];
@@ -431,6 +578,20 @@ __global__ void __launch_bounds__(NW * kWave)
   const int row = rg * (32 * NW) + 32 * w + col;  // this lane's query row (S^T column)
   const uint32_t tiles_lds = lds_offset(tiles);
 
+  // The first segment's query rows are touched (one dword per 128-byte line)
+  // while the tile-table reads are in flight, so that the wave's own query
+  // loads below hit L2 instead of making a further trip to HBM.
+  int bc = uniform(seq_of_tile(cu, p.B, k0));
+  uint32_t touch = 0;
+  {
+    const char* qa = (const char*)(p.q_lat + ((int64_t)bc * p.R + rg * (32 * NW)) * DC);
+    const char* qb = (const char*)(p.q_rope + ((int64_t)bc * p.R + rg * (32 * NW)) * 64);
+    const int rows = min(32 * NW, p.R - rg * (32 * NW));
+    const int la = rows * DC * 2 / 128, lb = rows * 64 * 2 / 128;
+    for (int i = tid; i < la + lb; i += NW * kWave)
+      touch += i < la ? *(const uint32_t*)(qa + 128 * i) : *(const uint32_t*)(qb + 128 * (i - la));
+  }
+
   // ---- tile source table: page, position and valid-token count of each tile
   // this part loads, kTab tiles at a time in LDS, so that starting a tile's
   // copy needs no memory round trip (a block-table read in the loop would).
@@ -447,6 +608,7 @@ __global__ void __launch_bounds__(NW * kWave)
     }
   };
   fill_tab(k0);
+  asm volatile("" ::"v"(touch));  // the touches complete together with the table reads
   block_sync();
 
   // ---- tile loader: next tile to load (kl) and its source.
@@ -499,11 +661,7 @@ __global__ void __launch_bounds__(NW * kWave)
     stage.load_chunk(p, src, lane_off8, 0, w);
   };
 
-  if constexpr (!FP8) {
-#pragma unroll
-    for (int i = 0; i < AHEAD; ++i)
-      if (kl < k1) dma_next();
-  } else {
+  if constexpr (FP8) {
     stage_start();
     stage_finish();
     block_sync();
@@ -511,12 +669,15 @@ __global__ void __launch_bounds__(NW * kWave)
 
   // Before computing tile k: its data is in LDS and visible to all waves, and
   // the next copy is started (bf16) or its loads are issued (fp8).
-  auto tile_begin = [&](int k, int cub, int L) {
+  // FULL: every position of the tile is visible to every row (so it lies
+  // inside the sequence and needs no zero fill either).
+  auto tile_begin = [&](int k, int cub, int L, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int buf = (k - k0) % NBUF;
     if constexpr (!FP8) {
       wait_dma_groups<NI, AHEAD - 1>(kl - 1 - k);
       block_sync();
-      if ((k - cub + 1) * kTile > L) {  // last tile of the sequence, partially filled
+      if (!FULL && (k - cub + 1) * kTile > L) {  // last tile of the sequence, partially filled
         zero_tail<DC, NW>(tiles + buf * TB, L - (k - cub) * kTile, tid);
         block_sync();
       }
@@ -533,12 +694,12 @@ __global__ void __launch_bounds__(NW * kWave)
 
   // ---- segments: maximal runs of this part's tiles inside one sequence
   int k = k0;
-  int bc = uniform(seq_of_tile(cu, p.B, k0));
-  while (k < k1) {
+  while (true) {
     const int cub = uniform(cu[bc]);
     const int kend = min(uniform(cu[bc + 1]), k1);
     const int L = seq_lens[bc];
     const int limit = min(L - p.S + 1 + row / p.H, L);
+    const int lim_all = L - p.S + 1;  // positions below this are visible to every query row
 
     bf16x8 qf[Gm::KS];
     if (row < p.R) {
@@ -550,13 +711,22 @@ __global__ void __launch_bounds__(NW * kWave)
       for (int ks = 0; ks < DC / 16; ++ks) qf[ks] = ql[2 * ks];
 #pragma unroll
       for (int ks = DC / 16; ks < Gm::KS; ++ks) qf[ks] = qr[2 * (ks - DC / 16)];
-      // Let the compiler see the query loads complete here (vmcnt(0)), so it
-      // places no waits for them inside the tile loop, where they would also
-      // drain the in-flight tile DMA.
-      __builtin_amdgcn_s_waitcnt(0x0F70);
     } else {
 #pragma unroll
       for (int ks = 0; ks < Gm::KS; ++ks) qf[ks] = bf16x8{};
+    }
+    // Let the compiler see the query loads complete here, so it places no
+    // waits for them inside the tile loop (where they would also drain the
+    // in-flight tile DMA).  On the part's first segment the first tile
+    // copies are started after the queries were requested, and the wait
+    // leaves them in flight.
+    if (!FP8 && k == k0) {
+#pragma unroll
+      for (int i = 0; i < AHEAD; ++i)
+        if (kl < k1) dma_next();
+      if (kl - k0 == AHEAD) vm_wait<NI * AHEAD>(); else vm_wait<0>();
+    } else {
+      vm_wait<0>();
     }
     f32x16 O[Gm::NB];
     float m_run = -__builtin_inff(), l_run = 0.0f;
@@ -566,9 +736,10 @@ __global__ void __launch_bounds__(NW * kWave)
     // One tile.  The first tile of a segment starts the accumulators with its
     // P.V (a zero accumulator input), so O needs no initialisation and no
     // rescale there (alpha is 0 or 1 on a first tile, and O would be 0).
-    auto one_tile = [&](auto first_tag) {
+    auto one_tile = [&](auto first_tag, auto full_tag) {
       constexpr bool FIRST = decltype(first_tag)::value;
-      tile_begin(k, cub, L);
+      constexpr bool FULL = decltype(full_tag)::value;
+      tile_begin(k, cub, L, full_tag);
       const int buf = (k - k0) % NBUF;
       if (!FP8 && kl < k1) {
         // the copy of tile kl (AHEAD tiles on) is issued inside the score product
@@ -577,12 +748,13 @@ __global__ void __launch_bounds__(NW * kWave)
                                   (uint32_t)load_token(ol) * (uint32_t)p.token_stride + 16u * (ol >> 5),
                                   tiles_lds + (uint32_t)(((kl - k0) % NBUF) * TB), w};
         score_tile<DC, FP8, TileDma<DC, NW>::NI>(tiles + buf * TB, tscale + buf * kTile, qf, m_run, l_run,
-                                                 (k - cub) * kTile, limit, p.scale_log2, pf0, pf1, alpha, dma);
+                                                 (k - cub) * kTile, limit, FULL, p.scale_log2, pf0, pf1, alpha,
+                                                 dma);
         ++kl;
         if (kl < k1) locate();
       } else {
         score_tile<DC, FP8, 0>(tiles + buf * TB, tscale + buf * kTile, qf, m_run, l_run, (k - cub) * kTile, limit,
-                               p.scale_log2, pf0, pf1, alpha, NoDma{});
+                               FULL, p.scale_log2, pf0, pf1, alpha, NoDma{});
       }
       if constexpr (!FIRST) {
         if (__any(alpha != 1.0f)) rescale<DC>(O, alpha);
@@ -591,8 +763,12 @@ __global__ void __launch_bounds__(NW * kWave)
       tile_end();
       ++k;
     };
-    one_tile(std::true_type{});
-    while (k < kend) one_tile(std::false_type{});
+    // The segment's first tile starts the sums (general path); then the tiles
+    // every row sees in full run branch-free; then the masked tail.
+    one_tile(std::true_type{}, std::false_type{});
+    const int kfull = min(kend, cub + lim_all / kTile);
+    while (k < kfull) one_tile(std::false_type{}, std::integral_constant<bool, !FP8>{});
+    while (k < kend) one_tile(std::false_type{}, std::false_type{});
 
     // ---- normalise and write this (sequence, part) partial
     const float l_tot = pair_sum(l_run);
@@ -609,10 +785,19 @@ __global__ void __launch_bounds__(NW * kWave)
       const int lhalf = ln >> 5, lcol = ln & 31;
       const int lrow = rg * (32 * NW) + 32 * w + lcol;
       if (lrow < p.R && lhalf == 0) p.lse_part[slot * p.R + lrow] = lse;
-      if (lrow < p.R) store_partial<Gm::NB>(p, O, inv, (slot * p.R + lrow) * DC, lhalf);
+      // After the part's last tile the ring is idle (every copy has landed and
+      // been consumed), so an fp16 partial is staged through it.
+      constexpr bool STAGE_FITS = NW * 32 * stage_pitch<DC>() <= NBUF * TB;
+      if (STAGE_FITS && p.o_half && kend == k1) {
+        block_sync();
+        store_partial_staged<DC>(p, O, inv, slot, rg * (32 * NW) + 32 * w, tiles + w * 32 * stage_pitch<DC>());
+      } else if (lrow < p.R) {
+        store_partial<Gm::NB>(p, O, inv, (slot * p.R + lrow) * DC, lhalf);
+      }
     }
     ++bc;
     while (bc < p.B - 1 && uniform(cu[bc + 1]) == uniform(cu[bc])) ++bc;
+    if (k >= k1) break;
   }
 }
 

@@ -44,7 +44,7 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // lanes write consecutive 16-byte slots starting at LDS offset `lds`
 // (wave-uniform).  Issued from inline asm so that the compiler does not put a
 // full vmcnt(0) wait in front of every LDS read; completion is tracked by
-// hand with vm_wait<N>().  M0 is saved and restored around the load.
+// hand with vm_wait<N>().  M0 (the LDS destination) is declared clobbered.
 __device__ __forceinline__ void lds_dma16(const void* base_any, uint32_t voff, uint32_t lds) {
   // Make the base provably wave-uniform.  readfirstlane returns int: widen
   // each half through uint32_t so the low half is zero-, not sign-, extended.
@@ -52,16 +52,13 @@ __device__ __forceinline__ void lds_dma16(const void* base_any, uint32_t voff, u
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
   const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "global_load_lds_dwordx4 %0, %1"
+      :
       : "v"(voff), "s"(base), "s"(lds)
-      : "memory");
+      : "memory", "m0");
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight.
