@@ -3,7 +3,10 @@ LSE combine -> up-projection) on one MI355X, on synthetic inputs.
 
 Prints one JSON line.  ``value`` is the effective latent-cache read rate of
 the whole step (algorithmic cache bytes / step time) with every input already
-resident in HBM; the step time itself is ``ms_per_step`` (and ``us_per_step``).
+resident in HBM; the step time itself is ``ms_per_step`` (and ``us_per_step``),
+timed over replays of the step captured as a HIP graph (``--no-graph``: four
+eager launches).  Per-call times and the decode kernel's roofline come from
+an eager loop with HIP events between the calls.
 Consecutive steps rotate through independent replicas of all inputs whose
 total exceeds three times the 256 MB Infinity Cache, so each step reads its
 cache and weights from HBM.
@@ -135,6 +138,8 @@ def main():
     ap.add_argument("--partial", default="fp16", choices=("fp16", "fp32"), help="element type of the split partials")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run a plain copy of this many MiB (counter calibration)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the step as four eager launches instead of one HIP-graph replay")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -171,6 +176,27 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    # Whole-step time: each replica's step captured once as a HIP graph (the
+    # four kernels, no host work between them) and replayed; --no-graph times
+    # the eager loop below instead.
+    graph_ms = None
+    if not args.no_graph:
+        for st in steps:
+            st.capture()
+        for i in range(args.warmup):
+            steps[i % nrep].replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for i in range(K):
+            steps[(args.warmup + i) % nrep].replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / K
+
+    # Per-call times: the same steps as eager launches with HIP events
+    # between the calls, on the stream the kernels run on.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -193,7 +219,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / K
+    eager_ms = total_ms / K
+    ms_per_step = graph_ms if graph_ms is not None else eager_ms
     per_call = {name: [ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(K)]
                 for j, name in enumerate(("absorb", "decode", "combine", "up_v"))}
     med = {k: float(np.median(v)) for k, v in per_call.items()}
@@ -224,6 +251,8 @@ def main():
             "tokens": alg["tokens"], "cache_bytes": alg["cache_bytes"], "input_replicas": nrep,
             "num_parts": steps[0].num_parts, "partials": args.partial,
         },
+        "step_launch": "hip_graph" if graph_ms is not None else "eager",
+        "eager_us_per_step": round(eager_ms * 1e3, 2),
         "per_call_us_median": {k: round(v, 2) for k, v in med.items()},
         "decode_combine_tbs": round(alg["cache_bytes"] / ((med["decode"] + med["combine"]) * 1e-6) / 1e12, 4),
         "step_hbm_frac": round(value * 1e3 / HBM_PEAK_GBS, 4),

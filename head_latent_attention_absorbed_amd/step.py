@@ -113,3 +113,26 @@ class DecodeStep:
         self.combine(stream)
         self.up(stream)
         return self.out
+
+    def capture(self):
+        """Record the whole step (the four launches, no allocation, no host
+        work) into a HIP graph; replay() then issues it with one launch.  The
+        graph reads and writes this step's buffers in place, so new inputs are
+        copied into them (q_nope, q_rope, cache, seq_lens, block_table ...)
+        before a replay.  The library's one-time kernel attribute setup runs in
+        an eager step first."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run()  # eager warm-up outside the capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.run()
+        return self.graph
+
+    def replay(self):
+        self.graph.replay()
+        return self.out

@@ -151,3 +151,29 @@ def test_full_workload_sampled(name):
         ref_l.append(l_ref)
     compare(f"{name} out (sampled)", np.stack(got), np.stack(ref), tol_abs, tol_rel, scaled_abs=False)
     compare(f"{name} lse (sampled)", np.stack(got_l), np.stack(ref_l), tol_abs, tol_rel)
+
+
+def test_graph_replay_matches_eager():
+    """The step captured as a HIP graph: several replays, with eager steps and
+    synchronisations between them, each equal bit for bit to the eager result
+    (the kernels are deterministic) and within tolerance of the oracle."""
+    import torch
+
+    inputs = make_inputs(SMALL_CASES["h128_ragged"])
+    _announce("graph", inputs)
+    eager = run_step(inputs)
+    ref_out = to_np(eager.out)
+    from head_latent_attention_absorbed_amd import DecodeStep
+
+    st = DecodeStep(inputs)
+    st.capture()
+    other = DecodeStep(inputs)
+    for i in range(3):
+        st.out.fill_(float("nan"))
+        st.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(st.out), ref_out), f"replay {i} differs from the eager step"
+        other.run()  # eager work between replays
+        torch.cuda.synchronize()
+    tol_abs, tol_rel = tolerances(inputs["workload"])
+    compare("graph out", to_np(st.out), oracle.decode(inputs)["out"], tol_abs, tol_rel)
