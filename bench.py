@@ -1,12 +1,13 @@
 """Benchmark: one absorbed-MLA decode step (absorb -> split-K paged decode ->
-LSE combine -> up-projection) on one MI355X, on synthetic inputs.
+LSE merge fused with the up-projection) on one MI355X, on synthetic inputs.
 
 Prints one JSON line.  ``value`` is the effective latent-cache read rate of
 the whole step (algorithmic cache bytes / step time) with every input already
 resident in HBM; the step time itself is ``ms_per_step`` (and ``us_per_step``),
-timed over replays of the step captured as a HIP graph (``--no-graph``: four
-eager launches).  Per-call times and the decode kernel's roofline come from
-an eager loop with HIP events between the calls.
+timed over replays of the step captured as a HIP graph (``--no-graph``: eager
+launches; ``--unfused``: separate merge and up-projection launches).  Per-call
+times and the decode kernel's roofline come from an eager loop with HIP events
+between the calls.
 Consecutive steps rotate through independent replicas of all inputs whose
 total exceeds three times the 256 MB Infinity Cache, so each step reads its
 cache and weights from HBM.
@@ -139,7 +140,9 @@ def main():
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run a plain copy of this many MiB (counter calibration)")
     ap.add_argument("--no-graph", action="store_true",
-                    help="time the step as four eager launches instead of one HIP-graph replay")
+                    help="time the step as eager launches instead of one HIP-graph replay")
+    ap.add_argument("--unfused", action="store_true",
+                    help="merge (mla_combine_lse) and up-project (mla_up_v) in two launches")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -166,7 +169,8 @@ def main():
     per_rep = alg["step_bytes"]
     nrep = args.replicas or max(3, math.ceil(3 * INFINITY_CACHE_BYTES / max(per_rep, 1)) + 1)
     nrep = min(nrep, 64)
-    steps = [DecodeStep(inputs, partial=args.partial) for _ in range(nrep)]
+    steps = [DecodeStep(inputs, partial=args.partial, fused=False if args.unfused else None) for _ in range(nrep)]
+    calls = ("absorb", "decode", "combine_up_v") if steps[0].fused else ("absorb", "decode", "combine", "up_v")
     stream = torch.cuda.current_stream()
     log(f"workload {w.name}: tokens={alg['tokens']} cache={alg['cache_bytes'] / 1e6:.1f} MB "
         f"replicas={nrep} num_parts={steps[0].num_parts}")
@@ -176,8 +180,8 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    # Whole-step time: each replica's step captured once as a HIP graph (the
-    # four kernels, no host work between them) and replayed; --no-graph times
+    # Whole-step time: each replica's step captured once as a HIP graph (its
+    # kernels, no host work between them) and replayed; --no-graph times
     # the eager loop below instead.
     graph_ms = None
     if not args.no_graph:
@@ -197,7 +201,7 @@ def main():
 
     # Per-call times: the same steps as eager launches with HIP events
     # between the calls, on the stream the kernels run on.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(K)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -211,10 +215,14 @@ def main():
         e[1].record(stream)
         st.decode()
         e[2].record(stream)
-        st.combine()
-        e[3].record(stream)
-        st.up()
-        e[4].record(stream)
+        if st.fused:
+            st.combine_up()
+            e[3].record(stream)
+        else:
+            st.combine()
+            e[3].record(stream)
+            st.up()
+            e[4].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -222,7 +230,7 @@ def main():
     eager_ms = total_ms / K
     ms_per_step = graph_ms if graph_ms is not None else eager_ms
     per_call = {name: [ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(K)]
-                for j, name in enumerate(("absorb", "decode", "combine", "up_v"))}
+                for j, name in enumerate(calls)}
     med = {k: float(np.median(v)) for k, v in per_call.items()}
     dec_us = float(np.mean(per_call["decode"]))
 
@@ -250,11 +258,11 @@ def main():
             "seq_lens": f"uniform[{w.seq_len[0]},{w.seq_len[1]}] seed {w.seed}",
             "tokens": alg["tokens"], "cache_bytes": alg["cache_bytes"], "input_replicas": nrep,
             "num_parts": steps[0].num_parts, "partials": args.partial,
+            "merge": "fused with up-projection" if steps[0].fused else "separate launches",
         },
         "step_launch": "hip_graph" if graph_ms is not None else "eager",
         "eager_us_per_step": round(eager_ms * 1e3, 2),
         "per_call_us_median": {k: round(v, 2) for k, v in med.items()},
-        "decode_combine_tbs": round(alg["cache_bytes"] / ((med["decode"] + med["combine"]) * 1e-6) / 1e12, 4),
         "step_hbm_frac": round(value * 1e3 / HBM_PEAK_GBS, 4),
         "roofline": {
             "kernel": "decode_kernel (mla_decode_paged)",

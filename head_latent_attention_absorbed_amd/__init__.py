@@ -26,7 +26,8 @@ from .binding import (  # noqa: F401
     mla_decode_paged,
     mla_combine_lse,
     mla_up_v,
+    mla_combine_up_v,
     mla_status_string,
     mla_last_error,
 )
-from .step import DecodeStep, split_plan  # noqa: F401
+from .step import DecodeStep, combine_up_supported, split_plan  # noqa: F401

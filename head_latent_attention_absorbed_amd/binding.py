@@ -78,7 +78,9 @@ def library() -> ctypes.CDLL:
     lib.mla_decode_paged.argtypes = [SP, P, P, P, P, I64, I64, P, P, P, I32, P, P, P]
     lib.mla_combine_lse.argtypes = [SP, I32, P, P, P, P, P, P]
     lib.mla_up_v.argtypes = [SP, P, P, P, P]
-    for fn in ("mla_absorb_q", "mla_decode_num_parts", "mla_decode_paged", "mla_combine_lse", "mla_up_v"):
+    lib.mla_combine_up_v.argtypes = [SP, I32, P, P, P, P, P, P, P]
+    for fn in ("mla_absorb_q", "mla_decode_num_parts", "mla_decode_paged", "mla_combine_lse", "mla_up_v",
+               "mla_combine_up_v"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
@@ -155,3 +157,10 @@ def mla_combine_lse(shape: MlaShape, num_parts: int, o_part, lse_part, seq_lens,
 def mla_up_v(shape: MlaShape, o_lat, w_uv, out, stream=None) -> None:
     _check(library().mla_up_v(ctypes.byref(shape), _ptr(o_lat), _ptr(w_uv), _ptr(out), _stream(stream)),
            "mla_up_v")
+
+
+def mla_combine_up_v(shape: MlaShape, num_parts: int, o_part, lse_part, seq_lens, w_uv, out, lse,
+                     stream=None) -> None:
+    _check(library().mla_combine_up_v(ctypes.byref(shape), int(num_parts), _ptr(o_part), _ptr(lse_part),
+                                      _ptr(seq_lens), _ptr(w_uv), _ptr(out), _ptr(lse), _stream(stream)),
+           "mla_combine_up_v")

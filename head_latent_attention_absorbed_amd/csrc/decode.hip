@@ -42,12 +42,6 @@ constexpr int kTab = 128;  // tiles per LDS source-table fill
 constexpr int kPvAhead = 2;     // V blocks read ahead of their MFMAs
 constexpr int kScoreAhead = 4;  // K fragments read ahead of their MFMAs
 
-__device__ __forceinline__ void block_sync() {
-  // Work-group barrier for LDS hand-offs: waits for this wave's LDS traffic,
-  // leaves its global loads in flight.
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 __device__ __forceinline__ int seq_of_tile(const int* cu, int B, int k) {
   int lo = 0, hi = B - 1;
   while (lo < hi) {

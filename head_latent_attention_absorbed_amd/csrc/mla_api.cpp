@@ -233,4 +233,36 @@ mla_status_t mla_up_v(const mla_shape_t* shape, const float* o_lat, const void* 
   return hip_status(mla::launch_head_gemm(p, true, shape->out_dtype == MLA_FP32, stream), "mla_up_v launch");
 }
 
+mla_status_t mla_combine_up_v(const mla_shape_t* shape, int32_t num_parts, const void* o_part,
+                              const float* lse_part, const int32_t* seq_lens, const void* w_uv, void* out,
+                              float* lse, hipStream_t stream) {
+  mla_status_t st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!o_part || !lse_part || !seq_lens || !w_uv || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARG, "mla_combine_up_v: NULL tensor");
+  if (!aligned16(o_part) || !aligned16(w_uv) || !aligned16(out))
+    return fail(MLA_ERR_INVALID_ARG, "mla_combine_up_v: o_part, w_uv and out must be 16-byte aligned");
+  if (num_parts < shape->batch)
+    return fail(MLA_ERR_INVALID_ARG, "mla_combine_up_v: num_parts %d < batch %d", num_parts, shape->batch);
+  if (!mla::combine_up_supported(shape->d_latent, shape->d_v))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_combine_up_v: no kernel for d_latent %d, d_v %d", shape->d_latent,
+                shape->d_v);
+  mla::CombineUpParams p{};
+  p.o_part = o_part;
+  p.o_half = shape->partial_dtype == MLA_FP16;
+  p.lse_part = lse_part;
+  p.seq_lens = seq_lens;
+  p.w = static_cast<const uint16_t*>(w_uv);
+  p.out = out;
+  p.out_f32 = shape->out_dtype == MLA_FP32;
+  p.lse = lse;
+  p.B = shape->batch;
+  p.S = shape->q_len;
+  p.H = shape->num_heads;
+  p.G = num_parts - shape->batch + 1;
+  p.DC = shape->d_latent;
+  p.NV = shape->d_v;
+  return hip_status(mla::launch_combine_up(p, stream), "mla_combine_up_v launch");
+}
+
 }  // extern "C"

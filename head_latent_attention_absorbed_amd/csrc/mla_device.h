@@ -29,6 +29,13 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).
+// Lane l holds A[l%16][8*(l/16) .. +8], B[8*(l/16) .. +8][l%16] and
+// D[4*(l/16) + i][l%16] in accumulator register i.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // Transposing LDS read of 4 bf16: within each 16-lane group, lane i receives
 // element (i % 4) of the 8-byte words addressed by lanes 4*j + i/4, j = 0..3.
 __device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
@@ -52,14 +59,19 @@ __device__ __forceinline__ void lds_dma16(const void* base_any, uint32_t voff, u
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
   const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %0, %1"
       :
-      : "v"(voff), "s"(base), "s"(lds)
+      : "v"(voff), "s"(base), "s"(dst)
       : "memory", "m0");
 }
+
+// Work-group barrier for LDS hand-offs: waits for this wave's LDS traffic,
+// leaves its global loads in flight.
+__device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>

@@ -51,6 +51,24 @@ struct CombineParams {
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 
+// The merge fused with the value up-projection: out[m, h, :] = o[m, h, :] . W[h]
+// for the merged row o of query row m = b*S + s, head h.
+struct CombineUpParams {
+  const void* o_part;        // fp32 or fp16 [parts, R, DC]
+  int32_t o_half;
+  const float* lse_part;
+  const int32_t* seq_lens;
+  const uint16_t* w;         // bf16 W_UV [H, DC, NV]
+  void* out;                 // bf16 or fp32 [B*S, H, NV]
+  int32_t out_f32;
+  float* lse;                // fp32 [B*S, H]
+  int32_t B, S, H, G, DC, NV;
+};
+
+// Whether the fused kernel exists for this latent rank and value width.
+bool combine_up_supported(int d_latent, int d_v);
+hipError_t launch_combine_up(const CombineUpParams& p, hipStream_t stream);
+
 // Per-head product C[m, h, :] = A[m, h, :] . W[h]  (A: [M, H, K], W: [H, K, N], C: [M, H, N]).
 struct HeadGemmParams {
   const void* a;             // bf16 or fp32

@@ -1,8 +1,10 @@
-"""One decode step on device: the four C-ABI calls in order on one stream.
+"""One decode step on device: the C-ABI calls in order on one stream.
 
 ``DecodeStep`` holds device copies of a workload's inputs (torch tensors used
 as plain device buffers), allocates the intermediate and output buffers, and
-issues mla_absorb_q -> mla_decode_paged -> mla_combine_lse -> mla_up_v.
+issues mla_absorb_q -> mla_decode_paged -> mla_combine_up_v (the merge and
+the up-projection in one launch), or with ``fused=False`` the separate
+mla_combine_lse -> mla_up_v, which also writes the merged latent rows o_lat.
 """
 from __future__ import annotations
 
@@ -10,8 +12,13 @@ import numpy as np
 
 from .binding import (
     MLA_BF16, MLA_FP8_E4M3, MLA_FP16, MLA_FP32, MLA_TILE_TOKENS, MlaShape,
-    mla_absorb_q, mla_decode_num_parts, mla_decode_paged, mla_combine_lse, mla_up_v,
+    mla_absorb_q, mla_decode_num_parts, mla_decode_paged, mla_combine_lse, mla_combine_up_v, mla_up_v,
 )
+
+
+def combine_up_supported(d_latent: int, d_v: int) -> bool:
+    """Shapes mla_combine_up_v has a kernel for (it returns MLA_ERR_UNSUPPORTED otherwise)."""
+    return d_latent in (256, 512) and d_v in (64, 128)
 
 
 def split_plan(seq_lens, num_parts: int, tile: int = MLA_TILE_TOKENS):
@@ -47,9 +54,11 @@ def _dev_bits(torch, arr: np.ndarray, device, dtype):
 
 
 class DecodeStep:
-    def __init__(self, inputs: dict, device: str = "cuda", num_parts: int | None = None, partial: str = "fp16"):
+    def __init__(self, inputs: dict, device: str = "cuda", num_parts: int | None = None, partial: str = "fp16",
+                 fused: bool | None = None):
         """``partial`` is the element type of the split partials o_part:
-        "fp16" (half the bytes) or "fp32"."""
+        "fp16" (half the bytes) or "fp32".  ``fused``: merge and up-project in
+        one launch (default where a kernel exists); o_lat is then None."""
         import torch
 
         if partial not in ("fp16", "fp32"):
@@ -84,7 +93,11 @@ class DecodeStep:
         self.o_part = torch.empty((self.num_parts, R, DC), dtype=torch.float16 if partial == "fp16" else f32,
                                   device=device)
         self.lse_part = torch.empty((self.num_parts, R), dtype=f32, device=device)
-        self.o_lat = torch.empty((B, S, H, DC), dtype=f32, device=device)
+        supported = combine_up_supported(DC, w.d_v)
+        if fused and not supported:
+            raise ValueError(f"no fused merge + up-projection kernel for d_latent {DC}, d_v {w.d_v}")
+        self.fused = supported if fused is None else bool(fused)
+        self.o_lat = None if self.fused else torch.empty((B, S, H, DC), dtype=f32, device=device)
         self.lse = torch.empty((B, S, H), dtype=f32, device=device)
         self.out = torch.empty((B, S, H, w.d_v), dtype=f32 if w.out_dtype == "fp32" else bf16, device=device)
 
@@ -106,16 +119,27 @@ class DecodeStep:
     def up(self, stream=None):
         mla_up_v(self.shape, self.o_lat, self.w_uv, self.out, stream)
 
+    def combine_up(self, stream=None):
+        mla_combine_up_v(self.shape, self.num_parts, self.o_part, self.lse_part, self.seq_lens, self.w_uv, self.out,
+                         self.lse, stream)
+
+    def finish(self, stream=None):
+        """Merge of the splits and up-projection: one launch when fused, else two."""
+        if self.fused:
+            self.combine_up(stream)
+        else:
+            self.combine(stream)
+            self.up(stream)
+
     def run(self, stream=None, cache=None, kv_scale=None):
-        """The whole step: absorb, split-K decode, LSE combine, up-projection."""
+        """The whole step: absorb, split-K decode, LSE merge, up-projection."""
         self.absorb(stream)
         self.decode(stream, cache, kv_scale)
-        self.combine(stream)
-        self.up(stream)
+        self.finish(stream)
         return self.out
 
     def capture(self):
-        """Record the whole step (the four launches, no allocation, no host
+        """Record the whole step (its launches, no allocation, no host
         work) into a HIP graph; replay() then issues it with one launch.  The
         graph reads and writes this step's buffers in place, so new inputs are
         copied into them (q_nope, q_rope, cache, seq_lens, block_table ...)

@@ -11,6 +11,8 @@
  *   mla_combine_lse   log-sum-exp merge of the splits -> o_lat, lse
  *   mla_up_v          out = o_lat . W_UV[h]                  (per head)
  *
+ * mla_combine_up_v does the last two in one launch without writing o_lat.
+ *
  * What the method is, and where the pages say it:
  *  - Only one low-rank latent c_KV per token is cached, next to one decoupled
  *    RoPE key that every head shares (TPLA abstract, taxoreview pages for
@@ -178,6 +180,29 @@ mla_status_t mla_combine_lse(const mla_shape_t* shape, int32_t num_parts, const 
  */
 mla_status_t mla_up_v(const mla_shape_t* shape, const float* o_lat, const void* w_uv, void* out,
                       hipStream_t stream);
+
+/*
+ * mla_combine_up_v -- mla_combine_lse and mla_up_v in one launch: the
+ * log-sum-exp merge of the splits (online softmax state merged exactly, BLASST
+ * abstract on the "GQA-to-MLA" Daily Papers listing) followed by the value
+ * up-projection applied after attention (early TransMLA abstract on that
+ * listing), with the merged latent row kept on chip:
+ *   lse[b,s,h]   = log sum_k exp(lse_part[k,r])                  (as mla_combine_lse)
+ *   out[b,s,h,:] = (sum_k exp(lse_part[k,r] - lse[b,s,h]) o_part[k,r]) . W_UV[h]
+ * with r = s*H + h over sequence b's slots, fp32 merge and accumulation.
+ * Arguments as for the two calls (same shape, num_parts and seq_lens as the
+ * decode that wrote o_part / lse_part):
+ *   w_uv bf16 [H, d_latent, d_v]; out [B, S_q, H, d_v] in shape->out_dtype,
+ *   lse fp32 [B, S_q, H] (both written); o_part, w_uv, out 16-byte aligned.
+ * A row with no visible position gets out = 0 and lse = -inf.
+ * Kernels exist for d_latent 512 or 256 with d_v 64 or 128 (else
+ * MLA_ERR_UNSUPPORTED: use the two calls).  The merge weighs the splits in
+ * batches of a different size than mla_combine_lse, so the two paths agree
+ * to rounding, not bit for bit; each is deterministic.
+ */
+mla_status_t mla_combine_up_v(const mla_shape_t* shape, int32_t num_parts, const void* o_part,
+                              const float* lse_part, const int32_t* seq_lens, const void* w_uv, void* out,
+                              float* lse, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* mla_status_string(mla_status_t status);

@@ -50,14 +50,17 @@ def compare(name, got, ref, tol_abs, tol_rel, finite_only=False, scaled_abs=True
     return max_abs, rel
 
 
-def run_step(inputs, num_parts=None, poison=True, partial="fp16"):
+def run_step(inputs, num_parts=None, poison=True, partial="fp16", fused=None):
+    """One step through the C ABI; ``fused`` None takes the step's default
+    (merge and up-projection in one launch where a kernel exists)."""
     import torch
     from head_latent_attention_absorbed_amd import DecodeStep
 
-    st = DecodeStep(inputs, num_parts=num_parts, partial=partial)
+    st = DecodeStep(inputs, num_parts=num_parts, partial=partial, fused=fused)
     if poison:
         for t in (st.q_lat, st.o_part, st.lse_part, st.o_lat, st.lse, st.out):
-            t.fill_(float("nan"))
+            if t is not None:
+                t.fill_(float("nan"))
     st.run()
     torch.cuda.synchronize()
     return st

@@ -21,7 +21,7 @@ def test_exports_every_declared_symbol():
     lib = _lib()
     declared = mla.exported_symbols()
     assert set(declared) >= {"mla_absorb_q", "mla_decode_num_parts", "mla_decode_paged", "mla_combine_lse",
-                             "mla_up_v", "mla_status_string", "mla_last_error"}
+                             "mla_up_v", "mla_combine_up_v", "mla_status_string", "mla_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", mla.library_path], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for name in declared:
@@ -89,6 +89,29 @@ def test_null_and_alignment_checks():
     assert lib.mla_absorb_q(ctypes.byref(sh), FAKE + 2, FAKE, FAKE, None) == mla.MLA_ERR_INVALID_ARG
     assert lib.mla_up_v(ctypes.byref(sh), FAKE, None, FAKE, None) == mla.MLA_ERR_INVALID_ARG
     assert lib.mla_combine_lse(ctypes.byref(sh), 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == mla.MLA_ERR_INVALID_ARG
+
+
+def _combine_up(sh, num_parts=8, **kw):
+    a = dict(o_part=FAKE, lse_part=FAKE, seq_lens=FAKE, w_uv=FAKE, out=FAKE, lse=FAKE)
+    a.update(kw)
+    return _lib().mla_combine_up_v(ctypes.byref(sh), num_parts, a["o_part"], a["lse_part"], a["seq_lens"],
+                                   a["w_uv"], a["out"], a["lse"], None)
+
+
+def test_combine_up_argument_checks():
+    sh = _shape()
+    for name in ("o_part", "lse_part", "seq_lens", "w_uv", "out", "lse"):
+        assert _combine_up(sh, **{name: None}) == mla.MLA_ERR_INVALID_ARG, name
+    for name in ("o_part", "w_uv", "out"):
+        assert _combine_up(sh, **{name: FAKE + 4}) == mla.MLA_ERR_INVALID_ARG, name
+    assert _combine_up(sh, num_parts=1) == mla.MLA_ERR_INVALID_ARG              # fewer parts than sequences
+    assert _combine_up(_shape(d_v=256)) == mla.MLA_ERR_UNSUPPORTED              # no fused kernel: two calls
+    assert "d_v 256" in mla.mla_last_error()
+    assert _combine_up(_shape(d_v=192)) == mla.MLA_ERR_UNSUPPORTED
+    assert _lib().mla_combine_up_v(None, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == mla.MLA_ERR_INVALID_ARG
+    from head_latent_attention_absorbed_amd import combine_up_supported
+    assert combine_up_supported(512, 128) and combine_up_supported(256, 64)
+    assert not combine_up_supported(512, 256) and not combine_up_supported(384, 128)
 
 
 def _decode(sh, **kw):
