@@ -71,11 +71,10 @@ __device__ __forceinline__ void split_range(const int* cu, int B, int G, int b, 
 // while every lane requests its columns of all U partial rows, so one memory
 // latency covers the whole batch (indices past the last split repeat it with
 // weight 0).
-template <int DC, bool HALF>
+template <int DC, bool HALF, int U = 16>
 __device__ __forceinline__ float merge_row(const void* o_part, const float* lse_part, int R, int b, int r, int g0,
                                            int g1, int lane, float (&acc)[DC / 64]) {
   constexpr int E = DC / 64;
-  constexpr int U = 16;
 #pragma unroll
   for (int i = 0; i < E; ++i) acc[i] = 0.0f;
   float m = -__builtin_inff(), tot = 0.0f;
@@ -142,149 +141,134 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineParams p, const int
 // Merge fused with the value up-projection.
 //
 // out[m, h, :] = o[m, h, :] . W_UV[h], o the merged row above.  A work-group
-// takes one head h and 16 query rows m0 .. m0+15 (m = b*S + s); its four waves
-// split d_c into four column ranges of KW = d_c / 4.  A wave merges, for all
-// 16 rows, only its own KW columns, in exactly the layout of the A operand of
-// the 16x16x32 MFMA (lane l: row l % 16, columns 32 ks + 8 (l / 16) .. +7 of
-// k-step ks), so the merged rows never leave registers.  The wave's KW rows of
-// W_UV[h] are copied into its own LDS slice by DMA at the start (16-byte
-// granules XOR-swizzled per row) and read transposed as the B operand.  The
-// four partial products are summed through LDS (each wave reuses its own
-// slice) into 16-byte row stores.  The merged row is fp32, split into bf16
-// high and low parts (two MFMAs per step) for near-fp32 accuracy.
-//
-// The grid is (row tile, head) with the head fastest, so for H a multiple of 8
-// every row tile of a head lands on the same XCD and W_UV[h] is fetched from
-// HBM about once.
+// takes one head h and 16 query rows m0 .. m0+15 (m = b*S + s; the M extent
+// of one 16x16x32 MFMA) with sixteen waves:
+//  1. W_UV[h] is copied into LDS by DMA at the start (four slices of
+//     KW = d_c/4 rows, 16-byte granules XOR-swizzled per row) and stays in
+//     flight while the rows are merged.
+//  2. Wave w merges row w exactly as the stand-alone merge does (contiguous
+//     row loads, all of a row's splits in flight at once); the fp32 row goes
+//     to an LDS tile (granules XOR-swizzled by row).
+//  3. Wave w = 4 nq + kr multiplies the tile's columns kr*KW .. kr*KW + KW-1
+//     (A operand, split into bf16 high and low parts: two MFMAs per step for
+//     near-fp32 accuracy) by output columns nq*NV/4 .. of W_UV slice kr
+//     (B operand, transposing LDS reads).
+//  4. The four K parts of each output are summed through LDS (in the W_UV
+//     slices' place) into 16-byte row stores.
+// The grid is (row tile, head) with the head fastest, so for H a multiple of
+// 8 every row tile of a head lands on the same XCD and shares its L2.
 
-constexpr int kUpRows = 16;  // query rows per work-group (the M extent of one 16x16 MFMA)
+constexpr int kUpRows = 16;  // query rows per work-group, one per wave
 
 template <int DC, int NV>
 struct UpGeometry {
-  static constexpr int KW = DC / 4;             // latent columns of one wave
-  static constexpr int KSW = KW / 32;           // 32-deep k-steps of one wave
-  static constexpr int NT = NV / 16;            // 16-column output tiles
+  static constexpr int KW = DC / 4;             // latent columns of one K part
+  static constexpr int KSW = KW / 32;           // 32-deep k-steps of one K part
+  static constexpr int NQ = NV / 4;             // output columns of one wave
+  static constexpr int NTW = NQ / 16;           // 16-column output tiles of one wave
   static constexpr int ROWB = NV * 2;           // bytes of one W_UV row in LDS
   static constexpr int GR = NV / 8;             // 16-byte granules of one W_UV row
-  static constexpr int SLICE = KW * ROWB;       // bytes of one wave's W_UV slice
+  static constexpr int SLICE = KW * ROWB;       // bytes of one K part's W_UV slice
+  static constexpr int PIECES = SLICE / 1024;   // 1 KiB DMA pieces of one slice
+  static constexpr int AROW = DC * 4;           // bytes of one merged fp32 row
+  static constexpr int ATILE = kUpRows * AROW;  // the merged tile
   static constexpr int PITCH = NV + 4;          // fp32 row pitch of the reduction buffer
-  static constexpr size_t LDS = 4 * (size_t)SLICE + (kMaxBatch + 1) * sizeof(int);
+  static constexpr size_t LDS = 4 * (size_t)SLICE + ATILE;
   static_assert(GR >= 8, "the swizzle permutes eight granules");
-  static_assert(SLICE % 1024 == 0, "one DMA instruction fills 1 KiB");
-  static_assert(kUpRows * PITCH * 4 <= SLICE, "the reduction buffer reuses the wave's slice");
+  static_assert(NTW >= 1, "a wave takes whole 16-column tiles");
+  static_assert(SLICE % 4096 == 0, "four waves issue equal shares of 1 KiB DMAs per slice");
+  static_assert(4 * kUpRows * PITCH * 4 <= 4 * SLICE, "the reduction buffer reuses the W_UV slices");
+  static_assert((kMaxBatch + 1) * sizeof(int) <= (size_t)ATILE, "the tile prefix lives in the merged tile first");
 };
 
+// Byte offset of fp32 column c of merged row r: 16-byte granule c/4 at
+// position (c/4) ^ (r & 7), so that the sixteen rows of an A-fragment read
+// spread over the banks.
+__device__ __forceinline__ int arow_off(int r, int c, int arow) {
+  return r * arow + ((((c >> 2) ^ (r & 7)) << 4) | ((c & 3) << 2));
+}
+
 template <int DC, int NV, bool HALF, bool CF32>
-__global__ void __launch_bounds__(256) combine_up_kernel(CombineUpParams p) {
+__global__ void __launch_bounds__(1024) combine_up_kernel(CombineUpParams p) {
   using Geo = UpGeometry<DC, NV>;
-  constexpr int KW = Geo::KW, KSW = Geo::KSW, NT = Geo::NT, ROWB = Geo::ROWB, GR = Geo::GR;
-  constexpr int SLICE = Geo::SLICE, PITCH = Geo::PITCH;
-  constexpr int U = HALF ? 8 : 4;  // splits per batch: 8 (fp16) or 4 (fp32) x KSW 16-byte words in flight
+  constexpr int KW = Geo::KW, KSW = Geo::KSW, NQ = Geo::NQ, NTW = Geo::NTW, ROWB = Geo::ROWB, GR = Geo::GR;
+  constexpr int SLICE = Geo::SLICE, PIECES = Geo::PIECES, AROW = Geo::AROW, PITCH = Geo::PITCH;
+  constexpr int E = DC / 64;  // merged columns per lane
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  int* cu = (int*)(smem + 4 * SLICE);
+  char* atile = smem + 4 * SLICE;
+  int* cu = (int*)atile;  // the tile prefix, until the merged rows overwrite it
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int kr = w & 3, nq = w >> 2;  // K part and output-column quarter of the product
   const int H = p.H, M = p.B * p.S, R = p.S * H;
   const int h = blockIdx.x % H;
   const int m0 = (blockIdx.x / H) * kUpRows;
-  char* ws = smem + w * SLICE;
 
   // Tile prefix first (wave 0), so that its loads are not queued behind the DMA.
   if (w == 0) build_tile_prefix(p.seq_lens, p.B, cu, lane);
 
-  // W_UV[h] rows w*KW .. w*KW + KW-1 into this wave's slice: LDS granule
-  // position q of row k holds global granule q ^ swz(k).
+  // W_UV[h] rows kr*KW .. kr*KW + KW-1 into slice kr: LDS granule position q
+  // of row k holds global granule q ^ swz(k).  Wave (kr, nq) copies pieces
+  // nq*PIECES/4 .. of the slice.
   {
-    const uint16_t* wsrc = p.w + ((int64_t)h * DC + w * KW) * NV;
+    const uint16_t* wsrc = p.w + ((int64_t)h * DC + kr * KW) * NV;
 #pragma unroll
-    for (int i = 0; i < SLICE / 1024; ++i) {
+    for (int j = 0; j < PIECES / 4; ++j) {
+      const int i = nq * (PIECES / 4) + j;
       const int pos = 64 * i + lane;
       const int k = pos / GR, q = pos % GR;
-      lds_dma16(wsrc, (uint32_t)((k * NV + 8 * (q ^ swz(k))) * 2), lds_offset(ws + 1024 * i));
+      lds_dma16(wsrc, (uint32_t)((k * NV + 8 * (q ^ swz(k))) * 2), lds_offset(smem + kr * SLICE + 1024 * i));
     }
   }
   block_sync();
 
-  // ---- merge: this lane's row and its 8-column group of every k-step.
-  const int mr = lane & 15, cg = lane >> 4;
-  const int m = m0 + mr;
-  const int mc = min(m, M - 1);  // address row (rows past M merge nothing)
+  // ---- merge row w of the tile.
+  const int m = m0 + w;
+  const int mc = min(m, M - 1);
   const int b = mc / p.S, r = (mc % p.S) * H + h;
   int g0, g1;
   split_range(cu, p.B, p.G, b, g0, g1);
-  const int n = m < M ? g1 - g0 + 1 : 0;  // splits of this row (0: sees no position)
-  const int64_t row0 = ((int64_t)b + g0) * R + r;  // partial row of split 0
-  const int col0 = w * KW + 8 * cg;
+  if (m >= M) g1 = g0 - 1;  // rows past M merge nothing
+  block_sync();  // every read of cu is done before the merged rows overwrite it
+  float acc[E];
+  // 16 splits in flight per batch; 8 for fp32 rows of 512, which would not
+  // fit the 128 registers a lane has at 16 waves per work-group.
+  const float lse = merge_row<DC, HALF, (HALF || DC < 512) ? 16 : 8>(p.o_part, p.lse_part, R, b, r, g0, g1, lane, acc);
+  if (lane == 0 && m < M) p.lse[(int64_t)m * H + h] = lse;
+#pragma unroll
+  for (int e = 0; e < E; e += 4)
+    *(f32x4*)(atile + arow_off(w, E * lane + e, AROW)) = f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+  vm_wait<0>();  // this wave's pieces of the W_UV copy have landed ...
+  block_sync();  // ... and everyone's, and the merged tile is complete
 
-  float acc[KSW][8];
-#pragma unroll
-  for (int ks = 0; ks < KSW; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[ks][e] = 0.0f;
-  float m_run = -__builtin_inff(), tot = 0.0f;
-  for (int jb = 0; __ballot(jb < n) != 0; jb += U) {
-    float lk[U];
-    PartRow<8, HALF> part[U][KSW];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = max(0, min(jb + u, n - 1));  // past the row's last split: repeat it, weight 0
-      const int64_t rw = row0 + (int64_t)j * R;
-      lk[u] = p.lse_part[rw];
-#pragma unroll
-      for (int ks = 0; ks < KSW; ++ks) part[u][ks].load(p.o_part, rw * DC + col0 + 32 * ks);
-    }
-    asm volatile("" ::: "memory");  // every load of the batch is issued before the first use
-    float mb = m_run;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (jb + u >= n) lk[u] = -__builtin_inff();
-      mb = fmaxf(mb, lk[u]);
-    }
-    const float sc = m_run == mb ? 1.0f : __expf(m_run - mb);  // rescale of the earlier sum
-    tot *= sc;
-#pragma unroll
-    for (int ks = 0; ks < KSW; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[ks][e] *= sc;
-    m_run = mb;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float wu = lk[u] == -__builtin_inff() ? 0.0f : __expf(lk[u] - mb);
-      tot += wu;
-#pragma unroll
-      for (int ks = 0; ks < KSW; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[ks][e] += wu * part[u][ks].at(e);
-    }
-  }
-  // A row that sees nothing has read whatever its (unwritten) address held
-  // with weight 0; select zeros rather than scale, so NaN there cannot leak.
-  const bool seen = tot > 0.0f;
-  const float inv = seen ? 1.0f / tot : 0.0f;
-  if (w == 0 && cg == 0 && m < M) p.lse[(int64_t)m * H + h] = seen ? m_run + __logf(tot) : -__builtin_inff();
-
-  // ---- A fragments (bf16 high and low parts) of the merged row.
+  // ---- A fragments (bf16 high and low parts) of K part kr.
+  const int mr = lane & 15, cg = lane >> 4;
   bf16x8 ahi[KSW], alo[KSW];
 #pragma unroll
-  for (int ks = 0; ks < KSW; ++ks)
+  for (int ks = 0; ks < KSW; ++ks) {
+    const int c = kr * KW + 32 * ks + 8 * cg;
+    const f32x4 x0 = *(const f32x4*)(atile + arow_off(mr, c, AROW));
+    const f32x4 x1 = *(const f32x4*)(atile + arow_off(mr, c + 4, AROW));
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float x = seen ? acc[ks][e] * inv : 0.0f;
+      const float x = e < 4 ? x0[e] : x1[e - 4];
       const __bf16 hi = (__bf16)x;
       ahi[ks][e] = hi;
       alo[ks][e] = (__bf16)(x - (float)hi);
     }
+  }
 
-  // ---- this wave's share of the product: C[16 x NV] over its KW columns.
-  vm_wait<0>();  // the wave's W_UV slice has landed (only this wave reads it)
+  // ---- C[16 x NQ] (output columns nq*NQ ..) over K part kr.
+  const char* ws = smem + kr * SLICE;
   const int i16 = lane & 15, jj = i16 >> 2, qq = i16 & 3;
-  f32x4 c[NT];
+  f32x4 c[NTW];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) c[nt] = f32x4{};
+  for (int t = 0; t < NTW; ++t) c[t] = f32x4{};
 #pragma unroll
   for (int ks = 0; ks < KSW; ++ks) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int t = 0; t < NTW; ++t) {
+      const int nt = nq * NTW + t;
       s16x4 rr[2];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
@@ -293,28 +277,28 @@ __global__ void __launch_bounds__(256) combine_up_kernel(CombineUpParams p) {
         rr[h2] = lds_read_tr16(ws + k * ROWB + ((q ^ swz(k)) * 16) + (qq & 1) * 8);
       }
       const s16x8 bv = {rr[0][0], rr[0][1], rr[0][2], rr[0][3], rr[1][0], rr[1][1], rr[1][2], rr[1][3]};
-      c[nt] = mfma16(ahi[ks], (bf16x8)bv, c[nt]);
-      c[nt] = mfma16(alo[ks], (bf16x8)bv, c[nt]);
+      c[t] = mfma16(ahi[ks], (bf16x8)bv, c[t]);
+      c[t] = mfma16(alo[ks], (bf16x8)bv, c[t]);
     }
   }
-  // Partial product into the wave's own slice (its last reads of the slice
-  // precede these writes in the wave's LDS queue).
-  float* red = (float*)ws;
+  block_sync();  // every wave is done with W_UV
+  // Partial products red[kr][row][col] in the W_UV slices' place.
+  float* red = (float*)smem;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int t = 0; t < NTW; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[(4 * cg + i) * PITCH + 16 * nt + i16] = c[nt][i];
+    for (int i = 0; i < 4; ++i) red[(kr * kUpRows + 4 * cg + i) * PITCH + nq * NQ + 16 * t + i16] = c[t][i];
   block_sync();
 
-  // ---- sum the four K parts; 8 consecutive columns per thread.
-  for (int e = tid; e < kUpRows * (NV / 8); e += 256) {
+  // ---- sum the four K parts; 8 consecutive output columns per thread.
+  for (int e = tid; e < kUpRows * (NV / 8); e += 1024) {
     const int row = e / (NV / 8), nc = (e % (NV / 8)) * 8;
     const int mm = m0 + row;
     if (mm >= M) continue;
     float s[8] = {};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float* src = (const float*)(smem + q * SLICE) + row * PITCH + nc;
+      const float* src = red + (q * kUpRows + row) * PITCH + nc;
       const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -341,7 +325,7 @@ hipError_t launch_up_variant(const CombineUpParams& p, hipStream_t stream) {
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (attr != hipSuccess) return attr;
   const int tiles = (p.B * p.S + kUpRows - 1) / kUpRows;
-  hipLaunchKernelGGL((combine_up_kernel<DC, NV, HALF, CF32>), dim3(tiles * p.H), dim3(256), smem, stream, p);
+  hipLaunchKernelGGL((combine_up_kernel<DC, NV, HALF, CF32>), dim3(tiles * p.H), dim3(1024), smem, stream, p);
   return hipGetLastError();
 }
 
