@@ -20,3 +20,13 @@ from .mla_oracle import (  # noqa: F401
     combine,
     up_v,
 )
+from .append_oracle import (  # noqa: F401
+    rope,
+    f64_to_bf16_bits,
+    f64_to_e4m3_bits,
+    append_positions,
+    append_values,
+    encode_records,
+    apply_append,
+    with_appended,
+)

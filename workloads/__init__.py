@@ -8,6 +8,7 @@ any of the method's code.
 """
 from .configs import WORKLOADS, Workload, get_workload, small_workload
 from .generate import (
+    make_append_inputs,
     make_inputs,
     f32_to_bf16_bits,
     f32_to_e4m3_bits,
@@ -20,6 +21,7 @@ __all__ = [
     "get_workload",
     "small_workload",
     "make_inputs",
+    "make_append_inputs",
     "f32_to_bf16_bits",
     "f32_to_e4m3_bits",
     "replicate_cache",

@@ -32,6 +32,9 @@ class Workload:
     d_rope: int = 64
     d_v: int = 128
     block_size: int = 64
+    # Width of the hidden state the cache append projects from (the
+    # MHA-converted 7B model's 4096 = 32 heads x 128).
+    d_model: int = 4096
     # Largest length the block table has room for (defaults to seq_len[1]).
     max_seq_len: Optional[int] = None
     # Extra unused physical pages beyond those the sequences need.

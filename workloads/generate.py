@@ -130,3 +130,17 @@ def replicate_cache(inputs: dict, n: int) -> list:
     for _ in range(n):
         reps.append((inputs["cache"].copy(), None if inputs["kv_scale"] is None else inputs["kv_scale"].copy()))
     return reps
+
+
+def make_append_inputs(w: Workload, seed: int | None = None) -> dict:
+    """Inputs of the cache append for the S_q new tokens of every sequence:
+    hidden states x [B, S_q, d_model] ~ N(0, 1) and the combined projection
+    [W_DKV | W_KR] [d_model, d_c + d_r] ~ N(0, 1/d_model), both as bf16 bits,
+    and the RoPE base.  Drawn from child stream 5 of the workload seed (the
+    decode inputs use children 0-4, so they are unchanged)."""
+    seed = w.seed if seed is None else seed
+    rng = np.random.default_rng(np.random.SeedSequence(seed).spawn(6)[5])
+    D, B, S = w.d_model, w.batch, w.q_len
+    x = f32_to_bf16_bits(_normal(rng, (B, S, D)))
+    w_dkv = f32_to_bf16_bits(_normal(rng, (D, w.d_latent + w.d_rope), float(np.sqrt(1.0 / D))))
+    return dict(x=x, w_dkv=w_dkv, rope_base=10000.0)
