@@ -234,6 +234,26 @@ def main():
     med = {k: float(np.median(v)) for k, v in per_call.items()}
     dec_us = float(np.mean(per_call["decode"]))
 
+    # The cache append (x . [W_DKV | W_KR] -> RoPE -> records in the pages),
+    # timed on its own over the same replicas: events around each call.
+    from workloads import make_append_inputs
+    ap = make_append_inputs(w)
+    for st in steps:
+        st.set_append_inputs(ap)
+    for i in range(3):
+        steps[i % nrep].append()
+    torch.cuda.synchronize()
+    aev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        aev[i][0].record(stream)
+        steps[(args.warmup + i) % nrep].append()
+        aev[i][1].record(stream)
+    torch.cuda.synchronize()
+    app_us = [a.elapsed_time(b) * 1e3 for a, b in aev]
+    app_med = float(np.median(app_us))
+    M = w.batch * w.q_len
+    app_bytes = w.d_model * (w.d_latent + w.d_rope) * 2 + M * w.d_model * 2 + M * alg["record_bytes"]
+
     us_step = ms_per_step * 1e3
     value = alg["cache_bytes"] / (us_step * 1e-6) / 1e12
     achieved = alg["decode_bytes"] / (dec_us * 1e-6) / 1e9
@@ -277,6 +297,16 @@ def main():
             "mfma_frac": round(alg["attn_flops"] / (dec_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         },
         "wall_s": round(wall, 3),
+        "append": {
+            "what": "mla_append_kv: new tokens' [c_KV | k_rope] records from x [B*S_q, d_model] "
+                    "(product, RoPE, paged write)",
+            "d_model": w.d_model,
+            "us_median": round(app_med, 2),
+            "roofline": {"bound": "hbm", "achieved": round(app_bytes / (app_med * 1e-6) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(app_bytes / (app_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_call": app_bytes},
+        },
     }
     if args.copy_probe_mb > 0:
         copy_probe(args.copy_probe_mb)

@@ -27,6 +27,8 @@ from .binding import (  # noqa: F401
     mla_combine_lse,
     mla_up_v,
     mla_combine_up_v,
+    mla_append_kv,
+    mla_append_kv_workspace_bytes,
     mla_status_string,
     mla_last_error,
 )

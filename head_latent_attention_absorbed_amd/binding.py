@@ -79,8 +79,10 @@ def library() -> ctypes.CDLL:
     lib.mla_combine_lse.argtypes = [SP, I32, P, P, P, P, P, P]
     lib.mla_up_v.argtypes = [SP, P, P, P, P]
     lib.mla_combine_up_v.argtypes = [SP, I32, P, P, P, P, P, P, P]
+    lib.mla_append_kv_workspace_bytes.argtypes = [SP, I32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_append_kv.argtypes = [SP, I32, P, P, F, P, P, I64, I64, P, P, P, P, ctypes.c_size_t, P]
     for fn in ("mla_absorb_q", "mla_decode_num_parts", "mla_decode_paged", "mla_combine_lse", "mla_up_v",
-               "mla_combine_up_v"):
+               "mla_combine_up_v", "mla_append_kv_workspace_bytes", "mla_append_kv"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
@@ -164,3 +166,19 @@ def mla_combine_up_v(shape: MlaShape, num_parts: int, o_part, lse_part, seq_lens
     _check(library().mla_combine_up_v(ctypes.byref(shape), int(num_parts), _ptr(o_part), _ptr(lse_part),
                                       _ptr(seq_lens), _ptr(w_uv), _ptr(out), _ptr(lse), _stream(stream)),
            "mla_combine_up_v")
+
+
+def mla_append_kv_workspace_bytes(shape: MlaShape, d_model: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().mla_append_kv_workspace_bytes(ctypes.byref(shape), int(d_model), ctypes.byref(n)),
+           "mla_append_kv_workspace_bytes")
+    return n.value
+
+
+def mla_append_kv(shape: MlaShape, d_model: int, x, w_dkv, rope_base: float, c_kv, k_rope, token_stride: int,
+                  block_stride: int, kv_scale, block_table, seq_lens, workspace, workspace_bytes: int,
+                  stream=None) -> None:
+    _check(library().mla_append_kv(ctypes.byref(shape), int(d_model), _ptr(x), _ptr(w_dkv), float(rope_base),
+                                   _ptr(c_kv), _ptr(k_rope), int(token_stride), int(block_stride), _ptr(kv_scale),
+                                   _ptr(block_table), _ptr(seq_lens), _ptr(workspace), int(workspace_bytes),
+                                   _stream(stream)), "mla_append_kv")

@@ -227,6 +227,14 @@ hipError_t launch_up(const HeadGemmParams& p, hipStream_t stream) {
 
 }  // namespace
 
+// Split-K partial products of a product too deep for one work-group (the
+// cache append's x . [W_DKV | W_KR]): bf16 A and W, fp32 C, one K slice of
+// K = 128 or 256 per "head".
+hipError_t launch_head_gemm_partials(const HeadGemmParams& p, hipStream_t stream) {
+  if (p.N % kSub != 0 || (p.K != 128 && p.K != 256)) return hipErrorInvalidValue;
+  return launch_nks<false, true, 1, 2, 4>(p, p.K / 64, stream);
+}
+
 bool head_gemm_supported(int K, int N) {
   // K = 64 or 128 with N a multiple of 256 (four sub-tiles), or K a multiple
   // of 64 in [192, 512] with N a multiple of 64 (K split four ways).

@@ -265,4 +265,90 @@ mla_status_t mla_combine_up_v(const mla_shape_t* shape, int32_t num_parts, const
   return hip_status(mla::launch_combine_up(p, stream), "mla_combine_up_v launch");
 }
 
+namespace {
+
+mla_status_t append_slices(const mla_shape_t* shape, int32_t d_model, int* ks) {
+  if (d_model < mla::kAppendSlice || d_model % mla::kAppendSlice != 0 || d_model > (1 << 16))
+    return fail(MLA_ERR_UNSUPPORTED, "d_model %d (a multiple of %d up to 65536)", d_model, mla::kAppendSlice);
+  *ks = d_model / mla::kAppendSlice;
+  (void)shape;
+  return MLA_OK;
+}
+
+}  // namespace
+
+mla_status_t mla_append_kv_workspace_bytes(const mla_shape_t* shape, int32_t d_model, size_t* bytes) {
+  mla_status_t st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  int ks = 0;
+  st = append_slices(shape, d_model, &ks);
+  if (st != MLA_OK) return st;
+  *bytes = (size_t)shape->batch * shape->q_len * ks * (shape->d_latent + shape->d_rope) * sizeof(float);
+  return ok();
+}
+
+mla_status_t mla_append_kv(const mla_shape_t* shape, int32_t d_model, const void* x, const void* w_dkv,
+                           float rope_base, void* c_kv, void* k_rope, int64_t token_stride, int64_t block_stride,
+                           float* kv_scale, const int32_t* block_table, const int32_t* seq_lens, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  mla_status_t st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  int ks = 0;
+  st = append_slices(shape, d_model, &ks);
+  if (st != MLA_OK) return st;
+  if (!x || !w_dkv || !c_kv || !k_rope || !block_table || !seq_lens || !workspace)
+    return fail(MLA_ERR_INVALID_ARG, "mla_append_kv: NULL tensor");
+  if (!std::isfinite(rope_base) || rope_base <= 1.0f)
+    return fail(MLA_ERR_INVALID_ARG, "mla_append_kv: rope_base must be finite and > 1");
+  const bool fp8 = shape->cache_dtype == MLA_FP8_E4M3;
+  if (fp8 && !kv_scale) return fail(MLA_ERR_INVALID_ARG, "mla_append_kv: fp8 cache needs kv_scale");
+  if (!fp8 && kv_scale) return fail(MLA_ERR_INVALID_ARG, "mla_append_kv: kv_scale given for a bf16 cache");
+  if (!aligned16(x) || !aligned16(w_dkv) || !aligned16(workspace) || !aligned16(c_kv) || !aligned16(k_rope))
+    return fail(MLA_ERR_INVALID_ARG, "mla_append_kv: tensors must be 16-byte aligned");
+  const int elem = fp8 ? 1 : 2;
+  const int64_t rope_off = static_cast<const char*>(k_rope) - static_cast<const char*>(c_kv);
+  if (token_stride <= 0 || token_stride % 16 || block_stride % 16 ||
+      block_stride < (int64_t)shape->block_size * token_stride)
+    return fail(MLA_ERR_INVALID_ARG,
+                "mla_append_kv: token_stride/block_stride must be positive multiples of 16 with "
+                "block_stride >= block_size * token_stride");
+  if (rope_off < (int64_t)shape->d_latent * elem || rope_off + (int64_t)shape->d_rope * elem > token_stride)
+    return fail(MLA_ERR_INVALID_ARG, "mla_append_kv: k_rope must follow the latent inside the record");
+  size_t need = 0;
+  st = mla_append_kv_workspace_bytes(shape, d_model, &need);
+  if (st != MLA_OK) return st;
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_INVALID_ARG, "mla_append_kv: workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  const int M = shape->batch * shape->q_len;
+  mla::HeadGemmParams g{};
+  g.a = x;
+  g.w = static_cast<const uint16_t*>(w_dkv);
+  g.c = workspace;
+  g.M = M;
+  g.H = ks;
+  g.K = mla::kAppendSlice;
+  g.N = shape->d_latent + shape->d_rope;
+  hipError_t e = mla::launch_head_gemm_partials(g, stream);
+  if (e != hipSuccess) return hip_status(e, "mla_append_kv product launch");
+  mla::AppendParams p{};
+  p.part = static_cast<const float*>(workspace);
+  p.KS = ks;
+  p.M = M;
+  p.S = shape->q_len;
+  p.DC = shape->d_latent;
+  p.c_kv = static_cast<char*>(c_kv);
+  p.rope_off = rope_off;
+  p.token_stride = token_stride;
+  p.block_stride = block_stride;
+  p.kv_scale = kv_scale;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.bt_stride = shape->max_blocks_per_seq;
+  p.block_size = shape->block_size;
+  p.log2_base = std::log2((double)rope_base);
+  p.fp8 = fp8;
+  return hip_status(mla::launch_append_finish(p, stream), "mla_append_kv launch");
+}
+
 }  // extern "C"

@@ -80,5 +80,26 @@ struct HeadGemmParams {
 // Whether a kernel exists for reduction depth K and N output columns per head.
 bool head_gemm_supported(int K, int N);
 hipError_t launch_head_gemm(const HeadGemmParams& p, bool a_fp32, bool c_fp32, hipStream_t stream);
+// bf16 A, fp32 C, K = 128 or 256 per head, N a multiple of 64.
+hipError_t launch_head_gemm_partials(const HeadGemmParams& p, hipStream_t stream);
+
+// Cache append: the records of the S_q new tokens of every sequence from the
+// split-K partial products of x . [W_DKV | W_KR].
+constexpr int kAppendSlice = 256;  // d_model columns per partial product
+struct AppendParams {
+  const float* part;         // fp32 [M, KS, DC + 64]: row m's partial products
+  int32_t KS, M, S;          // K slices, rows (B * S_q), S_q
+  int32_t DC;                // latent width; the record is DC + 64 values
+  char* c_kv;                // latent of page 0, slot 0
+  int64_t rope_off;          // bytes from a record's latent to its RoPE key
+  int64_t token_stride, block_stride;
+  float* kv_scale;           // e4m3 only: [pages][block_size]
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int32_t bt_stride, block_size;
+  double log2_base;          // log2 of the RoPE base
+  int32_t fp8;
+};
+hipError_t launch_append_finish(const AppendParams& p, hipStream_t stream);
 
 }  // namespace mla

@@ -12,7 +12,8 @@ import numpy as np
 
 from .binding import (
     MLA_BF16, MLA_FP8_E4M3, MLA_FP16, MLA_FP32, MLA_TILE_TOKENS, MlaShape,
-    mla_absorb_q, mla_decode_num_parts, mla_decode_paged, mla_combine_lse, mla_combine_up_v, mla_up_v,
+    mla_absorb_q, mla_append_kv, mla_append_kv_workspace_bytes, mla_decode_num_parts, mla_decode_paged,
+    mla_combine_lse, mla_combine_up_v, mla_up_v,
 )
 
 
@@ -100,6 +101,27 @@ class DecodeStep:
         self.o_lat = None if self.fused else torch.empty((B, S, H, DC), dtype=f32, device=device)
         self.lse = torch.empty((B, S, H), dtype=f32, device=device)
         self.out = torch.empty((B, S, H, w.d_v), dtype=f32 if w.out_dtype == "fp32" else bf16, device=device)
+
+    def set_append_inputs(self, ap: dict):
+        """Device copies of the cache-append inputs (hidden states x and the
+        combined [W_DKV | W_KR]) and the append's workspace."""
+        torch = self.torch
+        device = self.q_nope.device
+        self.x = _dev_bits(torch, ap["x"], device, torch.bfloat16)
+        self.w_dkv = _dev_bits(torch, ap["w_dkv"], device, torch.bfloat16)
+        self.rope_base = float(ap["rope_base"])
+        self.d_model = int(ap["x"].shape[-1])
+        nbytes = mla_append_kv_workspace_bytes(self.shape, self.d_model)
+        self.append_ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+    def append(self, stream=None, cache=None, kv_scale=None):
+        """Write the new tokens' records [c_KV | k_rope] into the cache."""
+        cache = self.cache if cache is None else cache
+        kv_scale = self.kv_scale if kv_scale is None else kv_scale
+        base = cache.data_ptr()
+        mla_append_kv(self.shape, self.d_model, self.x, self.w_dkv, self.rope_base, base,
+                      base + self.workload.d_latent * self.elem, self.token_stride, self.block_stride, kv_scale,
+                      self.block_table, self.seq_lens, self.append_ws, self.append_ws.numel(), stream)
 
     def absorb(self, stream=None):
         mla_absorb_q(self.shape, self.q_nope, self.w_uk, self.q_lat, stream)

@@ -11,7 +11,8 @@
  *   mla_combine_lse   log-sum-exp merge of the splits -> o_lat, lse
  *   mla_up_v          out = o_lat . W_UV[h]                  (per head)
  *
- * mla_combine_up_v does the last two in one launch without writing o_lat.
+ * mla_combine_up_v does the last two in one launch without writing o_lat;
+ * mla_append_kv writes the new tokens' records into the cache beforehand.
  *
  * What the method is, and where the pages say it:
  *  - Only one low-rank latent c_KV per token is cached, next to one decoupled
@@ -203,6 +204,40 @@ mla_status_t mla_up_v(const mla_shape_t* shape, const float* o_lat, const void* 
 mla_status_t mla_combine_up_v(const mla_shape_t* shape, int32_t num_parts, const void* o_part,
                               const float* lse_part, const int32_t* seq_lens, const void* w_uv, void* out,
                               float* lse, hipStream_t stream);
+
+/*
+ * mla_append_kv -- write the records of the S_q new tokens of every sequence
+ * into the paged cache (the step before mla_decode_paged).
+ *   y        = x[b,s,:] . W                     (fp32 accumulation)
+ *   c_KV     = y[0 : d_latent]                  (the latent: x . W_DKV)
+ *   k_rope   = RoPE_pos(y[d_latent : d_latent + d_rope])
+ *   record   -> page block_table[b][pos / block_size], slot pos % block_size,
+ *               pos = seq_lens[b] - S_q + s (the new tokens are the last S_q
+ *               positions, the queries' convention); an idle slot (0) is skipped.
+ * The latent is the down-projection W_DKV of Eq. (11) on the TransMLA review
+ * page (referee_report.minor_comments); only it and one RoPE key shared by all
+ * heads are cached (core_discovery on that page; TPLA abstract).
+ *   x      bf16 [B, S_q, d_model]; d_model a multiple of 256 up to 65536
+ *   w_dkv  bf16 [d_model, d_latent + d_rope]: [W_DKV | W_KR], latent columns first
+ *   rope_base  RoPE base (> 1, e.g. 10000): pair (2i, 2i+1) of the d_rope
+ *          values turns by pos * rope_base^(-2i/d_rope), counter-clockwise
+ *   cache  as for mla_decode_paged (same c_kv, k_rope, strides, block_table,
+ *          seq_lens); bf16 records are rounded to nearest even; for an e4m3
+ *          cache the record is stored as e4m3 (nearest even) of v / scale with
+ *          scale = max|v| / 448 over the record (1 if all zero) written to
+ *          kv_scale[page][slot].
+ *   workspace  device scratch of at least mla_append_kv_workspace_bytes, 16-byte
+ *          aligned, owned by the caller; its contents are not needed afterwards.
+ * Two kernels are enqueued (the product, then the records).  Only the new
+ * tokens' slots (and their scales) are written.  x, w_dkv, c_kv, k_rope 16-byte
+ * aligned.
+ */
+mla_status_t mla_append_kv_workspace_bytes(const mla_shape_t* shape, int32_t d_model, size_t* bytes);
+mla_status_t mla_append_kv(const mla_shape_t* shape, int32_t d_model, const void* x, const void* w_dkv,
+                           float rope_base, void* c_kv, void* k_rope, int64_t token_stride,
+                           int64_t block_stride, float* kv_scale, const int32_t* block_table,
+                           const int32_t* seq_lens, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 /* Static description of a status code. */
 const char* mla_status_string(mla_status_t status);

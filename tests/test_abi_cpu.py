@@ -21,7 +21,8 @@ def test_exports_every_declared_symbol():
     lib = _lib()
     declared = mla.exported_symbols()
     assert set(declared) >= {"mla_absorb_q", "mla_decode_num_parts", "mla_decode_paged", "mla_combine_lse",
-                             "mla_up_v", "mla_combine_up_v", "mla_status_string", "mla_last_error"}
+                             "mla_up_v", "mla_combine_up_v", "mla_append_kv", "mla_append_kv_workspace_bytes",
+                             "mla_status_string", "mla_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", mla.library_path], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for name in declared:
@@ -162,3 +163,42 @@ def test_split_plan_covers_every_tile_once():
                 assert t0 == pos and t1 > t0
                 pos = t1
             assert pos == L
+
+
+def _append(sh, d_model=4096, ws_bytes=None, **kw):
+    lib = _lib()
+    need = ctypes.c_size_t(0)
+    st = lib.mla_append_kv_workspace_bytes(ctypes.byref(sh), d_model, ctypes.byref(need))
+    a = dict(x=FAKE, w=FAKE, base=10000.0, c_kv=FAKE, k_rope=FAKE + 1024, ts=1152, bst=64 * 1152, kv_scale=None,
+             bt=FAKE, sl=FAKE, ws=FAKE)
+    a.update(kw)
+    nbytes = need.value if ws_bytes is None else ws_bytes
+    return lib.mla_append_kv(ctypes.byref(sh), d_model, a["x"], a["w"], a["base"], a["c_kv"], a["k_rope"], a["ts"],
+                             a["bst"], a["kv_scale"], a["bt"], a["sl"], a["ws"], nbytes, None), st, need.value
+
+
+def test_append_workspace_size():
+    lib = _lib()
+    sh = _shape(batch=3, q_len=2)
+    n = ctypes.c_size_t(0)
+    assert lib.mla_append_kv_workspace_bytes(ctypes.byref(sh), 4096, ctypes.byref(n)) == mla.MLA_OK
+    assert n.value == 3 * 2 * (4096 // 256) * (512 + 64) * 4
+    assert lib.mla_append_kv_workspace_bytes(ctypes.byref(sh), 1000, ctypes.byref(n)) == mla.MLA_ERR_UNSUPPORTED
+    assert lib.mla_append_kv_workspace_bytes(ctypes.byref(sh), 4096, None) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_append_argument_checks():
+    sh = _shape()
+    for name in ("x", "w", "c_kv", "bt", "sl", "ws"):
+        assert _append(sh, **{name: None})[0] == mla.MLA_ERR_INVALID_ARG, name
+    assert _append(sh, x=FAKE + 2)[0] == mla.MLA_ERR_INVALID_ARG                     # misaligned
+    assert _append(sh, base=1.0)[0] == mla.MLA_ERR_INVALID_ARG                       # rope_base must exceed 1
+    assert _append(sh, base=math.nan)[0] == mla.MLA_ERR_INVALID_ARG
+    assert _append(sh, kv_scale=FAKE)[0] == mla.MLA_ERR_INVALID_ARG                  # scale with a bf16 cache
+    assert _append(_shape(cache_dtype=mla.MLA_FP8_E4M3), k_rope=FAKE + 512, ts=576,
+                   bst=64 * 576)[0] == mla.MLA_ERR_INVALID_ARG                       # fp8 needs kv_scale
+    assert _append(sh, k_rope=FAKE + 512)[0] == mla.MLA_ERR_INVALID_ARG              # RoPE key overlaps the latent
+    assert _append(sh, d_model=1000)[0] == mla.MLA_ERR_UNSUPPORTED                   # not a multiple of 256
+    st, _, need = _append(sh)
+    assert _append(sh, ws_bytes=need - 4)[0] == mla.MLA_ERR_INVALID_ARG              # workspace too small
+    assert "workspace" in mla.mla_last_error()
