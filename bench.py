@@ -4,8 +4,11 @@ LSE merge fused with the up-projection) on one MI355X, on synthetic inputs.
 Prints one JSON line.  ``value`` is the effective latent-cache read rate of
 the whole step (algorithmic cache bytes / step time) with every input already
 resident in HBM; the step time itself is ``ms_per_step`` (and ``us_per_step``),
-timed over replays of the step captured as a HIP graph (``--no-graph``: eager
-launches; ``--unfused``: separate merge and up-projection launches).  Per-call
+timed over replays of HIP graphs that each run the steps of all input
+replicas in order, as the attention of consecutive layers runs within one
+captured forward pass (``--graph-steps 1``: one step per replay, also
+reported as ``graph_1step_us_per_step``; ``--no-graph``: eager launches;
+``--unfused``: separate merge and up-projection launches).  Per-call
 times and the decode kernel's roofline come from an eager loop with HIP events
 between the calls.
 Consecutive steps rotate through independent replicas of all inputs whose
@@ -141,6 +144,9 @@ def main():
                     help="after timing, run a plain copy of this many MiB (counter calibration)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the step as eager launches instead of one HIP-graph replay")
+    ap.add_argument("--graph-steps", type=int, default=0,
+                    help="steps per graph replay (consecutive replicas, like the layers of one forward "
+                         "pass); 0 = all replicas, 1 = one step per replay")
     ap.add_argument("--unfused", action="store_true",
                     help="merge (mla_combine_lse) and up-project (mla_up_v) in two launches")
     args = ap.parse_args()
@@ -184,20 +190,41 @@ def main():
     # kernels, no host work between them) and replayed; --no-graph times
     # the eager loop below instead.
     graph_ms = None
+    graph1_ms = None
+    R = nrep if args.graph_steps <= 0 else min(args.graph_steps, nrep)
     if not args.no_graph:
+        from head_latent_attention_absorbed_amd import capture_steps
+
         for st in steps:
             st.capture()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        # One step per replay (each replica's own graph).
         for i in range(args.warmup):
             steps[i % nrep].replay()
         torch.cuda.synchronize()
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
         g0.record(stream)
         for i in range(K):
             steps[(args.warmup + i) % nrep].replay()
         g1.record(stream)
         torch.cuda.synchronize()
-        graph_ms = g0.elapsed_time(g1) / K
+        graph1_ms = g0.elapsed_time(g1) / K
+        # R consecutive replicas per replay, as the layers of one forward pass:
+        # K // R such replays plus K % R single-step ones, K steps in all.
+        graph_ms = graph1_ms
+        if R > 1:
+            multi = capture_steps(steps[:R])
+            for i in range(max(1, args.warmup // R)):
+                multi.replay()
+            torch.cuda.synchronize()
+            g0.record(stream)
+            for i in range(K // R):
+                multi.replay()
+            for i in range(K % R):
+                steps[i].replay()
+            g1.record(stream)
+            torch.cuda.synchronize()
+            graph_ms = g0.elapsed_time(g1) / K
 
     # Per-call times: the same steps as eager launches with HIP events
     # between the calls, on the stream the kernels run on.
@@ -280,7 +307,9 @@ def main():
             "num_parts": steps[0].num_parts, "partials": args.partial,
             "merge": "fused with up-projection" if steps[0].fused else "separate launches",
         },
-        "step_launch": "hip_graph" if graph_ms is not None else "eager",
+        "step_launch": (f"hip_graph, {R} steps (replicas) per replay" if R > 1 else "hip_graph, 1 step per replay")
+                       if graph_ms is not None else "eager",
+        "graph_1step_us_per_step": round(graph1_ms * 1e3, 2) if graph1_ms is not None else None,
         "eager_us_per_step": round(eager_ms * 1e3, 2),
         "per_call_us_median": {k: round(v, 2) for k, v in med.items()},
         "step_hbm_frac": round(value * 1e3 / HBM_PEAK_GBS, 4),

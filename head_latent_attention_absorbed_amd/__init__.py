@@ -32,4 +32,4 @@ from .binding import (  # noqa: F401
     mla_status_string,
     mla_last_error,
 )
-from .step import DecodeStep, combine_up_supported, split_plan  # noqa: F401
+from .step import DecodeStep, capture_steps, combine_up_supported, split_plan  # noqa: F401

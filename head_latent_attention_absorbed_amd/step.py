@@ -182,3 +182,25 @@ class DecodeStep:
     def replay(self):
         self.graph.replay()
         return self.out
+
+
+def capture_steps(steps):
+    """Record several steps (e.g. the attention of consecutive layers, each
+    with its own cache and weights) into one HIP graph that runs them in
+    order, as a whole forward pass would be captured.  Like DecodeStep.capture,
+    the graph works on the steps' buffers in place, and one eager pass runs
+    first (outside the capture) to do the library's one-time setup."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for st in steps:
+            st.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for st in steps:
+            st.run()
+    return graph

@@ -216,3 +216,28 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
     tol_abs, tol_rel = tolerances(inputs["workload"])
     compare("graph out", to_np(st.out), oracle.decode(inputs)["out"], tol_abs, tol_rel)
+
+
+def test_multi_step_graph_matches_eager():
+    """Three steps over different inputs (as consecutive layers would be)
+    captured in one graph: every replay equals each step's eager result bit
+    for bit, with eager work and synchronisations between the replays."""
+    import torch
+    from head_latent_attention_absorbed_amd import DecodeStep, capture_steps
+
+    cases = [SMALL_CASES["h128_ragged"], SMALL_CASES["dc256"], SMALL_CASES["fp8_sq4_h64"]]
+    inputs = [make_inputs(w) for w in cases]
+    _announce("multi-step graph", inputs[0])
+    refs = [to_np(run_step(i).out) for i in inputs]
+    steps = [DecodeStep(i) for i in inputs]
+    graph = capture_steps(steps)
+    other = DecodeStep(inputs[0])
+    for rep in range(3):
+        for st in steps:
+            st.out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for j, st in enumerate(steps):
+            assert np.array_equal(to_np(st.out), refs[j]), f"replay {rep}, step {j} differs from the eager step"
+        other.run()
+        torch.cuda.synchronize()
