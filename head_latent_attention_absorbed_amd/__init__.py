@@ -29,7 +29,10 @@ from .binding import (  # noqa: F401
     mla_combine_up_v,
     mla_append_kv,
     mla_append_kv_workspace_bytes,
+    mla_prefill_workspace_bytes,
+    mla_prefill_kv,
+    mla_prefill_attention,
     mla_status_string,
     mla_last_error,
 )
-from .step import DecodeStep, capture_steps, combine_up_supported, split_plan  # noqa: F401
+from .step import DecodeStep, PrefillStep, capture_steps, combine_up_supported, split_plan  # noqa: F401

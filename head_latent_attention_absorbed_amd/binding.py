@@ -81,8 +81,12 @@ def library() -> ctypes.CDLL:
     lib.mla_combine_up_v.argtypes = [SP, I32, P, P, P, P, P, P, P]
     lib.mla_append_kv_workspace_bytes.argtypes = [SP, I32, ctypes.POINTER(ctypes.c_size_t)]
     lib.mla_append_kv.argtypes = [SP, I32, P, P, F, P, P, I64, I64, P, P, P, P, ctypes.c_size_t, P]
+    lib.mla_prefill_workspace_bytes.argtypes = [SP, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_prefill_kv.argtypes = [SP, I32, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.mla_prefill_attention.argtypes = [SP, I32, P, P, P, P, P, P, P, P, P]
     for fn in ("mla_absorb_q", "mla_decode_num_parts", "mla_decode_paged", "mla_combine_lse", "mla_up_v",
-               "mla_combine_up_v", "mla_append_kv_workspace_bytes", "mla_append_kv"):
+               "mla_combine_up_v", "mla_append_kv_workspace_bytes", "mla_append_kv", "mla_prefill_workspace_bytes",
+               "mla_prefill_kv", "mla_prefill_attention"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
@@ -182,3 +186,23 @@ def mla_append_kv(shape: MlaShape, d_model: int, x, w_dkv, rope_base: float, c_k
                                    _ptr(c_kv), _ptr(k_rope), int(token_stride), int(block_stride), _ptr(kv_scale),
                                    _ptr(block_table), _ptr(seq_lens), _ptr(workspace), int(workspace_bytes),
                                    _stream(stream)), "mla_append_kv")
+
+
+def mla_prefill_workspace_bytes(shape: MlaShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().mla_prefill_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)), "mla_prefill_workspace_bytes")
+    return n.value
+
+
+def mla_prefill_kv(shape: MlaShape, prompt_len: int, ckr, w_uk, w_uv, k_nope, v, workspace, workspace_bytes: int,
+                   stream=None) -> None:
+    _check(library().mla_prefill_kv(ctypes.byref(shape), int(prompt_len), _ptr(ckr), _ptr(w_uk), _ptr(w_uv),
+                                    _ptr(k_nope), _ptr(v), _ptr(workspace), int(workspace_bytes), _stream(stream)),
+           "mla_prefill_kv")
+
+
+def mla_prefill_attention(shape: MlaShape, prompt_len: int, q_nope, q_rope, k_nope, ckr, v, seq_lens, out, lse,
+                          stream=None) -> None:
+    _check(library().mla_prefill_attention(ctypes.byref(shape), int(prompt_len), _ptr(q_nope), _ptr(q_rope),
+                                           _ptr(k_nope), _ptr(ckr), _ptr(v), _ptr(seq_lens), _ptr(out), _ptr(lse),
+                                           _stream(stream)), "mla_prefill_attention")

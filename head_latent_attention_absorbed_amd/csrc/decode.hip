@@ -819,6 +819,137 @@ hipError_t launch_dc(const DecodeParams& p, int nw, hipStream_t stream) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill in the MLA form (keys and values reconstructed per head, as the
+// prefill-decode separation of the TPLA abstract keeps for the compute-bound
+// prefill): every position of a prompt attends causally to the positions up
+// to it, per head, over K = [W_UK c ; k_rope] (128 + 64) and V = c W_UV (128)
+// made by mla_prefill_kv.  The tile products, the online softmax and P.V
+// are the decode's, at latent width 128: a 32-token tile of K (24 granule
+// rows) and of V (16 rows) in the same granule-major LDS layout, one wave per
+// 32 query positions of one head, four waves per work-group.  Tiles are
+// loaded through registers, one tile ahead, into two LDS buffers.
+constexpr int kPfRows = 128;  // query positions per work-group
+
+template <int TPT>
+struct PfTileLoad {  // this thread's 16-byte granules of one K + V tile
+  uint4 v[TPT];
+};
+
+__global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
+  using Gm = Geo<128>;
+  constexpr int KROWS = Gm::GPT;   // 24 granule rows of K
+  constexpr int VROWS = 16;        // 16 granule rows of V
+  constexpr int TB = (KROWS + VROWS) * kRow;
+  constexpr int GRAN = (KROWS + VROWS) * kTile;  // granules per tile
+  constexpr int TPT = GRAN / 256;                // per thread
+  static_assert(GRAN % 256 == 0, "granules split evenly over the threads");
+  __shared__ __attribute__((aligned(1024))) char tiles[2 * TB];
+
+  const int tid = threadIdx.x;
+  const int w = uniform(tid >> 6);
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int ntile = (p.P + kPfRows - 1) / kPfRows;
+  const int qt = ntile - 1 - (int)blockIdx.x;  // longest rows first
+  const int L = min(p.seq_lens[b], p.P);
+  const int q0 = qt * kPfRows;
+  if (q0 >= L) return;
+  const int nkt = (min(L, q0 + kPfRows) + kTile - 1) / kTile;  // key tiles this group needs
+
+  // Granule i of a tile (row g = i / 32, token t = i % 32): global source.
+  const int64_t tok0 = (int64_t)b * p.P;
+  auto load = [&](int kt, PfTileLoad<TPT>& r) {
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      const int i = tid + 256 * j;
+      const int g = i >> 5, t = i & 31;
+      const int pos = kt * kTile + t;
+      const int64_t tk = tok0 + min(pos, L - 1);
+      const uint16_t* src;
+      if (g < 16) src = p.k_nope + (tk * p.H + h) * 128 + 8 * g;
+      else if (g < KROWS) src = p.ckr + tk * (p.DCK + 64) + p.DCK + 8 * (g - 16);
+      else src = p.v + (tk * p.H + h) * 128 + 8 * (g - KROWS);
+      r.v[j] = *(const uint4*)src;
+    }
+  };
+  auto store = [&](int kt, const PfTileLoad<TPT>& r, char* tb) {
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      const int i = tid + 256 * j;
+      const int g = i >> 5, t = i & 31;
+      const bool valid = kt * kTile + t < L;  // positions past the prompt read as zeros
+      *(uint4*)(tb + g * kRow + ((t ^ ((g & 1) << 2)) << 4)) = valid ? r.v[j] : uint4{0, 0, 0, 0};
+    }
+  };
+
+  // This wave's 32 query positions.
+  const int lane = opaque_lane();
+  const int col = lane & 31;
+  const int pos = q0 + 32 * w + col;
+  bf16x8 qf[Gm::KS];
+  {
+    const int64_t row = (tok0 + min(pos, L - 1)) * p.H + h;
+    const bf16x8* ql = (const bf16x8*)(p.q_nope + row * 128 + 8 * (lane >> 5));
+    const bf16x8* qr = (const bf16x8*)(p.q_rope + row * 64 + 8 * (lane >> 5));
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = ql[2 * ks];
+#pragma unroll
+    for (int ks = 8; ks < Gm::KS; ++ks) qf[ks] = qr[2 * (ks - 8)];
+  }
+  const int limit = min(pos + 1, L);  // causal: this row sees positions < limit
+
+  PfTileLoad<TPT> nxt;
+  load(0, nxt);
+  store(0, nxt, tiles);
+  if (nkt > 1) load(1, nxt);
+  block_sync();
+
+  f32x16 O[Gm::NB];
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+  bf16x8 pf0, pf1;
+  float alpha;
+  auto tile = [&](int kt, auto first_tag) {
+    constexpr bool FIRST = decltype(first_tag)::value;
+    const char* tb = tiles + (kt & 1) * TB;
+    // fully visible to every row of the group: below its first position
+    const bool full = (kt + 1) * kTile <= q0;
+    score_tile<128, false, 0>(tb, nullptr, qf, m_run, l_run, kt * kTile, limit, full, p.scale_log2, pf0, pf1,
+                              alpha, NoDma{});
+    if constexpr (!FIRST) {
+      if (__any(alpha != 1.0f)) rescale<128>(O, alpha);
+    }
+    pv_tile<128, kPvAhead, FIRST>(tb + KROWS * kRow, pf0, pf1, O);
+    // the next tile into the other buffer, the one after into registers
+    if (kt + 1 < nkt) {
+      store(kt + 1, nxt, tiles + ((kt + 1) & 1) * TB);
+      if (kt + 2 < nkt) load(kt + 2, nxt);
+    }
+    block_sync();
+  };
+  tile(0, std::true_type{});
+  for (int kt = 1; kt < nkt; ++kt) tile(kt, std::false_type{});
+
+  // Normalise and write this wave's rows: lane (col, half) holds row `col`,
+  // columns 32 nb + 8 (i / 4) + 4 half + i % 4 of block nb.
+  const float l_tot = pair_sum(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (pos < L) {
+    const int half = opaque_lane() >> 5;
+    const int64_t row = (tok0 + pos) * p.H + h;
+    if (half == 0) p.lse[row] = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -__builtin_inff();
+    uint16_t* dst = p.out + row * 128 + 4 * half;
+#pragma unroll
+    for (int nb = 0; nb < Gm::NB; ++nb) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x2 a = {(__bf16)(O[nb][4 * q] * inv), (__bf16)(O[nb][4 * q + 1] * inv)};
+        const bf16x2 c = {(__bf16)(O[nb][4 * q + 2] * inv), (__bf16)(O[nb][4 * q + 3] * inv)};
+        *(uint2*)(dst + 32 * nb + 8 * q) = uint2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c)};
+      }
+    }
+  }
+}
+
 }  // namespace
 
 int decode_waves(int R) { return R <= 32 ? 1 : (R <= 64 ? 2 : 4); }
@@ -835,6 +966,13 @@ hipError_t launch_decode(const DecodeParams& p, int d_latent, bool fp8, hipStrea
   const int nw = decode_waves(p.R);
   if (d_latent == 512) return fp8 ? launch_dc<512, true>(p, nw, stream) : launch_dc<512, false>(p, nw, stream);
   return fp8 ? launch_dc<256, true>(p, nw, stream) : launch_dc<256, false>(p, nw, stream);
+}
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+  if (p.B <= 0 || p.P <= 0) return hipSuccess;
+  const dim3 grid((p.P + kPfRows - 1) / kPfRows, p.H, p.B);
+  hipLaunchKernelGGL(prefill_kernel, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace mla

@@ -40,7 +40,9 @@ __device__ __forceinline__ void load_a(const HeadGemmParams& p, int m0, int col,
                                        bf16x8 (&ahi)[NKS], f32x4 (&af)[2 * NKS]) {
   const int m = m0 + col;
   const bool valid = m < p.M;
-  const int64_t rowoff = ((int64_t)min(m, p.M - 1) * p.H + h) * p.K + kbeg + 8 * half;
+  const int64_t ar = p.a_row ? p.a_row : (int64_t)p.H * p.K;
+  const int64_t ah = p.a_row ? p.a_head : (int64_t)p.K;
+  const int64_t rowoff = (int64_t)min(m, p.M - 1) * ar + h * ah + kbeg + 8 * half;
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     if constexpr (AF32) {
@@ -233,6 +235,38 @@ hipError_t launch_up(const HeadGemmParams& p, hipStream_t stream) {
 hipError_t launch_head_gemm_partials(const HeadGemmParams& p, hipStream_t stream) {
   if (p.N % kSub != 0 || (p.K != 128 && p.K != 256)) return hipErrorInvalidValue;
   return launch_nks<false, true, 1, 2, 4>(p, p.K / 64, stream);
+}
+
+namespace {
+
+// W [H, R, C] -> [H, C, R], one 64 x 64 tile per work-group through LDS (rows
+// padded by 8 elements so that the transposed reads spread over the banks).
+__global__ void __launch_bounds__(256) transpose_heads_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ wt,
+                                                              int R, int C) {
+  __shared__ uint16_t t[64][64 + 8];
+  const int h = blockIdx.z, r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tid = threadIdx.x;
+  const uint16_t* src = w + ((int64_t)h * R + r0) * C + c0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int i = tid + 256 * j;
+    t[i / 64][i % 64] = src[(int64_t)(i / 64) * C + i % 64];
+  }
+  __syncthreads();
+  uint16_t* dst = wt + ((int64_t)h * C + c0) * R + r0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int i = tid + 256 * j;
+    dst[(int64_t)(i / 64) * R + i % 64] = t[i % 64][i / 64];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_transpose_heads(const uint16_t* w, uint16_t* wt, int H, int R, int C, hipStream_t stream) {
+  if (R % 64 || C % 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_heads_kernel, dim3(C / 64, R / 64, H), dim3(256), 0, stream, w, wt, R, C);
+  return hipGetLastError();
 }
 
 bool head_gemm_supported(int K, int N) {

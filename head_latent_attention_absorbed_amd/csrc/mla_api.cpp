@@ -351,4 +351,91 @@ mla_status_t mla_append_kv(const mla_shape_t* shape, int32_t d_model, const void
   return hip_status(mla::launch_append_finish(p, stream), "mla_append_kv launch");
 }
 
+namespace {
+
+mla_status_t check_prefill(const mla_shape_t* shape, int32_t prompt_len) {
+  mla_status_t st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (shape->d_nope != 128 || shape->d_v != 128)
+    return fail(MLA_ERR_UNSUPPORTED, "prefill: d_nope %d, d_v %d (kernels exist for 128, 128)", shape->d_nope,
+                shape->d_v);
+  if (prompt_len < 1 || (int64_t)shape->batch * prompt_len > (1 << 24))
+    return fail(MLA_ERR_INVALID_ARG, "prefill: prompt_len %d out of range", prompt_len);
+  return MLA_OK;
+}
+
+}  // namespace
+
+mla_status_t mla_prefill_workspace_bytes(const mla_shape_t* shape, size_t* bytes) {
+  mla_status_t st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = (size_t)shape->num_heads * shape->d_latent * shape->d_nope * 2;  // W_UK transposed
+  return ok();
+}
+
+mla_status_t mla_prefill_kv(const mla_shape_t* shape, int32_t prompt_len, const void* ckr, const void* w_uk,
+                            const void* w_uv, void* k_nope, void* v, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  mla_status_t st = check_prefill(shape, prompt_len);
+  if (st != MLA_OK) return st;
+  if (!ckr || !w_uk || !w_uv || !k_nope || !v || !workspace)
+    return fail(MLA_ERR_INVALID_ARG, "mla_prefill_kv: NULL tensor");
+  if (!aligned16(ckr) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(k_nope) || !aligned16(v) ||
+      !aligned16(workspace))
+    return fail(MLA_ERR_INVALID_ARG, "mla_prefill_kv: tensors must be 16-byte aligned");
+  size_t need = 0;
+  st = mla_prefill_workspace_bytes(shape, &need);
+  if (st != MLA_OK) return st;
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_INVALID_ARG, "mla_prefill_kv: workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  uint16_t* wukt = static_cast<uint16_t*>(workspace);
+  hipError_t e = mla::launch_transpose_heads(static_cast<const uint16_t*>(w_uk), wukt, shape->num_heads,
+                                             shape->d_nope, shape->d_latent, stream);
+  if (e != hipSuccess) return hip_status(e, "mla_prefill_kv transpose launch");
+  mla::HeadGemmParams g{};
+  g.a = ckr;
+  g.M = shape->batch * prompt_len;
+  g.H = shape->num_heads;
+  g.K = shape->d_latent;
+  g.a_row = shape->d_latent + shape->d_rope;  // one latent row for every head
+  g.a_head = 0;
+  g.w = wukt;
+  g.c = k_nope;
+  g.N = shape->d_nope;
+  e = mla::launch_head_gemm(g, false, false, stream);
+  if (e != hipSuccess) return hip_status(e, "mla_prefill_kv key launch");
+  g.w = static_cast<const uint16_t*>(w_uv);
+  g.c = v;
+  g.N = shape->d_v;
+  return hip_status(mla::launch_head_gemm(g, false, false, stream), "mla_prefill_kv value launch");
+}
+
+mla_status_t mla_prefill_attention(const mla_shape_t* shape, int32_t prompt_len, const void* q_nope,
+                                   const void* q_rope, const void* k_nope, const void* ckr, const void* v,
+                                   const int32_t* seq_lens, void* out, float* lse, hipStream_t stream) {
+  mla_status_t st = check_prefill(shape, prompt_len);
+  if (st != MLA_OK) return st;
+  if (!q_nope || !q_rope || !k_nope || !ckr || !v || !seq_lens || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARG, "mla_prefill_attention: NULL tensor");
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(k_nope) || !aligned16(ckr) || !aligned16(v) ||
+      !aligned16(out))
+    return fail(MLA_ERR_INVALID_ARG, "mla_prefill_attention: tensors must be 16-byte aligned");
+  mla::PrefillParams p{};
+  p.q_nope = static_cast<const uint16_t*>(q_nope);
+  p.q_rope = static_cast<const uint16_t*>(q_rope);
+  p.k_nope = static_cast<const uint16_t*>(k_nope);
+  p.ckr = static_cast<const uint16_t*>(ckr);
+  p.v = static_cast<const uint16_t*>(v);
+  p.seq_lens = seq_lens;
+  p.B = shape->batch;
+  p.P = prompt_len;
+  p.H = shape->num_heads;
+  p.DCK = shape->d_latent;
+  p.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  return hip_status(mla::launch_prefill(p, stream), "mla_prefill_attention launch");
+}
+
 }  // extern "C"

@@ -39,6 +39,23 @@ int decode_wgs_per_cu(int R, int d_latent);
 
 hipError_t launch_decode(const DecodeParams& p, int d_latent, bool fp8, hipStream_t stream);
 
+// MLA-form prefill attention (d_nope 128, d_rope 64, d_v 128).
+struct PrefillParams {
+  const uint16_t* q_nope;    // bf16 [B, P, H, 128]
+  const uint16_t* q_rope;    // bf16 [B, P, H, 64]
+  const uint16_t* k_nope;    // bf16 [B, P, H, 128]
+  const uint16_t* ckr;       // bf16 [B, P, DCK + 64]: k_rope at element DCK of each record
+  const uint16_t* v;         // bf16 [B, P, H, 128]
+  const int32_t* seq_lens;
+  int32_t B, P, H, DCK;
+  float scale_log2;          // softmax_scale * log2(e)
+  uint16_t* out;             // bf16 [B, P, H, 128]
+  float* lse;                // fp32 [B, P, H]
+};
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+// W [H, R, C] bf16 -> its transpose [H, C, R] (R, C multiples of 64).
+hipError_t launch_transpose_heads(const uint16_t* w, uint16_t* wt, int H, int R, int C, hipStream_t stream);
+
 struct CombineParams {
   const void* o_part;        // fp32 or fp16 [parts, R, DC]
   int32_t o_half;
@@ -75,6 +92,9 @@ struct HeadGemmParams {
   const uint16_t* w;         // bf16
   void* c;                   // bf16 or fp32
   int32_t M, H, K, N;
+  // Element strides of A between rows and between heads; both 0 = dense
+  // [M, H, K].  a_head = 0 multiplies one row by every head's matrix.
+  int64_t a_row, a_head;
 };
 
 // Whether a kernel exists for reduction depth K and N output columns per head.

@@ -13,7 +13,7 @@ import numpy as np
 from .binding import (
     MLA_BF16, MLA_FP8_E4M3, MLA_FP16, MLA_FP32, MLA_TILE_TOKENS, MlaShape,
     mla_absorb_q, mla_append_kv, mla_append_kv_workspace_bytes, mla_decode_num_parts, mla_decode_paged,
-    mla_combine_lse, mla_combine_up_v, mla_up_v,
+    mla_combine_lse, mla_combine_up_v, mla_prefill_attention, mla_prefill_kv, mla_prefill_workspace_bytes, mla_up_v,
 )
 
 
@@ -204,3 +204,46 @@ def capture_steps(steps):
         for st in steps:
             st.run()
     return graph
+
+
+class PrefillStep:
+    """Device copies of an MLA-form prefill's inputs (padded prompts) and its
+    buffers; kv() then attention() (run() does both)."""
+
+    def __init__(self, pf: dict, device: str = "cuda"):
+        import torch
+
+        self.torch = torch
+        w = pf["workload"]
+        self.workload = w
+        self.P = int(pf["prompt_len"])
+        self.shape = MlaShape.make(
+            batch=w.batch, num_heads=w.heads, q_len=1, d_latent=w.d_latent, d_nope=w.d_nope, d_rope=w.d_rope,
+            d_v=w.d_v, block_size=w.block_size, max_blocks_per_seq=1, softmax_scale=float(pf["softmax_scale"]))
+        bf16 = torch.bfloat16
+        self.q_nope = _dev_bits(torch, pf["q_nope"], device, bf16)
+        self.q_rope = _dev_bits(torch, pf["q_rope"], device, bf16)
+        self.ckr = _dev_bits(torch, pf["ckr"], device, bf16)
+        self.w_uk = _dev_bits(torch, pf["w_uk"], device, bf16)
+        self.w_uv = _dev_bits(torch, pf["w_uv"], device, bf16)
+        self.seq_lens = torch.from_numpy(pf["seq_lens"]).to(device)
+        B, P, H = w.batch, self.P, w.heads
+        self.k_nope = torch.empty((B, P, H, w.d_nope), dtype=bf16, device=device)
+        self.v = torch.empty((B, P, H, w.d_v), dtype=bf16, device=device)
+        self.out = torch.empty((B, P, H, w.d_v), dtype=bf16, device=device)
+        self.lse = torch.empty((B, P, H), dtype=torch.float32, device=device)
+        nbytes = mla_prefill_workspace_bytes(self.shape)
+        self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+    def kv(self, stream=None):
+        mla_prefill_kv(self.shape, self.P, self.ckr, self.w_uk, self.w_uv, self.k_nope, self.v, self.ws,
+                       self.ws.numel(), stream)
+
+    def attention(self, stream=None):
+        mla_prefill_attention(self.shape, self.P, self.q_nope, self.q_rope, self.k_nope, self.ckr, self.v,
+                              self.seq_lens, self.out, self.lse, stream)
+
+    def run(self, stream=None):
+        self.kv(stream)
+        self.attention(stream)
+        return self.out

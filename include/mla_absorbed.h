@@ -12,7 +12,8 @@
  *   mla_up_v          out = o_lat . W_UV[h]                  (per head)
  *
  * mla_combine_up_v does the last two in one launch without writing o_lat;
- * mla_append_kv writes the new tokens' records into the cache beforehand.
+ * mla_append_kv writes the new tokens' records into the cache beforehand;
+ * mla_prefill_kv / mla_prefill_attention attend a whole prompt in the MLA form.
  *
  * What the method is, and where the pages say it:
  *  - Only one low-rank latent c_KV per token is cached, next to one decoupled
@@ -238,6 +239,38 @@ mla_status_t mla_append_kv(const mla_shape_t* shape, int32_t d_model, const void
                            int64_t block_stride, float* kv_scale, const int32_t* block_table,
                            const int32_t* seq_lens, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/*
+ * Prefill in the MLA form.  A prompt is compute-bound, so it is attended with
+ * keys and values reconstructed per head from the latent (the form the
+ * prefill-decode separation of the TPLA abstract keeps for prefill), not in
+ * the absorbed form the decode uses.  The prompts of the batch are padded to
+ * prompt_len = P positions; sequence b uses its first seq_lens[b] (<= P).
+ *
+ * mla_prefill_kv -- per-head keys and values of every position:
+ *   k_nope[b,t,h,:] = W_UK[h] . c[b,t]        bf16 [B, P, H, d_nope]
+ *   v[b,t,h,:]      = c[b,t] . W_UV[h]        bf16 [B, P, H, d_v]
+ *   (fp32 accumulation, bf16 RNE results; every position is computed)
+ *   ckr    bf16 [B, P, d_latent + d_rope]: the prompt's records [c_KV | k_rope]
+ *   w_uk   bf16 [H, d_nope, d_latent], w_uv bf16 [H, d_latent, d_v]
+ *   workspace of at least mla_prefill_workspace_bytes (W_UK transposed).
+ * mla_prefill_attention -- causal attention of each position s < seq_lens[b]
+ * over positions t <= s, per head:
+ *   z = scale (q_nope . k_nope + q_rope . k_rope),  out = softmax(z) . v
+ *   q_nope bf16 [B, P, H, d_nope], q_rope bf16 [B, P, H, d_rope] (already rotated),
+ *   k_rope = ckr[..., d_latent:] (shared by all heads), k_nope and v from mla_prefill_kv
+ *   out bf16 [B, P, H, d_v] and lse fp32 [B, P, H] for positions < seq_lens[b];
+ *   the other positions are left untouched.
+ * Kernels exist for d_nope = d_v = 128, d_rope = 64, d_latent 512 or 256.
+ * All tensors 16-byte aligned.
+ */
+mla_status_t mla_prefill_workspace_bytes(const mla_shape_t* shape, size_t* bytes);
+mla_status_t mla_prefill_kv(const mla_shape_t* shape, int32_t prompt_len, const void* ckr, const void* w_uk,
+                            const void* w_uv, void* k_nope, void* v, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+mla_status_t mla_prefill_attention(const mla_shape_t* shape, int32_t prompt_len, const void* q_nope,
+                                   const void* q_rope, const void* k_nope, const void* ckr, const void* v,
+                                   const int32_t* seq_lens, void* out, float* lse, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* mla_status_string(mla_status_t status);

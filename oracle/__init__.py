@@ -19,6 +19,7 @@ from .mla_oracle import (  # noqa: F401
     partial,
     combine,
     up_v,
+    prefill,
 )
 from .append_oracle import (  # noqa: F401
     rope,

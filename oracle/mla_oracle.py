@@ -213,3 +213,35 @@ def combine(o_parts: np.ndarray, lse_parts: np.ndarray):
 def up_v(o_lat: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
     """Up-projection of the latent output: out[..., h, :] = o_lat[..., h, :] W_UV[h]."""
     return np.einsum("...hc,hcv->...hv", o_lat, w_uv)
+
+
+def prefill(pf: dict, batches=None, heads=None, positions=None):
+    """MLA-form prefill of padded prompts: for each sequence b, head h and
+    position s < L_b, the attention of [q_nope; q_rope] over the keys and
+    values reconstructed from the records of positions t <= s (causal).
+    Returns out [B, P, H, d_v] and lse [B, P, H] (NaN where not computed)."""
+    w = pf["workload"]
+    P = pf["prompt_len"]
+    B, H = w.batch, w.heads
+    batches = range(B) if batches is None else batches
+    heads = range(H) if heads is None else heads
+    out = np.full((B, P, H, w.d_v), np.nan)
+    lse = np.full((B, P, H), np.nan)
+    w_uk = bf16_to_f64(pf["w_uk"])
+    w_uv = bf16_to_f64(pf["w_uv"])
+    for b in batches:
+        L = int(pf["seq_lens"][b])
+        if L == 0:
+            continue
+        rec = bf16_to_f64(pf["ckr"][b, :L])
+        C, KR = rec[:, : w.d_latent], rec[:, w.d_latent:]
+        hs = list(heads)
+        K, V = reconstruct_kv(C, KR, w_uk[hs], w_uv[hs])
+        qn = bf16_to_f64(pf["q_nope"][b, :L])[:, hs]
+        qr = bf16_to_f64(pf["q_rope"][b, :L])[:, hs]
+        ss = range(L) if positions is None else [s for s in positions if s < L]
+        for s in ss:
+            for j, h in enumerate(hs):
+                q = np.concatenate([qn[s, j], qr[s, j]])
+                _, out[b, s, h], lse[b, s, h] = attend(q, K[j], V[j], pf["softmax_scale"], s + 1)
+    return dict(out=out, lse=lse)

@@ -413,6 +413,31 @@ def test_p15_record_size_against_printed_figures():
         assert WORKLOADS[name].record_elems == 576
 
 
+def check_prefill_sdpa(m):
+    """MLA-form prefill against torch's causal scaled-dot-product attention
+    on keys and values rebuilt here with torch from the raw weights."""
+    from workloads import make_prefill_inputs
+    w = tiny(batch=2, heads=3, seq_len=(9, 9), forced_lens=(9, 6))
+    pf = make_prefill_inputs(w, prompt_len=9)
+    res = m.prefill(pf)
+    t = lambda bits: torch.from_numpy(m.bf16_to_f64(bits))
+    w_uk, w_uv = t(pf["w_uk"]), t(pf["w_uv"])
+    for b in range(w.batch):
+        L = int(pf["seq_lens"][b])
+        rec = t(pf["ckr"][b, :L])
+        c, kr = rec[:, :w.d_latent], rec[:, w.d_latent:]
+        k = torch.cat([torch.einsum("hnc,tc->htn", w_uk, c), kr.expand(w.heads, L, w.d_rope)], dim=2)
+        v = torch.einsum("tc,hcv->htv", c, w_uv)
+        q = torch.cat([t(pf["q_nope"][b, :L]), t(pf["q_rope"][b, :L])], dim=2).permute(1, 0, 2)
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=pf["softmax_scale"])
+        close(res["out"][b, :L], ref.permute(1, 0, 2).numpy(), 1e-10)
+        assert np.all(np.isnan(res["out"][b, L:]))
+
+
+def test_p16_prefill_sdpa():
+    check_prefill_sdpa(oracle)
+
+
 # ------------------------------------------------------------------ planted mistakes
 
 def _mutant(**patches):
@@ -466,6 +491,7 @@ def _sign_flip_absorb(q_nope, w_uk):
     (dict(e4m3_to_f64=_e4m3_bias8), check_e4m3_decoder),
     (dict(combine=_bad_combine), check_split_merge),
     (dict(absorb_q=_sign_flip_absorb), check_absorb_identity),
+    (dict(reconstruct_kv=_no_rope_kv), check_prefill_sdpa),
 ])
 def test_planted_mistakes_are_caught(patch, check):
     with pytest.raises(AssertionError):

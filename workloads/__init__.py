@@ -10,6 +10,7 @@ from .configs import WORKLOADS, Workload, get_workload, small_workload
 from .generate import (
     make_append_inputs,
     make_inputs,
+    make_prefill_inputs,
     f32_to_bf16_bits,
     f32_to_e4m3_bits,
     replicate_cache,
@@ -22,6 +23,7 @@ __all__ = [
     "small_workload",
     "make_inputs",
     "make_append_inputs",
+    "make_prefill_inputs",
     "f32_to_bf16_bits",
     "f32_to_e4m3_bits",
     "replicate_cache",

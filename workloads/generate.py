@@ -144,3 +144,26 @@ def make_append_inputs(w: Workload, seed: int | None = None) -> dict:
     x = f32_to_bf16_bits(_normal(rng, (B, S, D)))
     w_dkv = f32_to_bf16_bits(_normal(rng, (D, w.d_latent + w.d_rope), float(np.sqrt(1.0 / D))))
     return dict(x=x, w_dkv=w_dkv, rope_base=10000.0)
+
+
+def make_prefill_inputs(w: Workload, prompt_len: int, seed: int | None = None) -> dict:
+    """Inputs of an MLA-form prefill: prompts of the workload's batch padded
+    to ``prompt_len`` positions, lengths drawn like the workload's (clipped to
+    prompt_len, ``forced_lens`` first); the prompt's records ckr
+    [B, P, d_c + d_r] and q_nope / q_rope [B, P, H, .] ~ N(0, 1), W_UK / W_UV
+    ~ N(0, weight_var), all as bf16 bits.  Child stream 6 of the seed."""
+    seed = w.seed if seed is None else seed
+    rng = np.random.default_rng(np.random.SeedSequence(seed).spawn(7)[6])
+    B, H, P = w.batch, w.heads, prompt_len
+    lo, hi = w.seq_len
+    lens = rng.integers(min(lo, P), min(hi, P) + 1, size=B, dtype=np.int64)
+    for i, v in enumerate(w.forced_lens[:B]):
+        lens[i] = min(v, P)
+    wstd = float(np.sqrt(w.weight_var))
+    w_uk = f32_to_bf16_bits(_normal(rng, (H, w.d_nope, w.d_latent), wstd))
+    w_uv = f32_to_bf16_bits(_normal(rng, (H, w.d_latent, w.d_v), wstd))
+    q_nope = f32_to_bf16_bits(_normal(rng, (B, P, H, w.d_nope)))
+    q_rope = f32_to_bf16_bits(_normal(rng, (B, P, H, w.d_rope)))
+    ckr = f32_to_bf16_bits(_normal(rng, (B, P, w.d_latent + w.d_rope)))
+    return dict(workload=w, prompt_len=P, seq_lens=lens.astype(np.int32), w_uk=w_uk, w_uv=w_uv, q_nope=q_nope,
+                q_rope=q_rope, ckr=ckr, softmax_scale=w.softmax_scale)
