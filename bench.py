@@ -281,6 +281,33 @@ def main():
     M = w.batch * w.q_len
     app_bytes = w.d_model * (w.d_latent + w.d_rope) * 2 + M * w.d_model * 2 + M * alg["record_bytes"]
 
+    # The MLA-form prefill of a prompt batch (keys and values expanded per
+    # head, then causal attention), timed on its own: events around each call.
+    from head_latent_attention_absorbed_amd import PrefillStep
+    from workloads import make_prefill_inputs, prefill_workload
+    pw, P = prefill_workload()
+    pf = make_prefill_inputs(pw, P)
+    pst = PrefillStep(pf)
+    for _ in range(2):
+        pst.run()
+    torch.cuda.synchronize()
+    KP = max(3, min(K, 10))
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(KP)]
+    for i in range(KP):
+        pev[i][0].record(stream)
+        pst.kv()
+        pev[i][1].record(stream)
+        pst.attention()
+        pev[i][2].record(stream)
+    torch.cuda.synchronize()
+    pkv_us = float(np.median([e[0].elapsed_time(e[1]) * 1e3 for e in pev]))
+    pat_us = float(np.median([e[1].elapsed_time(e[2]) * 1e3 for e in pev]))
+    plens = [int(v) for v in pf["seq_lens"]]
+    p_tokens = sum(plens)
+    p_attn_flops = pw.heads * (pw.d_nope + pw.d_rope + pw.d_v) * 2 * sum(L * (L + 1) // 2 for L in plens)
+    p_kv_flops = p_tokens * pw.heads * pw.d_latent * (pw.d_nope + pw.d_v) * 2
+    del pst
+
     us_step = ms_per_step * 1e3
     value = alg["cache_bytes"] / (us_step * 1e-6) / 1e12
     achieved = alg["decode_bytes"] / (dec_us * 1e-6) / 1e9
@@ -335,6 +362,22 @@ def main():
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(app_bytes / (app_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                          "algorithmic_bytes_per_call": app_bytes},
+        },
+        "prefill": {
+            "what": "mla_prefill_kv (K_nope, V per head from the records) + mla_prefill_attention (causal)",
+            "workload": pw.name, "batch": pw.batch, "prompt_len": P, "seq_lens": plens, "heads": pw.heads,
+            "tokens_per_s": round(p_tokens / ((pkv_us + pat_us) * 1e-6), 1),
+            "kv_us_median": round(pkv_us, 2),
+            "attention_us_median": round(pat_us, 2),
+            "roofline": {"kernel": "prefill_kernel (mla_prefill_attention)", "bound": "mfma",
+                         "achieved": round(p_attn_flops / (pat_us * 1e-6) / 1e12, 1),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(p_attn_flops / (pat_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "algorithmic_flops_per_launch": p_attn_flops},
+            "kv_roofline": {"bound": "mfma", "achieved": round(p_kv_flops / (pkv_us * 1e-6) / 1e12, 1),
+                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(p_kv_flops / (pkv_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                            "algorithmic_flops_per_call": p_kv_flops},
         },
     }
     if args.copy_probe_mb > 0:

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import get_workload, make_prefill_inputs, small_workload
+from workloads import make_prefill_inputs, prefill_workload, small_workload
 from gpu_helpers import compare, to_np, tolerances
 
 pytestmark = pytest.mark.gpu
@@ -98,17 +98,24 @@ def test_prefill_parity(name):
 
 
 def test_prefill_headline_sampled():
-    """DeepSeek-V3-shaped heads over a 1024-position prompt batch: sampled
-    positions (first, tile edges, last) of sampled heads against the oracle."""
-    w = replace(get_workload("deepseek_v3"), batch=2, seq_len=(700, 1024), forced_lens=(1024, 700))
-    pf = make_prefill_inputs(w, 1024)
-    print(f"[case] prefill headline-sampled lens={list(pf['seq_lens'])}", flush=True)
+    """The prompt batch the prefill is measured on (DeepSeek-V3 heads, two
+    prompts padded to 4096 positions): sampled positions (first, tile
+    edges, the shorter prompt's last, the end) of sampled heads against the
+    oracle; every computed output finite, padding untouched."""
+    w, P = prefill_workload()
+    pf = make_prefill_inputs(w, P)
+    print(f"[case] prefill headline-sampled P={P} lens={list(pf['seq_lens'])}", flush=True)
     st = _run(pf)
     heads = [0, 77, 127]
-    positions = [0, 31, 32, 127, 128, 511, 699, 1023]
+    L1 = int(pf["seq_lens"][1])
+    positions = sorted({0, 31, 32, 127, 128, 1023, 2047, L1 - 1, P - 1})
     ref = oracle.prefill(pf, heads=heads, positions=positions)
-    out = to_np(st.out)
+    out, lse = to_np(st.out), to_np(st.lse)
     p_abs, p_rel = prefill_tolerances(w)
     for b in range(w.batch):
-        ps = [s for s in positions if s < int(pf["seq_lens"][b])]
+        L = int(pf["seq_lens"][b])
+        ps = [s for s in positions if s < L]
         compare(f"out[{b}] sampled", out[b][ps][:, heads], ref["out"][b][ps][:, heads], p_abs, p_rel)
+        compare(f"lse[{b}] sampled", lse[b][ps][:, heads], ref["lse"][b][ps][:, heads], p_abs, p_rel)
+        assert np.all(np.isfinite(out[b, :L])) and np.all(np.isfinite(lse[b, :L]))
+        assert np.all(np.isnan(out[b, L:])), "wrote past the prompt"

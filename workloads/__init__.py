@@ -6,7 +6,7 @@ per-token scale).  It holds none of the attention arithmetic, so both the
 CPU oracle and the HIP path can take their inputs from here without sharing
 any of the method's code.
 """
-from .configs import WORKLOADS, Workload, get_workload, small_workload
+from .configs import WORKLOADS, Workload, get_workload, prefill_workload, small_workload
 from .generate import (
     make_append_inputs,
     make_inputs,
@@ -21,6 +21,7 @@ __all__ = [
     "Workload",
     "get_workload",
     "small_workload",
+    "prefill_workload",
     "make_inputs",
     "make_append_inputs",
     "make_prefill_inputs",

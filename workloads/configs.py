@@ -106,3 +106,16 @@ def small_workload(base: str, **overrides) -> Workload:
     w = get_workload(base)
     overrides.setdefault("name", f"{base}_small")
     return replace(w, **overrides)
+
+
+PREFILL_PROMPT_LEN = 4096
+
+
+def prefill_workload() -> tuple[Workload, int]:
+    """The prompt batch of the prefill measurement: DeepSeek-V3 heads
+    (H = 128, d_c = 512, d_nope = d_v = 128), two prompts padded to 4096
+    positions, the first full and the second of a length drawn from
+    [2048, 4096].  Returns (workload, padded prompt length)."""
+    w = replace(get_workload("deepseek_v3"), name="deepseek_v3_prefill", batch=2, seq_len=(2048, PREFILL_PROMPT_LEN),
+                forced_lens=(PREFILL_PROMPT_LEN,))
+    return w, PREFILL_PROMPT_LEN
