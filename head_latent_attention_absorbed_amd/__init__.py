@@ -30,6 +30,7 @@ from .binding import (  # noqa: F401
     mla_append_kv,
     mla_append_kv_workspace_bytes,
     mla_prefill_workspace_bytes,
+    mla_prefill_kv_elems,
     mla_prefill_kv,
     mla_prefill_attention,
     mla_status_string,

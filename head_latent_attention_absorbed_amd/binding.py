@@ -82,11 +82,12 @@ def library() -> ctypes.CDLL:
     lib.mla_append_kv_workspace_bytes.argtypes = [SP, I32, ctypes.POINTER(ctypes.c_size_t)]
     lib.mla_append_kv.argtypes = [SP, I32, P, P, F, P, P, I64, I64, P, P, P, P, ctypes.c_size_t, P]
     lib.mla_prefill_workspace_bytes.argtypes = [SP, ctypes.POINTER(ctypes.c_size_t)]
-    lib.mla_prefill_kv.argtypes = [SP, I32, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.mla_prefill_kv_elems.argtypes = [SP, I32, ctypes.POINTER(ctypes.c_int64)]
+    lib.mla_prefill_kv.argtypes = [SP, I32, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.mla_prefill_attention.argtypes = [SP, I32, P, P, P, P, P, P, P, P, P]
     for fn in ("mla_absorb_q", "mla_decode_num_parts", "mla_decode_paged", "mla_combine_lse", "mla_up_v",
                "mla_combine_up_v", "mla_append_kv_workspace_bytes", "mla_append_kv", "mla_prefill_workspace_bytes",
-               "mla_prefill_kv", "mla_prefill_attention"):
+               "mla_prefill_kv_elems", "mla_prefill_kv", "mla_prefill_attention"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
@@ -194,10 +195,19 @@ def mla_prefill_workspace_bytes(shape: MlaShape) -> int:
     return n.value
 
 
-def mla_prefill_kv(shape: MlaShape, prompt_len: int, ckr, w_uk, w_uv, k_nope, v, workspace, workspace_bytes: int,
-                   stream=None) -> None:
+def mla_prefill_kv_elems(shape: MlaShape, prompt_len: int) -> int:
+    """bf16 values in each of the tile-native k_nope and v buffers."""
+    n = ctypes.c_int64(0)
+    _check(library().mla_prefill_kv_elems(ctypes.byref(shape), int(prompt_len), ctypes.byref(n)),
+           "mla_prefill_kv_elems")
+    return n.value
+
+
+def mla_prefill_kv(shape: MlaShape, prompt_len: int, ckr, w_uk, w_uv, seq_lens, k_nope, v, workspace,
+                   workspace_bytes: int, stream=None) -> None:
     _check(library().mla_prefill_kv(ctypes.byref(shape), int(prompt_len), _ptr(ckr), _ptr(w_uk), _ptr(w_uv),
-                                    _ptr(k_nope), _ptr(v), _ptr(workspace), int(workspace_bytes), _stream(stream)),
+                                    _ptr(seq_lens), _ptr(k_nope), _ptr(v), _ptr(workspace), int(workspace_bytes),
+                                    _stream(stream)),
            "mla_prefill_kv")
 
 

@@ -37,7 +37,6 @@ namespace {
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRebase = 8.0f;  // log2 of the largest unnormalised weight kept between re-bases
-constexpr int kRow = kTile * 16;  // bytes of one granule row of a tile
 constexpr int kTab = 128;  // tiles per LDS source-table fill
 constexpr int kPvAhead = 2;     // V blocks read ahead of their MFMAs
 constexpr int kScoreAhead = 4;  // K fragments read ahead of their MFMAs
@@ -78,14 +77,6 @@ struct Geo {
   static constexpr int NB = DC / 32;             // 32-column blocks of O^T
 };
 
-// A lane id the compiler cannot see through, so that lane-derived constants
-// are recomputed where they are used instead of being kept live (and spilled)
-// across the whole kernel.
-__device__ __forceinline__ int opaque_lane() {
-  int l;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-  return l;
-}
 
 // The token a lane moves in every tile-load instruction: slot lane % 32 of
 // row 2m + lane / 32 holds token (lane % 32) ^ (4 * (lane / 32)).
@@ -827,27 +818,22 @@ hipError_t launch_dc(const DecodeParams& p, int nw, hipStream_t stream) {
 // made by mla_prefill_kv.  The tile products, the online softmax and P.V
 // are the decode's, at latent width 128: a 32-token tile of K (24 granule
 // rows) and of V (16 rows) in the same granule-major LDS layout, one wave per
-// 32 query positions of one head, four waves per work-group.  Tiles are
-// loaded through registers, one tile ahead, into two LDS buffers.
+// 32 query positions of one head, four waves per work-group.  The keys and
+// values are stored in that layout already (tile-native), so a tile is two
+// contiguous 8 KiB copies plus the shared RoPE keys gathered from the
+// records, all global->LDS DMA into a four-slot ring (three tiles in flight).
 constexpr int kPfRows = 128;  // query positions per work-group
-
-template <int TPT>
-struct PfTileLoad {  // this thread's 16-byte granules of one K + V tile
-  uint4 v[TPT];
-};
+constexpr int kPfBuf = 4;     // ring slots
 
 __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
   using Gm = Geo<128>;
   constexpr int KROWS = Gm::GPT;   // 24 granule rows of K
   constexpr int VROWS = 16;        // 16 granule rows of V
   constexpr int TB = (KROWS + VROWS) * kRow;
-  constexpr int GRAN = (KROWS + VROWS) * kTile;  // granules per tile
-  constexpr int TPT = GRAN / 256;                // per thread
-  static_assert(GRAN % 256 == 0, "granules split evenly over the threads");
-  __shared__ __attribute__((aligned(1024))) char tiles[2 * TB];
+  constexpr int NI = (KROWS + VROWS) / 8;  // DMA instructions per wave per tile (2 rows each, 4 waves)
+  __shared__ __attribute__((aligned(1024))) char tiles[kPfBuf * TB];
 
-  const int tid = threadIdx.x;
-  const int w = uniform(tid >> 6);
+  const int w = uniform(threadIdx.x >> 6);
   const int b = blockIdx.z, h = blockIdx.y;
   const int ntile = (p.P + kPfRows - 1) / kPfRows;
   const int qt = ntile - 1 - (int)blockIdx.x;  // longest rows first
@@ -855,30 +841,33 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
   const int q0 = qt * kPfRows;
   if (q0 >= L) return;
   const int nkt = (min(L, q0 + kPfRows) + kTile - 1) / kTile;  // key tiles this group needs
-
-  // Granule i of a tile (row g = i / 32, token t = i % 32): global source.
   const int64_t tok0 = (int64_t)b * p.P;
-  auto load = [&](int kt, PfTileLoad<TPT>& r) {
+
+  // Tile kt into ring slot s.  Instruction q of wave w fills granule rows
+  // 2c, 2c + 1 with c = 4 q + w: rows 0..15 from the key tile, 16..23 from
+  // the records' RoPE keys (lane l brings position 32 kt + (l % 32 ^ 4 (l / 32)),
+  // clamped to the prompt), 24..39 from the value tile.
+  const int T = (p.P + kTile - 1) / kTile;
+  const char* kbase = (const char*)(p.k_nope + ((int64_t)b * p.H + h) * T * (kTile * 128));
+  const char* vbase = (const char*)(p.v + ((int64_t)b * p.H + h) * T * (kTile * 128));
+  const char* rbase = (const char*)(p.ckr + tok0 * (p.DCK + 64) + p.DCK);
+  const uint32_t rec = (uint32_t)(p.DCK + 64) * 2;
+  const uint32_t tiles_lds = lds_offset(tiles);
+  const int dl = opaque_lane();
+  const int rope_tok = (dl & 31) ^ (4 * (dl >> 5));
+  auto issue = [&](int kt, int s) {
+    const uint32_t dst = tiles_lds + s * TB;
+    const uint32_t roff = (uint32_t)min(kt * kTile + rope_tok, L - 1) * rec + 16u * (dl >> 5);
 #pragma unroll
-    for (int j = 0; j < TPT; ++j) {
-      const int i = tid + 256 * j;
-      const int g = i >> 5, t = i & 31;
-      const int pos = kt * kTile + t;
-      const int64_t tk = tok0 + min(pos, L - 1);
-      const uint16_t* src;
-      if (g < 16) src = p.k_nope + (tk * p.H + h) * 128 + 8 * g;
-      else if (g < KROWS) src = p.ckr + tk * (p.DCK + 64) + p.DCK + 8 * (g - 16);
-      else src = p.v + (tk * p.H + h) * 128 + 8 * (g - KROWS);
-      r.v[j] = *(const uint4*)src;
-    }
-  };
-  auto store = [&](int kt, const PfTileLoad<TPT>& r, char* tb) {
-#pragma unroll
-    for (int j = 0; j < TPT; ++j) {
-      const int i = tid + 256 * j;
-      const int g = i >> 5, t = i & 31;
-      const bool valid = kt * kTile + t < L;  // positions past the prompt read as zeros
-      *(uint4*)(tb + g * kRow + ((t ^ ((g & 1) << 2)) << 4)) = valid ? r.v[j] : uint4{0, 0, 0, 0};
+    for (int q = 0; q < NI; ++q) {
+      const int c = 4 * q + w;
+      if (c < 8) {
+        lds_dma16(kbase + (int64_t)kt * 8192 + c * 1024, 16u * dl, dst + c * 1024);
+      } else if (c < 12) {
+        lds_dma16(rbase + 32 * (c - 8), roff, dst + c * 1024);
+      } else {
+        lds_dma16(vbase + (int64_t)kt * 8192 + (c - 12) * 1024, 16u * dl, dst + c * 1024);
+      }
     }
   };
 
@@ -898,11 +887,12 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
   }
   const int limit = min(pos + 1, L);  // causal: this row sees positions < limit
 
-  PfTileLoad<TPT> nxt;
-  load(0, nxt);
-  store(0, nxt, tiles);
-  if (nkt > 1) load(1, nxt);
-  block_sync();
+  // The queries have to be in registers before the ring copies start (the
+  // compiler counts only its own loads, and would otherwise wait for every
+  // copy in flight at their first use).
+#pragma unroll
+  for (int ks = 0; ks < Gm::KS; ++ks) asm volatile("" : "+v"(qf[ks]));
+  for (int i = 0; i < kPfBuf - 1 && i < nkt; ++i) issue(i, i);
 
   f32x16 O[Gm::NB];
   float m_run = -__builtin_inff(), l_run = 0.0f;
@@ -910,7 +900,11 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
   float alpha;
   auto tile = [&](int kt, auto first_tag) {
     constexpr bool FIRST = decltype(first_tag)::value;
-    const char* tb = tiles + (kt & 1) * TB;
+    // tile kt has landed (for every wave) and slot (kt - 1) % NBUF is free
+    if (kt + kPfBuf - 2 < nkt) vm_wait<(kPfBuf - 2) * NI>(); else vm_wait<0>();
+    block_sync();
+    if (kt + kPfBuf - 1 < nkt) issue(kt + kPfBuf - 1, (kt + kPfBuf - 1) % kPfBuf);
+    const char* tb = tiles + (kt % kPfBuf) * TB;
     // fully visible to every row of the group: below its first position
     const bool full = (kt + 1) * kTile <= q0;
     score_tile<128, false, 0>(tb, nullptr, qf, m_run, l_run, kt * kTile, limit, full, p.scale_log2, pf0, pf1,
@@ -919,12 +913,6 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
       if (__any(alpha != 1.0f)) rescale<128>(O, alpha);
     }
     pv_tile<128, kPvAhead, FIRST>(tb + KROWS * kRow, pf0, pf1, O);
-    // the next tile into the other buffer, the one after into registers
-    if (kt + 1 < nkt) {
-      store(kt + 1, nxt, tiles + ((kt + 1) & 1) * TB);
-      if (kt + 2 < nkt) load(kt + 2, nxt);
-    }
-    block_sync();
   };
   tile(0, std::true_type{});
   for (int kt = 1; kt < nkt; ++kt) tile(kt, std::false_type{});

@@ -359,7 +359,7 @@ mla_status_t check_prefill(const mla_shape_t* shape, int32_t prompt_len) {
   if (shape->d_nope != 128 || shape->d_v != 128)
     return fail(MLA_ERR_UNSUPPORTED, "prefill: d_nope %d, d_v %d (kernels exist for 128, 128)", shape->d_nope,
                 shape->d_v);
-  if (prompt_len < 1 || (int64_t)shape->batch * prompt_len > (1 << 24))
+  if (prompt_len < 1 || prompt_len > (1 << 20) || (int64_t)shape->batch * prompt_len > (1 << 24))
     return fail(MLA_ERR_INVALID_ARG, "prefill: prompt_len %d out of range", prompt_len);
   return MLA_OK;
 }
@@ -370,16 +370,24 @@ mla_status_t mla_prefill_workspace_bytes(const mla_shape_t* shape, size_t* bytes
   mla_status_t st = check_shape(shape);
   if (st != MLA_OK) return st;
   if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = (size_t)shape->num_heads * shape->d_latent * shape->d_nope * 2;  // W_UK transposed
+  *bytes = (size_t)shape->num_heads * shape->d_latent * shape->d_v * 2;  // W_UV transposed
+  return ok();
+}
+
+mla_status_t mla_prefill_kv_elems(const mla_shape_t* shape, int32_t prompt_len, int64_t* elems) {
+  mla_status_t st = check_prefill(shape, prompt_len);
+  if (st != MLA_OK) return st;
+  if (!elems) return fail(MLA_ERR_INVALID_ARG, "elems is NULL");
+  *elems = (int64_t)shape->batch * shape->num_heads * ((prompt_len + 31) / 32) * 32 * 128;
   return ok();
 }
 
 mla_status_t mla_prefill_kv(const mla_shape_t* shape, int32_t prompt_len, const void* ckr, const void* w_uk,
-                            const void* w_uv, void* k_nope, void* v, void* workspace, size_t workspace_bytes,
-                            hipStream_t stream) {
+                            const void* w_uv, const int32_t* seq_lens, void* k_nope, void* v, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
   mla_status_t st = check_prefill(shape, prompt_len);
   if (st != MLA_OK) return st;
-  if (!ckr || !w_uk || !w_uv || !k_nope || !v || !workspace)
+  if (!ckr || !w_uk || !w_uv || !seq_lens || !k_nope || !v || !workspace)
     return fail(MLA_ERR_INVALID_ARG, "mla_prefill_kv: NULL tensor");
   if (!aligned16(ckr) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(k_nope) || !aligned16(v) ||
       !aligned16(workspace))
@@ -389,26 +397,21 @@ mla_status_t mla_prefill_kv(const mla_shape_t* shape, int32_t prompt_len, const 
   if (st != MLA_OK) return st;
   if (workspace_bytes < need)
     return fail(MLA_ERR_INVALID_ARG, "mla_prefill_kv: workspace of %zu bytes, %zu needed", workspace_bytes, need);
-  uint16_t* wukt = static_cast<uint16_t*>(workspace);
-  hipError_t e = mla::launch_transpose_heads(static_cast<const uint16_t*>(w_uk), wukt, shape->num_heads,
-                                             shape->d_nope, shape->d_latent, stream);
+  uint16_t* wvt = static_cast<uint16_t*>(workspace);
+  hipError_t e = mla::launch_transpose_heads(static_cast<const uint16_t*>(w_uv), wvt, shape->num_heads,
+                                             shape->d_latent, shape->d_v, stream);
   if (e != hipSuccess) return hip_status(e, "mla_prefill_kv transpose launch");
-  mla::HeadGemmParams g{};
-  g.a = ckr;
-  g.M = shape->batch * prompt_len;
-  g.H = shape->num_heads;
-  g.K = shape->d_latent;
-  g.a_row = shape->d_latent + shape->d_rope;  // one latent row for every head
-  g.a_head = 0;
-  g.w = wukt;
-  g.c = k_nope;
-  g.N = shape->d_nope;
-  e = mla::launch_head_gemm(g, false, false, stream);
-  if (e != hipSuccess) return hip_status(e, "mla_prefill_kv key launch");
-  g.w = static_cast<const uint16_t*>(w_uv);
-  g.c = v;
-  g.N = shape->d_v;
-  return hip_status(mla::launch_head_gemm(g, false, false, stream), "mla_prefill_kv value launch");
+  mla::ExpandParams x{};
+  x.ckr = static_cast<const uint16_t*>(ckr);
+  x.wuk = static_cast<const uint16_t*>(w_uk);
+  x.wvt = wvt;
+  x.seq_lens = seq_lens;
+  x.B = shape->batch;
+  x.P = prompt_len;
+  x.H = shape->num_heads;
+  x.k_nope = static_cast<uint16_t*>(k_nope);
+  x.v = static_cast<uint16_t*>(v);
+  return hip_status(mla::launch_expand(x, shape->d_latent, stream), "mla_prefill_kv launch");
 }
 
 mla_status_t mla_prefill_attention(const mla_shape_t* shape, int32_t prompt_len, const void* q_nope,

@@ -21,6 +21,7 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 constexpr int kTile = 32;  // tokens per decode tile (the M extent of one 32x32 MFMA)
+constexpr int kRow = kTile * 16;  // bytes of one granule row of a tile
 
 // D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).
 // Lane l holds A[l%32][8*(l/32) .. +8], B[8*(l/32) .. +8][l%32] and
@@ -67,6 +68,15 @@ __device__ __forceinline__ void lds_dma16(const void* base_any, uint32_t voff, u
       :
       : "v"(voff), "s"(base), "s"(dst)
       : "memory", "m0");
+}
+
+// A lane id the compiler cannot see through, so that lane-derived constants
+// are recomputed where they are used instead of being kept live (and spilled)
+// across the whole kernel.
+__device__ __forceinline__ int opaque_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
 }
 
 // Work-group barrier for LDS hand-offs: waits for this wave's LDS traffic,

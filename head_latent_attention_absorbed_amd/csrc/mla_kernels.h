@@ -39,13 +39,29 @@ int decode_wgs_per_cu(int R, int d_latent);
 
 hipError_t launch_decode(const DecodeParams& p, int d_latent, bool fp8, hipStream_t stream);
 
+// Tile-native layout of the prefill's per-head keys and values: for
+// sequence b, head h and 32-position tile j, 16 granule rows g (elements
+// 8g..8g+7) of 32 slots; position 32 j + t sits in slot t ^ (4 (g & 1)).
+// One tile is 4096 bf16 (8 KiB) at element ((b H + h) T + j) 4096,
+// T = ceil(P / 32): the LDS image of the attention's key/value tiles.
+struct ExpandParams {
+  const uint16_t* ckr;       // bf16 [B, P, DC + 64] records
+  const uint16_t* wuk;       // bf16 [H, 128, DC] (W_UK)
+  const uint16_t* wvt;       // bf16 [H, 128, DC] (W_UV transposed)
+  const int32_t* seq_lens;
+  int32_t B, P, H;
+  uint16_t* k_nope;          // tile-native, bf16
+  uint16_t* v;               // tile-native, bf16
+};
+hipError_t launch_expand(const ExpandParams& p, int d_latent, hipStream_t stream);
+
 // MLA-form prefill attention (d_nope 128, d_rope 64, d_v 128).
 struct PrefillParams {
   const uint16_t* q_nope;    // bf16 [B, P, H, 128]
   const uint16_t* q_rope;    // bf16 [B, P, H, 64]
-  const uint16_t* k_nope;    // bf16 [B, P, H, 128]
+  const uint16_t* k_nope;    // tile-native (ExpandParams)
   const uint16_t* ckr;       // bf16 [B, P, DCK + 64]: k_rope at element DCK of each record
-  const uint16_t* v;         // bf16 [B, P, H, 128]
+  const uint16_t* v;         // tile-native (ExpandParams)
   const int32_t* seq_lens;
   int32_t B, P, H, DCK;
   float scale_log2;          // softmax_scale * log2(e)

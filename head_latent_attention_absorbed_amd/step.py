@@ -13,7 +13,8 @@ import numpy as np
 from .binding import (
     MLA_BF16, MLA_FP8_E4M3, MLA_FP16, MLA_FP32, MLA_TILE_TOKENS, MlaShape,
     mla_absorb_q, mla_append_kv, mla_append_kv_workspace_bytes, mla_decode_num_parts, mla_decode_paged,
-    mla_combine_lse, mla_combine_up_v, mla_prefill_attention, mla_prefill_kv, mla_prefill_workspace_bytes, mla_up_v,
+    mla_combine_lse, mla_combine_up_v, mla_prefill_attention, mla_prefill_kv, mla_prefill_kv_elems,
+    mla_prefill_workspace_bytes, mla_up_v,
 )
 
 
@@ -228,16 +229,18 @@ class PrefillStep:
         self.w_uv = _dev_bits(torch, pf["w_uv"], device, bf16)
         self.seq_lens = torch.from_numpy(pf["seq_lens"]).to(device)
         B, P, H = w.batch, self.P, w.heads
-        self.k_nope = torch.empty((B, P, H, w.d_nope), dtype=bf16, device=device)
-        self.v = torch.empty((B, P, H, w.d_v), dtype=bf16, device=device)
+        # tile-native per-head keys and values (see mla_prefill_kv)
+        n_kv = mla_prefill_kv_elems(self.shape, P)
+        self.k_nope = torch.empty(n_kv, dtype=bf16, device=device)
+        self.v = torch.empty(n_kv, dtype=bf16, device=device)
         self.out = torch.empty((B, P, H, w.d_v), dtype=bf16, device=device)
         self.lse = torch.empty((B, P, H), dtype=torch.float32, device=device)
         nbytes = mla_prefill_workspace_bytes(self.shape)
         self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
 
     def kv(self, stream=None):
-        mla_prefill_kv(self.shape, self.P, self.ckr, self.w_uk, self.w_uv, self.k_nope, self.v, self.ws,
-                       self.ws.numel(), stream)
+        mla_prefill_kv(self.shape, self.P, self.ckr, self.w_uk, self.w_uv, self.seq_lens, self.k_nope, self.v,
+                       self.ws, self.ws.numel(), stream)
 
     def attention(self, stream=None):
         mla_prefill_attention(self.shape, self.P, self.q_nope, self.q_rope, self.k_nope, self.ckr, self.v,

@@ -247,27 +247,37 @@ mla_status_t mla_append_kv(const mla_shape_t* shape, int32_t d_model, const void
  * the absorbed form the decode uses.  The prompts of the batch are padded to
  * prompt_len = P positions; sequence b uses its first seq_lens[b] (<= P).
  *
- * mla_prefill_kv -- per-head keys and values of every position:
- *   k_nope[b,t,h,:] = W_UK[h] . c[b,t]        bf16 [B, P, H, d_nope]
- *   v[b,t,h,:]      = c[b,t] . W_UV[h]        bf16 [B, P, H, d_v]
- *   (fp32 accumulation, bf16 RNE results; every position is computed)
+ * mla_prefill_kv -- per-head keys and values of every position t < seq_lens[b]:
+ *   k_nope[b,h,t,:] = W_UK[h] . c[b,t]        (d_nope values)
+ *   v[b,h,t,:]      = c[b,t] . W_UV[h]        (d_v values)
+ *   fp32 accumulation, bf16 RNE results, written in the tile-native layout
+ *   the attention reads: for sequence b, head h and tile j = t / 32
+ *   (T = ceil(P / 32) tiles per sequence), 4096 bf16 at element
+ *   ((b H + h) T + j) 4096, holding 16 granule rows g (elements 8g..8g+7)
+ *   of 32 slots each, position t in slot (t % 32) ^ (4 (g & 1)).  Positions
+ *   from seq_lens[b] to the end of their tile are written as zeros; later
+ *   tiles are not written.  Each of k_nope and v holds
+ *   mla_prefill_kv_elems(shape, P) bf16 values.
  *   ckr    bf16 [B, P, d_latent + d_rope]: the prompt's records [c_KV | k_rope]
  *   w_uk   bf16 [H, d_nope, d_latent], w_uv bf16 [H, d_latent, d_v]
- *   workspace of at least mla_prefill_workspace_bytes (W_UK transposed).
+ *   seq_lens int32 [B] (device), clamped to [0, P]
+ *   workspace of at least mla_prefill_workspace_bytes (W_UV transposed).
  * mla_prefill_attention -- causal attention of each position s < seq_lens[b]
  * over positions t <= s, per head:
  *   z = scale (q_nope . k_nope + q_rope . k_rope),  out = softmax(z) . v
  *   q_nope bf16 [B, P, H, d_nope], q_rope bf16 [B, P, H, d_rope] (already rotated),
- *   k_rope = ckr[..., d_latent:] (shared by all heads), k_nope and v from mla_prefill_kv
+ *   k_rope = ckr[..., d_latent:] (shared by all heads), k_nope and v from
+ *   mla_prefill_kv with the same seq_lens;
  *   out bf16 [B, P, H, d_v] and lse fp32 [B, P, H] for positions < seq_lens[b];
  *   the other positions are left untouched.
- * Kernels exist for d_nope = d_v = 128, d_rope = 64, d_latent 512 or 256.
- * All tensors 16-byte aligned.
+ * Kernels exist for d_nope = d_v = 128, d_rope = 64, d_latent 512 or 256,
+ * and 1 <= P <= 2^20 with B P <= 2^24.  All tensors 16-byte aligned.
  */
 mla_status_t mla_prefill_workspace_bytes(const mla_shape_t* shape, size_t* bytes);
+mla_status_t mla_prefill_kv_elems(const mla_shape_t* shape, int32_t prompt_len, int64_t* elems);
 mla_status_t mla_prefill_kv(const mla_shape_t* shape, int32_t prompt_len, const void* ckr, const void* w_uk,
-                            const void* w_uv, void* k_nope, void* v, void* workspace, size_t workspace_bytes,
-                            hipStream_t stream);
+                            const void* w_uv, const int32_t* seq_lens, void* k_nope, void* v, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
 mla_status_t mla_prefill_attention(const mla_shape_t* shape, int32_t prompt_len, const void* q_nope,
                                    const void* q_rope, const void* k_nope, const void* ckr, const void* v,
                                    const int32_t* seq_lens, void* out, float* lse, hipStream_t stream);

@@ -22,7 +22,7 @@ def test_exports_every_declared_symbol():
     declared = mla.exported_symbols()
     assert set(declared) >= {"mla_absorb_q", "mla_decode_num_parts", "mla_decode_paged", "mla_combine_lse",
                              "mla_up_v", "mla_combine_up_v", "mla_append_kv", "mla_append_kv_workspace_bytes",
-                             "mla_prefill_workspace_bytes", "mla_prefill_kv", "mla_prefill_attention",
+                             "mla_prefill_workspace_bytes", "mla_prefill_kv_elems", "mla_prefill_kv", "mla_prefill_attention",
                              "mla_status_string", "mla_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", mla.library_path], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -212,13 +212,19 @@ def test_prefill_argument_checks():
     assert lib.mla_prefill_workspace_bytes(ctypes.byref(sh), ctypes.byref(need)) == mla.MLA_OK
     assert need.value == 16 * 512 * 128 * 2
     kv = lambda shp, **kw: lib.mla_prefill_kv(ctypes.byref(shp), kw.get("P", 64), kw.get("ckr", FAKE), FAKE, FAKE,
-                                             FAKE, FAKE, kw.get("ws", FAKE), kw.get("nb", need.value), None)
+                                             kw.get("lens", FAKE), FAKE, FAKE, kw.get("ws", FAKE),
+                                             kw.get("nb", need.value), None)
     att = lambda shp, **kw: lib.mla_prefill_attention(ctypes.byref(shp), kw.get("P", 64), FAKE, FAKE, FAKE,
                                                       kw.get("ckr", FAKE), FAKE, FAKE, kw.get("out", FAKE), FAKE, None)
     assert kv(sh, ckr=None) == mla.MLA_ERR_INVALID_ARG
     assert kv(sh, ws=FAKE + 8) == mla.MLA_ERR_INVALID_ARG          # misaligned workspace
     assert kv(sh, nb=need.value - 2) == mla.MLA_ERR_INVALID_ARG    # workspace too small
     assert kv(sh, P=0) == mla.MLA_ERR_INVALID_ARG
+    assert kv(sh, P=(1 << 20) + 1) == mla.MLA_ERR_INVALID_ARG     # positions must fit 32-bit offsets
+    assert kv(sh, lens=None) == mla.MLA_ERR_INVALID_ARG
+    n = ctypes.c_int64(0)
+    assert lib.mla_prefill_kv_elems(ctypes.byref(sh), 65, ctypes.byref(n)) == mla.MLA_OK
+    assert n.value == sh.batch * sh.num_heads * 3 * 32 * 128      # three 32-position tiles per sequence
     assert kv(_shape(d_v=64)) == mla.MLA_ERR_UNSUPPORTED           # kernels exist for d_v 128
     assert att(sh, out=None) == mla.MLA_ERR_INVALID_ARG
     assert att(sh, ckr=FAKE + 4) == mla.MLA_ERR_INVALID_ARG

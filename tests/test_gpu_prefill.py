@@ -54,6 +54,18 @@ def _model_with_bf16_kv(pf, b, heads, positions):
     return out
 
 
+def untile_kv(x, B, H, P):
+    """[B, 32 T, H, 128] view of a tile-native key or value buffer: tile j of
+    (b, h) is 16 granule rows g of 32 slots, position 32 j + t in slot
+    t ^ (4 (g & 1))."""
+    T = (P + 31) // 32
+    x = np.asarray(x).reshape(B, H, T, 16, 32, 8)
+    g = np.arange(16)[:, None]
+    t = np.arange(32)[None, :]
+    y = x[:, :, :, g, t ^ (4 * (g & 1)), :]            # [B, H, T, 16 (g), 32 (t), 8]
+    return y.transpose(0, 2, 4, 1, 3, 5).reshape(B, T * 32, H, 128)
+
+
 def _run(pf):
     import torch
     from head_latent_attention_absorbed_amd import PrefillStep
@@ -74,14 +86,21 @@ def test_prefill_parity(name):
           flush=True)
     st = _run(pf)
     tol_abs, tol_rel = tolerances(w)
-    # keys and values of every position (bf16 results of fp32 sums)
-    k_got, v_got = to_np(st.k_nope), to_np(st.v)
+    # keys and values of every position < L_b (bf16 results of fp32 sums);
+    # the rest of the last tile is zero
+    k_got = untile_kv(to_np(st.k_nope), w.batch, w.heads, P)
+    v_got = untile_kv(to_np(st.v), w.batch, w.heads, P)
     for b in range(w.batch):
-        rec = oracle.bf16_to_f64(pf["ckr"][b])
+        L = int(pf["seq_lens"][b])
+        if L == 0:
+            continue
+        rec = oracle.bf16_to_f64(pf["ckr"][b, :L])
         K, V = oracle.reconstruct_kv(rec[:, :w.d_latent], rec[:, w.d_latent:], oracle.bf16_to_f64(pf["w_uk"]),
                                      oracle.bf16_to_f64(pf["w_uv"]))
-        compare(f"k_nope[{b}]", k_got[b].transpose(1, 0, 2), K[:, :, :w.d_nope], tol_abs, tol_rel)
-        compare(f"v[{b}]", v_got[b].transpose(1, 0, 2), V, tol_abs, tol_rel)
+        compare(f"k_nope[{b}]", k_got[b, :L].transpose(1, 0, 2), K[:, :, :w.d_nope], tol_abs, tol_rel)
+        compare(f"v[{b}]", v_got[b, :L].transpose(1, 0, 2), V, tol_abs, tol_rel)
+        end = -(-L // 32) * 32
+        assert np.all(k_got[b, L:end] == 0) and np.all(v_got[b, L:end] == 0), "tail of the last tile not zero"
     ref = oracle.prefill(pf)
     out, lse = to_np(st.out), to_np(st.lse)
     p_abs, p_rel = prefill_tolerances(w)
