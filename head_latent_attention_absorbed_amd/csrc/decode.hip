@@ -821,11 +821,17 @@ hipError_t launch_dc(const DecodeParams& p, int nw, hipStream_t stream) {
 // 32 query positions of one head, four waves per work-group.  The keys and
 // values are stored in that layout already (tile-native), so a tile is two
 // contiguous 8 KiB copies plus the shared RoPE keys gathered from the
-// records, all global->LDS DMA into a four-slot ring (three tiles in flight).
+// records, all global->LDS DMA into a two-slot ring.
 constexpr int kPfRows = 128;  // query positions per work-group
-constexpr int kPfBuf = 4;     // ring slots
+constexpr int kPfBuf = 2;     // ring slots: one tile computed while the next lands
 
-__global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
+// Three work-groups per CU (registers held to 168 per lane, a 40 KiB ring
+// each): the tile loop is a chain of dependent MFMA and softmax steps, so
+// more waves per SIMD pay more than a deeper ring (measured on the 2 x 4096
+// DeepSeek-V3 prompt batch: 2252 us with a 4-slot ring at two groups per CU,
+// 2018 us like this).
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+prefill_kernel(PrefillParams p) {
   using Gm = Geo<128>;
   constexpr int KROWS = Gm::GPT;   // 24 granule rows of K
   constexpr int VROWS = 16;        // 16 granule rows of V
