@@ -31,3 +31,10 @@ from .append_oracle import (  # noqa: F401
     apply_append,
     with_appended,
 )
+from .tpla_oracle import (  # noqa: F401
+    hadamard,
+    rotated,
+    shard_channels,
+    aggregate,
+    tpla_decode,
+)
