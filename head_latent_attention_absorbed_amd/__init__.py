@@ -33,7 +33,10 @@ from .binding import (  # noqa: F401
     mla_prefill_kv_elems,
     mla_prefill_kv,
     mla_prefill_attention,
+    mla_tpla_split_weights,
+    mla_tpla_rotate_cache,
+    mla_tpla_reduce,
     mla_status_string,
     mla_last_error,
 )
-from .step import DecodeStep, PrefillStep, capture_steps, combine_up_supported, split_plan  # noqa: F401
+from .step import DecodeStep, PrefillStep, TplaStep, capture_steps, combine_up_supported, split_plan  # noqa: F401

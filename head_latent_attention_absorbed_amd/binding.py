@@ -85,9 +85,13 @@ def library() -> ctypes.CDLL:
     lib.mla_prefill_kv_elems.argtypes = [SP, I32, ctypes.POINTER(ctypes.c_int64)]
     lib.mla_prefill_kv.argtypes = [SP, I32, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.mla_prefill_attention.argtypes = [SP, I32, P, P, P, P, P, P, P, P, P]
+    lib.mla_tpla_split_weights.argtypes = [SP, I32, I32, P, P, P, P, P]
+    lib.mla_tpla_rotate_cache.argtypes = [SP, P, I64, I64, I32, P]
+    lib.mla_tpla_reduce.argtypes = [SP, I32, P, P, P]
     for fn in ("mla_absorb_q", "mla_decode_num_parts", "mla_decode_paged", "mla_combine_lse", "mla_up_v",
                "mla_combine_up_v", "mla_append_kv_workspace_bytes", "mla_append_kv", "mla_prefill_workspace_bytes",
-               "mla_prefill_kv_elems", "mla_prefill_kv", "mla_prefill_attention"):
+               "mla_prefill_kv_elems", "mla_prefill_kv", "mla_prefill_attention", "mla_tpla_split_weights",
+               "mla_tpla_rotate_cache", "mla_tpla_reduce"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
@@ -216,3 +220,21 @@ def mla_prefill_attention(shape: MlaShape, prompt_len: int, q_nope, q_rope, k_no
     _check(library().mla_prefill_attention(ctypes.byref(shape), int(prompt_len), _ptr(q_nope), _ptr(q_rope),
                                            _ptr(k_nope), _ptr(ckr), _ptr(v), _ptr(seq_lens), _ptr(out), _ptr(lse),
                                            _stream(stream)), "mla_prefill_attention")
+
+
+def mla_tpla_split_weights(shape: MlaShape, n_shards: int, hadamard: bool, w_uk, w_uv, w_uk_shards, w_uv_shards,
+                           stream=None) -> None:
+    _check(library().mla_tpla_split_weights(ctypes.byref(shape), int(n_shards), int(bool(hadamard)), _ptr(w_uk),
+                                            _ptr(w_uv), _ptr(w_uk_shards), _ptr(w_uv_shards), _stream(stream)),
+           "mla_tpla_split_weights")
+
+
+def mla_tpla_rotate_cache(shape: MlaShape, c_kv, token_stride: int, block_stride: int, num_pages: int,
+                          stream=None) -> None:
+    _check(library().mla_tpla_rotate_cache(ctypes.byref(shape), _ptr(c_kv), int(token_stride), int(block_stride),
+                                           int(num_pages), _stream(stream)), "mla_tpla_rotate_cache")
+
+
+def mla_tpla_reduce(shape: MlaShape, n_shards: int, parts, out, stream=None) -> None:
+    _check(library().mla_tpla_reduce(ctypes.byref(shape), int(n_shards), _ptr(parts), _ptr(out), _stream(stream)),
+           "mla_tpla_reduce")

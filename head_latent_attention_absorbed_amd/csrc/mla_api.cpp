@@ -441,4 +441,89 @@ mla_status_t mla_prefill_attention(const mla_shape_t* shape, int32_t prompt_len,
   return hip_status(mla::launch_prefill(p, stream), "mla_prefill_attention launch");
 }
 
+mla_status_t mla_tpla_split_weights(const mla_shape_t* shape, int32_t n_shards, int32_t hadamard, const void* w_uk,
+                                    const void* w_uv, void* w_uk_shards, void* w_uv_shards, hipStream_t stream) {
+  mla_status_t st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (n_shards != 1 && n_shards != 2 && n_shards != 4)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_tpla_split_weights: n_shards %d (1, 2 or 4)", n_shards);
+  if (!w_uk || !w_uv || !w_uk_shards || !w_uv_shards)
+    return fail(MLA_ERR_INVALID_ARG, "mla_tpla_split_weights: NULL tensor");
+  if (!aligned16(w_uk) || !aligned16(w_uk_shards) || !aligned16(w_uv) || !aligned16(w_uv_shards))
+    return fail(MLA_ERR_INVALID_ARG, "mla_tpla_split_weights: tensors must be 16-byte aligned");
+  const int64_t H = shape->num_heads, dn = shape->d_nope, dc = shape->d_latent, dv = shape->d_v;
+  const int64_t dcs = dc / n_shards;
+  mla::HadamardParams k{};
+  k.in = static_cast<const uint16_t*>(w_uk);
+  k.out = static_cast<uint16_t*>(w_uk_shards);
+  k.n_vec = H * dn;  // the rows of every W_UK[h]
+  k.inner = 1;
+  k.in_outer = dc;
+  k.in_elem = 1;
+  k.out_outer = dcs;
+  k.out_elem = 1;
+  k.out_shard = H * dn * dcs;
+  k.d = (int32_t)dc;
+  k.n_shards = n_shards;
+  k.rotate = hadamard != 0;
+  hipError_t e = mla::launch_hadamard(k, stream);
+  if (e != hipSuccess) return hip_status(e, "mla_tpla_split_weights key launch");
+  mla::HadamardParams v{};
+  v.in = static_cast<const uint16_t*>(w_uv);
+  v.out = static_cast<uint16_t*>(w_uv_shards);
+  v.n_vec = H * dv;  // the columns of every W_UV[h]
+  v.inner = dv;
+  v.in_outer = dc * dv;
+  v.in_inner = 1;
+  v.in_elem = dv;
+  v.out_outer = dcs * dv;
+  v.out_inner = 1;
+  v.out_elem = dv;
+  v.out_shard = H * dcs * dv;
+  v.d = (int32_t)dc;
+  v.n_shards = n_shards;
+  v.rotate = hadamard != 0;
+  return hip_status(mla::launch_hadamard(v, stream), "mla_tpla_split_weights value launch");
+}
+
+mla_status_t mla_tpla_rotate_cache(const mla_shape_t* shape, void* c_kv, int64_t token_stride, int64_t block_stride,
+                                   int32_t num_pages, hipStream_t stream) {
+  mla_status_t st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (shape->cache_dtype != MLA_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_tpla_rotate_cache: bf16 caches only");
+  if (!c_kv) return fail(MLA_ERR_INVALID_ARG, "mla_tpla_rotate_cache: NULL cache");
+  if (num_pages < 0) return fail(MLA_ERR_INVALID_ARG, "mla_tpla_rotate_cache: num_pages %d", num_pages);
+  if (!aligned16(c_kv) || token_stride % 16 || block_stride % 16 ||
+      token_stride < (int64_t)shape->d_latent * 2 || block_stride < (int64_t)shape->block_size * token_stride)
+    return fail(MLA_ERR_INVALID_ARG, "mla_tpla_rotate_cache: bad alignment or strides");
+  mla::HadamardParams k{};
+  k.in = static_cast<const uint16_t*>(c_kv);
+  k.out = static_cast<uint16_t*>(c_kv);
+  k.n_vec = (int64_t)num_pages * shape->block_size;
+  k.inner = shape->block_size;
+  k.in_outer = k.out_outer = block_stride / 2;
+  k.in_inner = k.out_inner = token_stride / 2;
+  k.in_elem = k.out_elem = 1;
+  k.out_shard = 0;
+  k.d = shape->d_latent;
+  k.n_shards = 1;
+  k.rotate = true;
+  return hip_status(mla::launch_hadamard(k, stream), "mla_tpla_rotate_cache launch");
+}
+
+mla_status_t mla_tpla_reduce(const mla_shape_t* shape, int32_t n_shards, const float* parts, void* out,
+                             hipStream_t stream) {
+  mla_status_t st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (n_shards < 1 || n_shards > 64) return fail(MLA_ERR_INVALID_ARG, "mla_tpla_reduce: n_shards %d", n_shards);
+  if (!parts || !out) return fail(MLA_ERR_INVALID_ARG, "mla_tpla_reduce: NULL tensor");
+  if (!aligned16(parts) || !aligned16(out))
+    return fail(MLA_ERR_INVALID_ARG, "mla_tpla_reduce: tensors must be 16-byte aligned");
+  const int64_t count = (int64_t)shape->batch * shape->q_len * shape->num_heads * shape->d_v;
+  if (count % 4) return fail(MLA_ERR_UNSUPPORTED, "mla_tpla_reduce: output size not a multiple of 4");
+  return hip_status(mla::launch_shard_sum(parts, n_shards, count, out, shape->out_dtype == MLA_FP32, stream),
+                    "mla_tpla_reduce launch");
+}
+
 }  // extern "C"

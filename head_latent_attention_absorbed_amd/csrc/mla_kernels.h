@@ -69,6 +69,27 @@ struct PrefillParams {
   float* lse;                // fp32 [B, P, H]
 };
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+// Hadamard change of basis (x H / sqrt(d), Sylvester order) of bf16 vectors
+// of length d (256 or 512), or a plain copy when !rotate, with the result's
+// elements split over n_shards outputs.  Vector v starts at element
+// (v / inner) in_outer + (v % inner) in_inner of `in`, element k at + k in_elem;
+// its element k goes to (v / inner) out_outer + (v % inner) out_inner
+// + (k / (d / n_shards)) out_shard + (k % (d / n_shards)) out_elem of `out`.
+// in == out is allowed when both layouts are the same.
+struct HadamardParams {
+  const uint16_t* in;
+  uint16_t* out;
+  int64_t n_vec;
+  int64_t inner;
+  int64_t in_outer, in_inner, in_elem;
+  int64_t out_outer, out_inner, out_elem, out_shard;
+  int32_t d, n_shards;
+  bool rotate;
+};
+hipError_t launch_hadamard(const HadamardParams& p, hipStream_t stream);
+// out[m] = sum over i < n of parts[i * count + m] (fp32 in; bf16 RNE or fp32 out).
+hipError_t launch_shard_sum(const float* parts, int n, int64_t count, void* out, bool out_f32, hipStream_t stream);
+
 // W [H, R, C] bf16 -> its transpose [H, C, R] (R, C multiples of 64).
 hipError_t launch_transpose_heads(const uint16_t* w, uint16_t* wt, int H, int R, int C, hipStream_t stream);
 

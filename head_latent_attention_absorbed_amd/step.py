@@ -14,7 +14,7 @@ from .binding import (
     MLA_BF16, MLA_FP8_E4M3, MLA_FP16, MLA_FP32, MLA_TILE_TOKENS, MlaShape,
     mla_absorb_q, mla_append_kv, mla_append_kv_workspace_bytes, mla_decode_num_parts, mla_decode_paged,
     mla_combine_lse, mla_combine_up_v, mla_prefill_attention, mla_prefill_kv, mla_prefill_kv_elems,
-    mla_prefill_workspace_bytes, mla_up_v,
+    mla_prefill_workspace_bytes, mla_tpla_reduce, mla_tpla_rotate_cache, mla_tpla_split_weights, mla_up_v,
 )
 
 
@@ -249,4 +249,75 @@ class PrefillStep:
     def run(self, stream=None):
         self.kv(stream)
         self.attention(stream)
+        return self.out
+
+
+class TplaStep:
+    """The TPLA latent split run on one device: ``n_shards`` decodes over the
+    same paged cache, shard i with latent channels [i d_c/n, (i+1) d_c/n), its
+    slices of W_UK and W_UV and the whole RoPE key, then the sum of their fp32
+    outputs (what the all-reduce would produce).  With ``hadamard`` the cache
+    copy held here and the weight slices are first put in the Hadamard basis
+    (prepare())."""
+
+    def __init__(self, inputs: dict, n_shards: int = 2, hadamard: bool = True, device: str = "cuda",
+                 partial: str = "fp16"):
+        torch = self.torch = __import__("torch")
+        w = inputs["workload"]
+        if w.d_latent % n_shards:
+            raise ValueError("d_latent must split evenly over the shards")
+        if hadamard and w.cache_dtype != "bf16":
+            raise ValueError("the Hadamard basis change needs a bf16 cache")
+        self.base = DecodeStep(inputs, device=device, partial=partial)
+        self.workload = w
+        self.n, self.hadamard = n_shards, bool(hadamard)
+        self.num_pages = int(inputs["cache"].shape[0])
+        dcs = w.d_latent // n_shards
+        self.dcs = dcs
+        b = self.base
+        self.shard_shape = MlaShape.make(
+            batch=w.batch, num_heads=w.heads, q_len=w.q_len, d_latent=dcs, d_nope=w.d_nope, d_rope=w.d_rope,
+            d_v=w.d_v, block_size=w.block_size, max_blocks_per_seq=w.max_blocks_per_seq,
+            softmax_scale=float(inputs["softmax_scale"]), cache_dtype=b.shape.cache_dtype, out_dtype=MLA_FP32,
+            partial_dtype=b.shape.partial_dtype)
+        if not combine_up_supported(dcs, w.d_v):
+            raise ValueError(f"no merge + up-projection kernel for a {dcs}-wide shard")
+        B, S, H = w.batch, w.q_len, w.heads
+        bf16, f32 = torch.bfloat16, torch.float32
+        self.w_uk_s = torch.empty((n_shards, H, w.d_nope, dcs), dtype=bf16, device=device)
+        self.w_uv_s = torch.empty((n_shards, H, dcs, w.d_v), dtype=bf16, device=device)
+        self.num_parts = mla_decode_num_parts(self.shard_shape)
+        self.q_lat = torch.empty((n_shards, B, S, H, dcs), dtype=bf16, device=device)
+        self.o_part = torch.empty((self.num_parts, S * H, dcs), dtype=b.o_part.dtype, device=device)
+        self.lse_part = torch.empty((self.num_parts, S * H), dtype=f32, device=device)
+        self.parts = torch.empty((n_shards, B, S, H, w.d_v), dtype=f32, device=device)
+        self.shard_lse = torch.empty((n_shards, B, S, H), dtype=f32, device=device)
+        self.out = b.out  # [B, S_q, H, d_v] in the workload's output type
+
+    def prepare(self, stream=None):
+        """Weight slices (in the Hadamard basis if asked) and, then, the cache in that basis."""
+        b = self.base
+        mla_tpla_split_weights(b.shape, self.n, self.hadamard, b.w_uk, b.w_uv, self.w_uk_s, self.w_uv_s, stream)
+        if self.hadamard:
+            mla_tpla_rotate_cache(b.shape, b.cache, b.token_stride, b.block_stride, self.num_pages, stream)
+
+    def shard(self, i: int, stream=None):
+        """Shard i's decode: its absorbed queries, the split-K attention over its
+        latent channels (and the whole RoPE key), the merge and its W_UV slice."""
+        b, sh = self.base, self.shard_shape
+        mla_absorb_q(sh, b.q_nope, self.w_uk_s[i], self.q_lat[i], stream)
+        base = b.cache.data_ptr()
+        mla_decode_paged(sh, self.q_lat[i], b.q_rope, base + i * self.dcs * b.elem,
+                         base + self.workload.d_latent * b.elem, b.token_stride, b.block_stride, b.kv_scale,
+                         b.block_table, b.seq_lens, self.num_parts, self.o_part, self.lse_part, stream)
+        mla_combine_up_v(sh, self.num_parts, self.o_part, self.lse_part, b.seq_lens, self.w_uv_s[i], self.parts[i],
+                         self.shard_lse[i], stream)
+
+    def reduce(self, stream=None):
+        mla_tpla_reduce(self.base.shape, self.n, self.parts, self.out, stream)
+
+    def run(self, stream=None):
+        for i in range(self.n):
+            self.shard(i, stream)
+        self.reduce(stream)
         return self.out

@@ -282,6 +282,41 @@ mla_status_t mla_prefill_attention(const mla_shape_t* shape, int32_t prompt_len,
                                    const void* q_rope, const void* k_nope, const void* ckr, const void* v,
                                    const int32_t* seq_lens, void* out, float* lse, hipStream_t stream);
 
+/*
+ * TPLA latent split, run on one device.  TPLA splits the cached latent, and
+ * each head's input dimension with it, over n devices; each shard attends on
+ * its slice with the whole RoPE key, and an all-reduce adds the shards'
+ * outputs.  An orthogonal Hadamard change of basis of the latent, applied
+ * first, evens out the shards; full MLA is unchanged by it (TPLA abstract on
+ * the taxoreview pages for dblp:408/6122 and dblp:256/5536-3).  Shard i
+ * (of n) holds latent channels [i d_latent/n, (i+1) d_latent/n).  Its decode
+ * is the ordinary one at d_latent / n: mla_absorb_q with its W_UK slice,
+ * mla_decode_paged over the records viewed from latent channel i d_latent/n
+ * (c_kv advanced by that many elements, k_rope and the strides unchanged),
+ * and mla_combine_up_v with its W_UV slice into fp32; mla_tpla_reduce then
+ * adds the n results.  With H = R / sqrt(d_latent), R the Sylvester-ordered
+ * Hadamard matrix of order d_latent:
+ *
+ * mla_tpla_split_weights -- per-shard weight slices, in the changed basis if
+ *   `hadamard` is non-zero (W_UK' = W_UK H, W_UV' = H^T W_UV), else as given:
+ *   w_uk_shards[i][h] = W_UK'[h][:, S_i]   bf16 [n, H, d_nope, d_latent / n]
+ *   w_uv_shards[i][h] = W_UV'[h][S_i, :]   bf16 [n, H, d_latent / n, d_v]
+ *   fp32 transform, bf16 RNE results; n_shards 1, 2 or 4.
+ * mla_tpla_rotate_cache -- in place, c' = c H for the d_latent latent values
+ *   of every slot of pages 0 .. num_pages - 1 (slot j of page p at
+ *   c_kv + p block_stride + j token_stride bytes); bf16 caches only.  This is
+ *   the cache the same model would hold with W_DKV H as its down-projection.
+ * mla_tpla_reduce -- out = sum over i < n of parts[i]:
+ *   parts fp32 [n, B, S_q, H, d_v], out [B, S_q, H, d_v] in shape->out_dtype.
+ * All tensors are device pointers, 16-byte aligned.
+ */
+mla_status_t mla_tpla_split_weights(const mla_shape_t* shape, int32_t n_shards, int32_t hadamard, const void* w_uk,
+                                    const void* w_uv, void* w_uk_shards, void* w_uv_shards, hipStream_t stream);
+mla_status_t mla_tpla_rotate_cache(const mla_shape_t* shape, void* c_kv, int64_t token_stride, int64_t block_stride,
+                                   int32_t num_pages, hipStream_t stream);
+mla_status_t mla_tpla_reduce(const mla_shape_t* shape, int32_t n_shards, const float* parts, void* out,
+                             hipStream_t stream);
+
 /* Static description of a status code. */
 const char* mla_status_string(mla_status_t status);
 

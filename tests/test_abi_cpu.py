@@ -23,6 +23,7 @@ def test_exports_every_declared_symbol():
     assert set(declared) >= {"mla_absorb_q", "mla_decode_num_parts", "mla_decode_paged", "mla_combine_lse",
                              "mla_up_v", "mla_combine_up_v", "mla_append_kv", "mla_append_kv_workspace_bytes",
                              "mla_prefill_workspace_bytes", "mla_prefill_kv_elems", "mla_prefill_kv", "mla_prefill_attention",
+                             "mla_tpla_split_weights", "mla_tpla_rotate_cache", "mla_tpla_reduce",
                              "mla_status_string", "mla_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", mla.library_path], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -229,3 +230,25 @@ def test_prefill_argument_checks():
     assert att(sh, out=None) == mla.MLA_ERR_INVALID_ARG
     assert att(sh, ckr=FAKE + 4) == mla.MLA_ERR_INVALID_ARG
     assert att(_shape(d_nope=192)) == mla.MLA_ERR_UNSUPPORTED
+
+
+def test_tpla_argument_checks():
+    lib = _lib()
+    sh = _shape()
+    split = lambda shp, n=2, **kw: lib.mla_tpla_split_weights(ctypes.byref(shp), n, 1, kw.get("w_uk", FAKE), FAKE,
+                                                               FAKE, kw.get("out", FAKE), None)
+    assert split(sh, n=3) == mla.MLA_ERR_UNSUPPORTED
+    assert split(sh, n=8) == mla.MLA_ERR_UNSUPPORTED
+    assert split(sh, w_uk=None) == mla.MLA_ERR_INVALID_ARG
+    assert split(sh, out=FAKE + 2) == mla.MLA_ERR_INVALID_ARG
+    rot = lambda shp, **kw: lib.mla_tpla_rotate_cache(ctypes.byref(shp), kw.get("c", FAKE), kw.get("ts", 1152),
+                                                      kw.get("bs", 1152 * 64), kw.get("np", 4), None)
+    assert rot(_shape(cache_dtype=mla.MLA_FP8_E4M3), ts=576, bs=576 * 64) == mla.MLA_ERR_UNSUPPORTED
+    assert rot(sh, c=None) == mla.MLA_ERR_INVALID_ARG
+    assert rot(sh, ts=1000) == mla.MLA_ERR_INVALID_ARG               # latent does not fit the record
+    assert rot(sh, bs=1152 * 63) == mla.MLA_ERR_INVALID_ARG          # pages overlap
+    assert rot(sh, np=-1) == mla.MLA_ERR_INVALID_ARG
+    red = lambda shp, n=2, **kw: lib.mla_tpla_reduce(ctypes.byref(shp), n, kw.get("parts", FAKE), FAKE, None)
+    assert red(sh, n=0) == mla.MLA_ERR_INVALID_ARG
+    assert red(sh, parts=None) == mla.MLA_ERR_INVALID_ARG
+    assert red(sh, parts=FAKE + 4) == mla.MLA_ERR_INVALID_ARG
