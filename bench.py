@@ -308,6 +308,54 @@ def main():
     p_kv_flops = p_tokens * pw.heads * pw.d_latent * (pw.d_nope + pw.d_v) * 2
     del pst
 
+    # The TPLA latent split on one device: two Hadamard-basis shards of the
+    # same decode (each over half the latent and the whole RoPE key), summed.
+    # Each call is timed with events; the split's error against the MLA
+    # decode is measured on the same inputs, with and without the basis change.
+    from head_latent_attention_absorbed_amd import TplaStep
+    steps[0].run()
+    torch.cuda.synchronize()
+    mla_out = steps[0].out.float().clone()
+    tp_err, tst = {}, None
+    for had in (False, True):
+        t = TplaStep(inputs, 2, had, partial=args.partial)
+        t.prepare()
+        t.run()
+        torch.cuda.synchronize()
+        tp_err["hadamard" if had else "plain"] = float((t.out.float() - mla_out).norm() / mla_out.norm())
+        if had:
+            tst = t
+        else:
+            plain = t
+    KT = max(3, min(K, 10))
+    names = ("absorb", "decode", "combine_up")
+    tev = [[torch.cuda.Event(enable_timing=True) for _ in range(3 * tst.n + 2)] for _ in range(KT)]
+    for i in range(KT):
+        e = tev[i]
+        e[0].record(stream)
+        for sh in range(tst.n):
+            for j, nm in enumerate(names):
+                getattr(tst, nm)(sh)
+                e[1 + 3 * sh + j].record(stream)
+        tst.reduce()
+        e[-1].record(stream)
+    torch.cuda.synchronize()
+    tp_step = float(np.median([e[0].elapsed_time(e[-1]) * 1e3 for e in tev]))
+    tp_dec = float(np.median([e[1 + 3 * sh].elapsed_time(e[2 + 3 * sh]) * 1e3 for e in tev for sh in range(tst.n)]))
+    sh_bytes = alg["tokens"] * (tst.dcs + w.d_rope) * 2 + w.batch * w.q_len * w.heads * (tst.dcs + w.d_rope) * 2
+    # the basis change of the whole cache (latent of every slot, read and written once)
+    rev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    from head_latent_attention_absorbed_amd import mla_tpla_rotate_cache
+    b0 = plain.base
+    for i in range(3):
+        rev[i].record(stream)
+        mla_tpla_rotate_cache(b0.shape, b0.cache, b0.token_stride, b0.block_stride, plain.num_pages)
+    rev[3].record(stream)
+    torch.cuda.synchronize()
+    rot_us = float(np.median([rev[i].elapsed_time(rev[i + 1]) * 1e3 for i in range(3)]))
+    rot_bytes = 2 * plain.num_pages * w.block_size * w.d_latent * 2
+    del plain
+
     us_step = ms_per_step * 1e3
     value = alg["cache_bytes"] / (us_step * 1e-6) / 1e12
     achieved = alg["decode_bytes"] / (dec_us * 1e-6) / 1e9
@@ -362,6 +410,19 @@ def main():
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(app_bytes / (app_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                          "algorithmic_bytes_per_call": app_bytes},
+        },
+        "tpla": {
+            "what": "TPLA latent split on one GPU: 2 Hadamard-basis shards (absorb + decode + merge/up-proj "
+                    "at d_c/2 each) + mla_tpla_reduce",
+            "n_shards": tst.n, "us_per_step": round(tp_step, 2), "shard_decode_us_median": round(tp_dec, 2),
+            "rel_l2_vs_mla": {k: round(v, 5) for k, v in tp_err.items()},
+            "roofline": {"kernel": "decode_kernel (one shard, d_latent 256)", "bound": "hbm",
+                         "achieved": round(sh_bytes / (tp_dec * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(sh_bytes / (tp_dec * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": sh_bytes},
+            "rotate_cache": {"us": round(rot_us, 2), "bytes": rot_bytes,
+                             "achieved_gbs": round(rot_bytes / (rot_us * 1e-6) / 1e9, 1),
+                             "frac": round(rot_bytes / (rot_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         },
         "prefill": {
             "what": "mla_prefill_kv (K_nope, V per head from the records) + mla_prefill_attention (causal)",

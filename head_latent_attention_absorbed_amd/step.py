@@ -301,17 +301,28 @@ class TplaStep:
         if self.hadamard:
             mla_tpla_rotate_cache(b.shape, b.cache, b.token_stride, b.block_stride, self.num_pages, stream)
 
-    def shard(self, i: int, stream=None):
-        """Shard i's decode: its absorbed queries, the split-K attention over its
-        latent channels (and the whole RoPE key), the merge and its W_UV slice."""
-        b, sh = self.base, self.shard_shape
-        mla_absorb_q(sh, b.q_nope, self.w_uk_s[i], self.q_lat[i], stream)
+    def absorb(self, i: int, stream=None):
+        mla_absorb_q(self.shard_shape, self.base.q_nope, self.w_uk_s[i], self.q_lat[i], stream)
+
+    def decode(self, i: int, stream=None):
+        """Split-K attention of shard i over its latent channels and the whole RoPE key."""
+        b = self.base
         base = b.cache.data_ptr()
-        mla_decode_paged(sh, self.q_lat[i], b.q_rope, base + i * self.dcs * b.elem,
+        mla_decode_paged(self.shard_shape, self.q_lat[i], b.q_rope, base + i * self.dcs * b.elem,
                          base + self.workload.d_latent * b.elem, b.token_stride, b.block_stride, b.kv_scale,
                          b.block_table, b.seq_lens, self.num_parts, self.o_part, self.lse_part, stream)
-        mla_combine_up_v(sh, self.num_parts, self.o_part, self.lse_part, b.seq_lens, self.w_uv_s[i], self.parts[i],
-                         self.shard_lse[i], stream)
+
+    def combine_up(self, i: int, stream=None):
+        b = self.base
+        mla_combine_up_v(self.shard_shape, self.num_parts, self.o_part, self.lse_part, b.seq_lens, self.w_uv_s[i],
+                         self.parts[i], self.shard_lse[i], stream)
+
+    def shard(self, i: int, stream=None):
+        """Shard i's decode: its absorbed queries, the split-K attention, the
+        merge and its W_UV slice (fp32 into parts[i])."""
+        self.absorb(i, stream)
+        self.decode(i, stream)
+        self.combine_up(i, stream)
 
     def reduce(self, stream=None):
         mla_tpla_reduce(self.base.shape, self.n, self.parts, self.out, stream)
