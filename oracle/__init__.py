@@ -38,3 +38,8 @@ from .tpla_oracle import (  # noqa: F401
     aggregate,
     tpla_decode,
 )
+from .gqla_oracle import (  # noqa: F401
+    group_of,
+    gqa_stream,
+    gqa_decode,
+)

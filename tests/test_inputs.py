@@ -78,6 +78,33 @@ def test_named_workloads_match_the_configs():
     assert (t.batch, t.heads, t.d_latent, t.seq_len, t.out_dtype, t.weight_var) == (8, 128, 256, (32768, 32768), "fp32", 1 / 256)
     k = d["kimi_k2_fp8"]
     assert (k.batch, k.heads, k.q_len, k.seq_len, k.cache_dtype) == (16, 64, 4, (16384, 32768), "fp8_e4m3")
+    g = d["gqla_gqa"]
+    assert (g.batch, g.heads, g.q_len, g.seq_len, g.d_nope, g.d_v) == (16, 32, 2, (8192, 8192), 128, 128)
     for w in d.values():
         assert abs(w.softmax_scale - 192 ** -0.5) < 1e-15
-        assert w.seed == 1000 + ("tiny", "deepseek_v3", "gqa7b", "tpla_shard", "kimi_k2_fp8").index(w.name)
+        assert w.seed == 1000 + ("tiny", "deepseek_v3", "gqa7b", "tpla_shard", "kimi_k2_fp8", "gqla_gqa").index(w.name)
+
+
+def test_gqa_inputs_layout():
+    """Per-group streams: own pages, the shared RoPE key repeated in every
+    group's record, poison past the length, reproducible."""
+    from workloads import make_gqa_inputs
+
+    w = small_workload("gqla_gqa", batch=3, seq_len=(5, 130), max_seq_len=192, forced_lens=(130, 1, 0), spare_blocks=2)
+    a, b = make_gqa_inputs(w, 4), make_gqa_inputs(w, 4)
+    assert all(np.array_equal(a[k], b[k]) for k in ("q_nope", "cache", "block_table"))
+    G, bs = 4, w.block_size
+    pages = a["block_table"][a["block_table"] >= 0]
+    assert len(pages) == len(set(pages.tolist()))                     # no page shared by two streams
+    assert np.array_equal(a["stream_lens"], np.repeat(a["seq_lens"], G))
+    dn, dv = w.d_nope, w.d_v
+    for bq in range(3):
+        L = int(a["seq_lens"][bq])
+        t = np.arange(L)
+        recs = [a["cache"][a["block_table"][bq * G + g, t // bs], t % bs] for g in range(G)]
+        for g in range(1, G):
+            assert np.array_equal(recs[g][:, dn + dv:], recs[0][:, dn + dv:])        # one RoPE key per token
+            assert L == 0 or not np.array_equal(recs[g][:, :dn], recs[0][:, :dn])    # own K_nope per group
+        if L % bs:
+            last = a["block_table"][bq * G, (L - 1) // bs]
+            assert np.all(a["cache"][last, L % bs:] == 0x7FC0)                       # poisoned tail

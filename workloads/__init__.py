@@ -9,6 +9,7 @@ any of the method's code.
 from .configs import WORKLOADS, Workload, get_workload, prefill_workload, small_workload
 from .generate import (
     make_append_inputs,
+    make_gqa_inputs,
     make_inputs,
     make_prefill_inputs,
     f32_to_bf16_bits,
@@ -24,6 +25,7 @@ __all__ = [
     "prefill_workload",
     "make_inputs",
     "make_append_inputs",
+    "make_gqa_inputs",
     "make_prefill_inputs",
     "f32_to_bf16_bits",
     "f32_to_e4m3_bits",

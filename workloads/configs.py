@@ -83,6 +83,12 @@ WORKLOADS = {
         paged=True, cache_dtype="bf16", out_dtype="fp32", weight_var=1.0 / 256, seed=1003,
         description="One latent-split TP shard: B=8, H=128, d_c=256, context 32768, fp32 partial out + LSE",
     ),
+    "gqla_gqa": Workload(
+        name="gqla_gqa", batch=16, heads=32, q_len=2, d_latent=512, seq_len=(8192, 8192),
+        paged=True, cache_dtype="bf16", out_dtype="bf16", weight_var=1.0 / 512, seed=1005,
+        description="GQLA's two decoding paths at s_q = 2 for a LLaMA-3-8B-shaped model: B=16, H=32 in 8 "
+                    "groups, context 8192 (MQA-absorb over the latent, or GQA over per-group K/V)",
+    ),
     "kimi_k2_fp8": Workload(
         name="kimi_k2_fp8", batch=16, heads=64, q_len=4, d_latent=512, seq_len=(16384, 32768),
         paged=True, cache_dtype="fp8_e4m3", out_dtype="bf16", weight_var=1.0 / 512, seed=1004,
@@ -90,8 +96,8 @@ WORKLOADS = {
     ),
 }
 
-# The order of the five workloads; the seed of workload i is 1000 + i.
-WORKLOAD_ORDER = ("tiny", "deepseek_v3", "gqa7b", "tpla_shard", "kimi_k2_fp8")
+# The order of the workloads; the seed of workload i is 1000 + i.
+WORKLOAD_ORDER = ("tiny", "deepseek_v3", "gqa7b", "tpla_shard", "kimi_k2_fp8", "gqla_gqa")
 
 
 def get_workload(name: str) -> Workload:
@@ -119,3 +125,7 @@ def prefill_workload() -> tuple[Workload, int]:
     w = replace(get_workload("deepseek_v3"), name="deepseek_v3_prefill", batch=2, seq_len=(2048, PREFILL_PROMPT_LEN),
                 forced_lens=(PREFILL_PROMPT_LEN,))
     return w, PREFILL_PROMPT_LEN
+
+
+# Key/value groups of the GQLA workload (LLaMA-3-8B: 32 query heads, 8 KV heads).
+GQLA_GROUPS = 8

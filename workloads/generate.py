@@ -167,3 +167,54 @@ def make_prefill_inputs(w: Workload, prompt_len: int, seed: int | None = None) -
     ckr = f32_to_bf16_bits(_normal(rng, (B, P, w.d_latent + w.d_rope)))
     return dict(workload=w, prompt_len=P, seq_lens=lens.astype(np.int32), w_uk=w_uk, w_uv=w_uv, q_nope=q_nope,
                 q_rope=q_rope, ckr=ckr, softmax_scale=w.softmax_scale)
+
+
+def make_gqa_inputs(w: Workload, groups: int, seed: int | None = None, poison: bool = True) -> dict:
+    """Inputs of a GQA decode over a per-group expanded cache (the second
+    decoding path of the GQLA abstract): the H heads form ``groups`` groups of
+    H / groups consecutive heads; each (sequence, group) stream holds, per
+    position, the record [K_nope (d_n) | V (d_v) | k_rope (d_r)], the RoPE key
+    being the token's one shared key repeated in every group's record.
+    Queries q_nope / q_rope [B, S_q, H, .], K_nope, V, k_rope ~ N(0, 1), bf16.
+    Streams are paged like the latent cache: stream (b, g) = b * groups + g
+    has its own block-table row; seq_lens [B] and per stream.  Child stream 7
+    of the seed (lengths, queries, cache, pages)."""
+    seed = w.seed if seed is None else seed
+    if w.heads % groups:
+        raise ValueError("heads must split evenly into groups")
+    s_len, s_q, s_kv, s_pg = [np.random.default_rng(c) for c in np.random.SeedSequence(seed).spawn(8)[7].spawn(4)]
+    B, H, S, G, bs = w.batch, w.heads, w.q_len, groups, w.block_size
+    dn, dv, dr = w.d_nope, w.d_v, w.d_rope
+    lo, hi = w.seq_len
+    lens = s_len.integers(lo, hi + 1, size=B, dtype=np.int64)
+    for i, v in enumerate(w.forced_lens[:B]):
+        lens[i] = v
+    if np.any(lens > w.capacity) or np.any(lens < 0):
+        raise ValueError("sequence length outside [0, capacity]")
+    q_nope = f32_to_bf16_bits(_normal(s_q, (B, S, H, dn)))
+    q_rope = f32_to_bf16_bits(_normal(s_q, (B, S, H, dr)))
+    # pages of the B * G streams
+    nblk = [-(-int(lens[bg // G]) // bs) for bg in range(B * G)]
+    total_blocks = max(1, int(sum(nblk)) + w.spare_blocks)
+    perm = s_pg.permutation(total_blocks).astype(np.int32) if w.paged else np.arange(total_blocks, dtype=np.int32)
+    MB = w.max_blocks_per_seq
+    block_table = np.full((B * G, MB), -1, dtype=np.int32)
+    off = 0
+    for bg in range(B * G):
+        block_table[bg, : nblk[bg]] = perm[off: off + nblk[bg]]
+        off += nblk[bg]
+    rec = dn + dv + dr
+    cache = np.full((total_blocks * bs, rec), BF16_NAN if poison else 0, dtype=np.uint16)
+    for b in range(B):
+        L = int(lens[b])
+        t = np.arange(L, dtype=np.int64)
+        kr = f32_to_bf16_bits(_normal(s_kv, (L, dr)))           # one RoPE key per token
+        for g in range(G):
+            kv = f32_to_bf16_bits(_normal(s_kv, (L, dn + dv)))  # this group's K_nope | V
+            dest = block_table[b * G + g, t // bs].astype(np.int64) * bs + t % bs
+            cache[dest, : dn + dv] = kv
+            cache[dest, dn + dv:] = kr
+    return dict(workload=w, groups=G, q_nope=q_nope, q_rope=q_rope, seq_lens=lens.astype(np.int32),
+                stream_lens=np.repeat(lens.astype(np.int32), G), block_table=block_table,
+                cache=cache.reshape(total_blocks, bs, rec), num_blocks=total_blocks,
+                softmax_scale=w.softmax_scale)
