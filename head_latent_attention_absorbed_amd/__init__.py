@@ -36,7 +36,9 @@ from .binding import (  # noqa: F401
     mla_tpla_split_weights,
     mla_tpla_rotate_cache,
     mla_tpla_reduce,
+    mla_gqa_queries,
+    mla_gqa_output,
     mla_status_string,
     mla_last_error,
 )
-from .step import DecodeStep, PrefillStep, TplaStep, capture_steps, combine_up_supported, split_plan  # noqa: F401
+from .step import DecodeStep, GqaStep, PrefillStep, TplaStep, capture_steps, combine_up_supported, split_plan  # noqa: F401

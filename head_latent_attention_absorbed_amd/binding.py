@@ -88,10 +88,12 @@ def library() -> ctypes.CDLL:
     lib.mla_tpla_split_weights.argtypes = [SP, I32, I32, P, P, P, P, P]
     lib.mla_tpla_rotate_cache.argtypes = [SP, P, I64, I64, I32, P]
     lib.mla_tpla_reduce.argtypes = [SP, I32, P, P, P]
+    lib.mla_gqa_queries.argtypes = [SP, I32, P, P, P, P, P]
+    lib.mla_gqa_output.argtypes = [SP, I32, P, P, P, P, P]
     for fn in ("mla_absorb_q", "mla_decode_num_parts", "mla_decode_paged", "mla_combine_lse", "mla_up_v",
                "mla_combine_up_v", "mla_append_kv_workspace_bytes", "mla_append_kv", "mla_prefill_workspace_bytes",
                "mla_prefill_kv_elems", "mla_prefill_kv", "mla_prefill_attention", "mla_tpla_split_weights",
-               "mla_tpla_rotate_cache", "mla_tpla_reduce"):
+               "mla_tpla_rotate_cache", "mla_tpla_reduce", "mla_gqa_queries", "mla_gqa_output"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
@@ -238,3 +240,13 @@ def mla_tpla_rotate_cache(shape: MlaShape, c_kv, token_stride: int, block_stride
 def mla_tpla_reduce(shape: MlaShape, n_shards: int, parts, out, stream=None) -> None:
     _check(library().mla_tpla_reduce(ctypes.byref(shape), int(n_shards), _ptr(parts), _ptr(out), _stream(stream)),
            "mla_tpla_reduce")
+
+
+def mla_gqa_queries(shape: MlaShape, groups: int, q_nope, q_rope, q_cat, q_rope_g, stream=None) -> None:
+    _check(library().mla_gqa_queries(ctypes.byref(shape), int(groups), _ptr(q_nope), _ptr(q_rope), _ptr(q_cat),
+                                     _ptr(q_rope_g), _stream(stream)), "mla_gqa_queries")
+
+
+def mla_gqa_output(shape: MlaShape, groups: int, o_lat, lse_g, out, lse, stream=None) -> None:
+    _check(library().mla_gqa_output(ctypes.byref(shape), int(groups), _ptr(o_lat), _ptr(lse_g), _ptr(out), _ptr(lse),
+                                    _stream(stream)), "mla_gqa_output")

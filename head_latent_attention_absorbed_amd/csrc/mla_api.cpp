@@ -526,4 +526,63 @@ mla_status_t mla_tpla_reduce(const mla_shape_t* shape, int32_t n_shards, const f
                     "mla_tpla_reduce launch");
 }
 
+namespace {
+
+mla_status_t check_gqa(const mla_shape_t* shape, int32_t groups) {
+  mla_status_t st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (groups < 1 || shape->num_heads % groups)
+    return fail(MLA_ERR_INVALID_ARG, "gqa: %d heads do not split into %d groups", shape->num_heads, groups);
+  const int dq = shape->d_nope + shape->d_v;
+  if (dq != 256 && dq != 512)
+    return fail(MLA_ERR_UNSUPPORTED, "gqa: d_nope + d_v = %d (the decode reads 256- or 512-wide records)", dq);
+  if ((int64_t)shape->batch * groups > mla::kMaxBatch)
+    return fail(MLA_ERR_UNSUPPORTED, "gqa: batch * groups %d > %d", shape->batch * groups, mla::kMaxBatch);
+  return MLA_OK;
+}
+
+mla::GqaParams gqa_params(const mla_shape_t* shape, int32_t groups) {
+  mla::GqaParams p{};
+  p.B = shape->batch;
+  p.S = shape->q_len;
+  p.H = shape->num_heads;
+  p.G = groups;
+  p.dn = shape->d_nope;
+  p.dv = shape->d_v;
+  p.dr = shape->d_rope;
+  return p;
+}
+
+}  // namespace
+
+mla_status_t mla_gqa_queries(const mla_shape_t* shape, int32_t groups, const void* q_nope, const void* q_rope,
+                             void* q_cat, void* q_rope_g, hipStream_t stream) {
+  mla_status_t st = check_gqa(shape, groups);
+  if (st != MLA_OK) return st;
+  if (!q_nope || !q_rope || !q_cat || !q_rope_g) return fail(MLA_ERR_INVALID_ARG, "mla_gqa_queries: NULL tensor");
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(q_cat) || !aligned16(q_rope_g))
+    return fail(MLA_ERR_INVALID_ARG, "mla_gqa_queries: tensors must be 16-byte aligned");
+  mla::GqaParams p = gqa_params(shape, groups);
+  p.q_nope = static_cast<const uint16_t*>(q_nope);
+  p.q_rope = static_cast<const uint16_t*>(q_rope);
+  p.q_cat = static_cast<uint16_t*>(q_cat);
+  p.q_rope_g = static_cast<uint16_t*>(q_rope_g);
+  return hip_status(mla::launch_gqa_queries(p, stream), "mla_gqa_queries launch");
+}
+
+mla_status_t mla_gqa_output(const mla_shape_t* shape, int32_t groups, const float* o_lat, const float* lse_g,
+                            void* out, float* lse, hipStream_t stream) {
+  mla_status_t st = check_gqa(shape, groups);
+  if (st != MLA_OK) return st;
+  if (!o_lat || !lse_g || !out || !lse) return fail(MLA_ERR_INVALID_ARG, "mla_gqa_output: NULL tensor");
+  if (!aligned16(o_lat) || !aligned16(out))
+    return fail(MLA_ERR_INVALID_ARG, "mla_gqa_output: o_lat and out must be 16-byte aligned");
+  mla::GqaParams p = gqa_params(shape, groups);
+  p.o_lat = o_lat;
+  p.lse_g = lse_g;
+  p.out = out;
+  p.lse = lse;
+  return hip_status(mla::launch_gqa_output(p, shape->out_dtype == MLA_FP32, stream), "mla_gqa_output launch");
+}
+
 }  // extern "C"

@@ -90,6 +90,23 @@ hipError_t launch_hadamard(const HadamardParams& p, hipStream_t stream);
 // out[m] = sum over i < n of parts[i * count + m] (fp32 in; bf16 RNE or fp32 out).
 hipError_t launch_shard_sum(const float* parts, int n, int64_t count, void* out, bool out_f32, hipStream_t stream);
 
+// Regrouping around the GQA decoding path (GQLA), run as the latent decode
+// over per-group records [K_nope (dn) | V (dv) | k_rope (dr)] with streams
+// (b, g) as sequences and the group's H / G heads as rows.
+struct GqaParams {
+  int32_t B, S, H, G, dn, dv, dr;
+  const uint16_t* q_nope;    // bf16 [B, S, H, dn]
+  const uint16_t* q_rope;    // bf16 [B, S, H, dr]
+  uint16_t* q_cat;           // bf16 [B G, S, H / G, dn + dv]: [q_nope | 0]
+  uint16_t* q_rope_g;        // bf16 [B G, S, H / G, dr]
+  const float* o_lat;        // fp32 [B G, S, H / G, dn + dv]: merged rows
+  const float* lse_g;        // fp32 [B G, S, H / G]
+  void* out;                 // [B, S, H, dv], bf16 or fp32
+  float* lse;                // fp32 [B, S, H]
+};
+hipError_t launch_gqa_queries(const GqaParams& p, hipStream_t stream);
+hipError_t launch_gqa_output(const GqaParams& p, bool out_f32, hipStream_t stream);
+
 // W [H, R, C] bf16 -> its transpose [H, C, R] (R, C multiples of 64).
 hipError_t launch_transpose_heads(const uint16_t* w, uint16_t* wt, int H, int R, int C, hipStream_t stream);
 

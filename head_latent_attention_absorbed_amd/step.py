@@ -15,6 +15,7 @@ from .binding import (
     mla_absorb_q, mla_append_kv, mla_append_kv_workspace_bytes, mla_decode_num_parts, mla_decode_paged,
     mla_combine_lse, mla_combine_up_v, mla_prefill_attention, mla_prefill_kv, mla_prefill_kv_elems,
     mla_prefill_workspace_bytes, mla_tpla_reduce, mla_tpla_rotate_cache, mla_tpla_split_weights, mla_up_v,
+    mla_gqa_output, mla_gqa_queries,
 )
 
 
@@ -331,4 +332,69 @@ class TplaStep:
         for i in range(self.n):
             self.shard(i, stream)
         self.reduce(stream)
+        return self.out
+
+
+class GqaStep:
+    """GQLA's GQA decoding path: the latent decode run over per-group records
+    [K_nope | V | k_rope], each (sequence, group) stream a sequence of the
+    view and the group's heads its rows; the queries [q_nope | 0] are
+    regrouped before (mla_gqa_queries) and the value columns of the merged
+    rows regrouped after (mla_gqa_output)."""
+
+    def __init__(self, gi: dict, device: str = "cuda", partial: str = "fp16"):
+        torch = self.torch = __import__("torch")
+        w = gi["workload"]
+        G = int(gi["groups"])
+        self.workload, self.groups = w, G
+        hpg = w.heads // G
+        dq = w.d_nope + w.d_v
+        common = dict(q_len=w.q_len, d_nope=w.d_nope, d_rope=w.d_rope, d_v=w.d_v, block_size=w.block_size,
+                      max_blocks_per_seq=w.max_blocks_per_seq, softmax_scale=float(gi["softmax_scale"]),
+                      cache_dtype=MLA_BF16, partial_dtype=MLA_FP16 if partial == "fp16" else MLA_FP32)
+        self.shape = MlaShape.make(batch=w.batch, num_heads=w.heads, d_latent=w.d_latent,
+                                   out_dtype=MLA_FP32 if w.out_dtype == "fp32" else MLA_BF16, **common)
+        self.view = MlaShape.make(batch=w.batch * G, num_heads=hpg, d_latent=dq, out_dtype=MLA_FP32, **common)
+        bf16, f32 = torch.bfloat16, torch.float32
+        self.q_nope = _dev_bits(torch, gi["q_nope"], device, bf16)
+        self.q_rope = _dev_bits(torch, gi["q_rope"], device, bf16)
+        self.cache = _dev_bits(torch, gi["cache"], device, bf16)
+        self.block_table = torch.from_numpy(gi["block_table"]).to(device)
+        self.stream_lens = torch.from_numpy(gi["stream_lens"]).to(device)
+        self.token_stride = (dq + w.d_rope) * 2
+        self.block_stride = w.block_size * self.token_stride
+        self.elem_off = dq * 2
+        B, S, H = w.batch, w.q_len, w.heads
+        self.q_cat = torch.empty((B * G, S, hpg, dq), dtype=bf16, device=device)
+        self.q_rope_g = torch.empty((B * G, S, hpg, w.d_rope), dtype=bf16, device=device)
+        self.num_parts = mla_decode_num_parts(self.view)
+        self.o_part = torch.empty((self.num_parts, S * hpg, dq), dtype=torch.float16 if partial == "fp16" else f32,
+                                  device=device)
+        self.lse_part = torch.empty((self.num_parts, S * hpg), dtype=f32, device=device)
+        self.o_lat = torch.empty((B * G, S, hpg, dq), dtype=f32, device=device)
+        self.lse_g = torch.empty((B * G, S, hpg), dtype=f32, device=device)
+        self.out = torch.empty((B, S, H, w.d_v), dtype=f32 if w.out_dtype == "fp32" else bf16, device=device)
+        self.lse = torch.empty((B, S, H), dtype=f32, device=device)
+
+    def queries(self, stream=None):
+        mla_gqa_queries(self.shape, self.groups, self.q_nope, self.q_rope, self.q_cat, self.q_rope_g, stream)
+
+    def decode(self, stream=None):
+        base = self.cache.data_ptr()
+        mla_decode_paged(self.view, self.q_cat, self.q_rope_g, base, base + self.elem_off, self.token_stride,
+                         self.block_stride, None, self.block_table, self.stream_lens, self.num_parts, self.o_part,
+                         self.lse_part, stream)
+
+    def combine(self, stream=None):
+        mla_combine_lse(self.view, self.num_parts, self.o_part, self.lse_part, self.stream_lens, self.o_lat,
+                        self.lse_g, stream)
+
+    def output(self, stream=None):
+        mla_gqa_output(self.shape, self.groups, self.o_lat, self.lse_g, self.out, self.lse, stream)
+
+    def run(self, stream=None):
+        self.queries(stream)
+        self.decode(stream)
+        self.combine(stream)
+        self.output(stream)
         return self.out

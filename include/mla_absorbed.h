@@ -317,6 +317,38 @@ mla_status_t mla_tpla_rotate_cache(const mla_shape_t* shape, void* c_kv, int64_t
 mla_status_t mla_tpla_reduce(const mla_shape_t* shape, int32_t n_shards, const float* parts, void* out,
                              hipStream_t stream);
 
+/*
+ * GQLA's GQA decoding path.  GQLA weights expose two equivalent decoding
+ * paths: MLA's absorbed MQA path over the latent (the calls above) and a GQA
+ * path over a cache expanded per head group, which GQLA runs with two query
+ * tokens per step (GQLA abstract on the "GQA-to-MLA" Daily Papers listing).
+ * Heads h of a model with G groups belong to group h / (H / G).  The per-group
+ * cache holds, for each stream s = b G + g, records
+ *   [K_nope (d_nope) | V (d_v) | k_rope (d_rope)]   (the RoPE key is the token's
+ *   one shared key), paged like the latent cache with its own block-table row.
+ * The path is the latent decode run with a view shape: batch B G, num_heads
+ * H / G, d_latent = d_nope + d_v (256 or 512), the same d_rope, q_len,
+ * softmax_scale and block_size:
+ *   1. mla_gqa_queries  -- q_cat[s, t, j] = [q_nope[b, t, g H/G + j] | 0]
+ *      bf16 [B G, S_q, H/G, d_nope + d_v], and q_rope_g likewise
+ *      bf16 [B G, S_q, H/G, d_rope];
+ *   2. mla_decode_paged (view shape) with q_lat = q_cat, q_rope = q_rope_g,
+ *      c_kv = the records, k_rope = c_kv + (d_nope + d_v) elements, the
+ *      per-stream block table and seq_lens (each sequence's length repeated
+ *      for its G streams); the scores are exactly q_nope . K_nope + q_rope . k_rope;
+ *   3. mla_combine_lse (view shape) -> o_lat fp32 [B G, S_q, H/G, d_nope + d_v]
+ *      and lse fp32 [B G, S_q, H/G]: the last d_v columns of o_lat are sum_t p_t V_t;
+ *   4. mla_gqa_output -- out[b, t, h, :] = o_lat[s, t, j, d_nope:] in
+ *      shape->out_dtype, lse[b, t, h] = lse_g[s, t, j] (fp32 [B, S_q, H]).
+ * `shape` here is the model's (batch B, num_heads H, q_len, d_nope, d_rope,
+ * d_v); `groups` must divide H and B G <= 1024.  All tensors are device
+ * pointers; q_nope, q_rope, q_cat, q_rope_g, o_lat and out 16-byte aligned.
+ */
+mla_status_t mla_gqa_queries(const mla_shape_t* shape, int32_t groups, const void* q_nope, const void* q_rope,
+                             void* q_cat, void* q_rope_g, hipStream_t stream);
+mla_status_t mla_gqa_output(const mla_shape_t* shape, int32_t groups, const float* o_lat, const float* lse_g,
+                            void* out, float* lse, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* mla_status_string(mla_status_t status);
 

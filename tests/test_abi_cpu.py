@@ -24,6 +24,7 @@ def test_exports_every_declared_symbol():
                              "mla_up_v", "mla_combine_up_v", "mla_append_kv", "mla_append_kv_workspace_bytes",
                              "mla_prefill_workspace_bytes", "mla_prefill_kv_elems", "mla_prefill_kv", "mla_prefill_attention",
                              "mla_tpla_split_weights", "mla_tpla_rotate_cache", "mla_tpla_reduce",
+                             "mla_gqa_queries", "mla_gqa_output",
                              "mla_status_string", "mla_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", mla.library_path], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -252,3 +253,19 @@ def test_tpla_argument_checks():
     assert red(sh, n=0) == mla.MLA_ERR_INVALID_ARG
     assert red(sh, parts=None) == mla.MLA_ERR_INVALID_ARG
     assert red(sh, parts=FAKE + 4) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_gqa_argument_checks():
+    lib = _lib()
+    q = lambda shp, g=4, **kw: lib.mla_gqa_queries(ctypes.byref(shp), g, kw.get("qn", FAKE), FAKE, FAKE,
+                                                   kw.get("qr", FAKE), None)
+    o = lambda shp, g=4, **kw: lib.mla_gqa_output(ctypes.byref(shp), g, FAKE, FAKE, kw.get("out", FAKE), FAKE, None)
+    sh = _shape()                                              # 16 heads
+    assert q(sh, g=3) == mla.MLA_ERR_INVALID_ARG                # 16 heads do not split into 3 groups
+    assert q(sh, g=0) == mla.MLA_ERR_INVALID_ARG
+    assert q(_shape(d_v=64)) == mla.MLA_ERR_UNSUPPORTED         # d_nope + d_v = 192: no decode of that width
+    assert q(_shape(batch=300), g=4) == mla.MLA_ERR_UNSUPPORTED  # 1200 streams
+    assert q(sh, qn=None) == mla.MLA_ERR_INVALID_ARG
+    assert q(sh, qr=FAKE + 2) == mla.MLA_ERR_INVALID_ARG
+    assert o(sh, out=None) == mla.MLA_ERR_INVALID_ARG
+    assert o(sh, out=FAKE + 8) == mla.MLA_ERR_INVALID_ARG
