@@ -356,6 +356,38 @@ def main():
     rot_bytes = 2 * plain.num_pages * w.block_size * w.d_latent * 2
     del plain
 
+    # GQLA's two decoding paths at s_q = 2 on a LLaMA-3-8B-shaped model
+    # (H = 32 in 8 groups, B = 16, context 8192): the absorbed MQA path over
+    # the latent and the GQA path over the per-group expanded cache, each
+    # call timed with events.
+    from head_latent_attention_absorbed_amd import GqaStep
+    from workloads import GQLA_GROUPS, make_gqa_inputs
+    gw = get_workload("gqla_gqa")
+    g_mla = DecodeStep(make_inputs(gw), partial=args.partial)
+    g_gqa = GqaStep(make_gqa_inputs(gw, GQLA_GROUPS), partial=args.partial)
+    for _ in range(2):
+        g_mla.run()
+        g_gqa.run()
+    torch.cuda.synchronize()
+    paths = {"mqa_absorb": (g_mla, ("absorb", "decode", "combine_up")),
+             "gqa": (g_gqa, ("queries", "decode", "combine", "output"))}
+    g_res = {}
+    for name, (st, calls) in paths.items():
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(KT)]
+        for i in range(KT):
+            ev[i][0].record(stream)
+            for j, c in enumerate(calls):
+                getattr(st, c)()
+                ev[i][j + 1].record(stream)
+        torch.cuda.synchronize()
+        g_res[name] = {c: float(np.median([e[j].elapsed_time(e[j + 1]) * 1e3 for e in ev])) for j, c in
+                       enumerate(calls)}
+        g_res[name]["step"] = float(np.median([e[0].elapsed_time(e[-1]) * 1e3 for e in ev]))
+    g_tokens = int(sum(int(x) for x in make_inputs(gw)["seq_lens"]))
+    g_bytes = {"mqa_absorb": g_tokens * gw.record_elems * 2,
+               "gqa": g_tokens * GQLA_GROUPS * (gw.d_nope + gw.d_v + gw.d_rope) * 2}
+    del g_mla, g_gqa
+
     us_step = ms_per_step * 1e3
     value = alg["cache_bytes"] / (us_step * 1e-6) / 1e12
     achieved = alg["decode_bytes"] / (dec_us * 1e-6) / 1e9
@@ -423,6 +455,14 @@ def main():
             "rotate_cache": {"us": round(rot_us, 2), "bytes": rot_bytes,
                              "achieved_gbs": round(rot_bytes / (rot_us * 1e-6) / 1e9, 1),
                              "frac": round(rot_bytes / (rot_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        },
+        "gqla": {
+            "what": "GQLA's two decoding paths at s_q = 2, H = 32 in 8 groups, B = 16, context 8192: absorbed MQA "
+                    "over the latent vs GQA over per-group [K_nope | V | k_rope] records",
+            "paths": {k: {"us_median": {c: round(t, 2) for c, t in v.items()}, "cache_bytes": g_bytes[k],
+                          "decode_gbs": round(g_bytes[k] / (v["decode"] * 1e-6) / 1e9, 1),
+                          "decode_frac": round(g_bytes[k] / (v["decode"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                      for k, v in g_res.items()},
         },
         "prefill": {
             "what": "mla_prefill_kv (K_nope, V per head from the records) + mla_prefill_attention (causal)",

@@ -6,7 +6,7 @@ per-token scale).  It holds none of the attention arithmetic, so both the
 CPU oracle and the HIP path can take their inputs from here without sharing
 any of the method's code.
 """
-from .configs import WORKLOADS, Workload, get_workload, prefill_workload, small_workload
+from .configs import GQLA_GROUPS, WORKLOADS, Workload, get_workload, prefill_workload, small_workload
 from .generate import (
     make_append_inputs,
     make_gqa_inputs,
@@ -18,6 +18,7 @@ from .generate import (
 )
 
 __all__ = [
+    "GQLA_GROUPS",
     "WORKLOADS",
     "Workload",
     "get_workload",
