@@ -175,11 +175,15 @@ struct Fp8Stage {
 // to the accumulator input of the next MFMA of the same chain; a VALU read of
 // the result needs wait states that the compiler cannot see through inline
 // asm, so every chain ends with mfma_v_drain before its values are used.
+// The other direction needs them too: an MFMA may read a VGPR only two wait
+// states after a VALU instruction wrote it, and the compiler may place such a
+// write (say a v_accvgpr_read bringing back an operand it parked in an AGPR)
+// right before the asm, so each MFMA here starts with s_nop 1.
 __device__ __forceinline__ void mfma_v_first(f32x16& acc, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_v_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_v_drain(f32x16& x) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
@@ -432,6 +436,8 @@ __device__ __forceinline__ void rescale(f32x16 (&O)[Geo<DC>::NB], float alpha) {
       O[nb][i] = x;
     }
   }
+  // an MFMA may read the accumulators two wait states after the last write
+  asm volatile("s_nop 1" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
