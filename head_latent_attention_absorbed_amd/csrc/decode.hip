@@ -872,10 +872,10 @@ prefill_kernel(PrefillParams p) {
     const uint32_t roff = (uint32_t)min(kt * kTile + rope_tok, L - 1) * rec + 16u * (dl >> 5);
 #pragma unroll
     for (int q = 0; q < NI; ++q) {
-      const int c = 4 * q + w;
-      if (c < 8) {
+      const int c = 4 * q + w;  // q 0, 1: key rows; 2: RoPE rows; 3, 4: value rows
+      if (q < 2) {
         lds_dma16(kbase + (int64_t)kt * 8192 + c * 1024, 16u * dl, dst + c * 1024);
-      } else if (c < 12) {
+      } else if (q == 2) {
         lds_dma16(rbase + 32 * (c - 8), roff, dst + c * 1024);
       } else {
         lds_dma16(vbase + (int64_t)kt * 8192 + (c - 12) * 1024, 16u * dl, dst + c * 1024);
@@ -910,24 +910,34 @@ prefill_kernel(PrefillParams p) {
   float m_run = -__builtin_inff(), l_run = 0.0f;
   bf16x8 pf0, pf1;
   float alpha;
-  auto tile = [&](int kt, auto first_tag) {
+  auto tile = [&](int kt, auto first_tag, auto full_tag) {
     constexpr bool FIRST = decltype(first_tag)::value;
+    // FULL: the tile lies wholly below the group's first position, so every
+    // row sees all of it (no causal mask, and the softmax takes its
+    // branch-free form); a compile-time choice.
+    constexpr bool FULL = decltype(full_tag)::value;
     // tile kt has landed (for every wave) and slot (kt - 1) % NBUF is free
     if (kt + kPfBuf - 2 < nkt) vm_wait<(kPfBuf - 2) * NI>(); else vm_wait<0>();
     block_sync();
     if (kt + kPfBuf - 1 < nkt) issue(kt + kPfBuf - 1, (kt + kPfBuf - 1) % kPfBuf);
     const char* tb = tiles + (kt % kPfBuf) * TB;
-    // fully visible to every row of the group: below its first position
-    const bool full = (kt + 1) * kTile <= q0;
-    score_tile<128, false, 0>(tb, nullptr, qf, m_run, l_run, kt * kTile, limit, full, p.scale_log2, pf0, pf1,
+    score_tile<128, false, 0>(tb, nullptr, qf, m_run, l_run, kt * kTile, limit, FULL, p.scale_log2, pf0, pf1,
                               alpha, NoDma{});
     if constexpr (!FIRST) {
       if (__any(alpha != 1.0f)) rescale<128>(O, alpha);
     }
     pv_tile<128, kPvAhead, FIRST>(tb + KROWS * kRow, pf0, pf1, O);
   };
-  tile(0, std::true_type{});
-  for (int kt = 1; kt < nkt; ++kt) tile(kt, std::false_type{});
+  // Key tiles 0 .. kfull - 1 lie below the group's first position q0.
+  const int kfull = min(nkt, q0 / kTile);
+  int kt = 1;
+  if (kfull > 0) {
+    tile(0, std::true_type{}, std::true_type{});
+    for (; kt < kfull; ++kt) tile(kt, std::false_type{}, std::true_type{});
+  } else {
+    tile(0, std::true_type{}, std::false_type{});
+  }
+  for (; kt < nkt; ++kt) tile(kt, std::false_type{}, std::false_type{});
 
   // Normalise and write this wave's rows: lane (col, half) holds row `col`,
   // columns 32 nb + 8 (i / 4) + 4 half + i % 4 of block nb.
