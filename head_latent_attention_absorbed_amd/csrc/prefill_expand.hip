@@ -13,11 +13,12 @@
 // the prefill attention copies straight into LDS, so every store is a
 // contiguous 512-byte run per wave.
 //
-// A work-group owns one (head, keys|values) pair: each of its four waves keeps
-// its 32 rows of W^T in registers for the whole launch and streams 32-position
-// tiles of records, which are copied into a four-slot LDS ring with
-// global->LDS DMA (three tiles in flight) in the decode's granule-major
-// layout, so the B-operand reads are conflict-free.  Only the tiles that hold
+// A work-group owns one head, keys and values: each of its eight waves (two
+// per SIMD) keeps its 32 rows of one W^T in registers for the whole launch
+// and streams 32-position tiles of records, which are copied into a
+// four-slot LDS ring with global->LDS DMA (three tiles in flight) in the
+// decode's granule-major layout, so the B-operand reads are conflict-free.
+// Serving keys and values from one copy halves the re-reads of the records.  Only the tiles that hold
 // positions < L_b are computed; positions L_b..end of the last one are
 // written as zeros, and tiles past it are not written.
 #include "mla_device.h"
@@ -28,22 +29,24 @@ namespace {
 
 constexpr int kXBuf = 4;  // ring slots
 
+constexpr int kXWaves = 8;  // four for keys, four for values
+
 template <int DC>
-__global__ void __launch_bounds__(256) expand_kernel(ExpandParams p) {
+__global__ void __launch_bounds__(kXWaves * 64) expand_kernel(ExpandParams p) {
   constexpr int KS = DC / 16;        // 16-deep k-steps
   constexpr int ROWS = DC / 8;       // granule rows of a record tile
   constexpr int TBX = ROWS * kRow;   // bytes of one ring slot
-  constexpr int NI = ROWS / 8;       // DMA instructions per wave per tile (2 rows each, 4 waves)
+  constexpr int NI = ROWS / (2 * kXWaves);  // DMA instructions per wave per tile (2 rows each)
   __shared__ __attribute__((aligned(1024))) char ring[kXBuf * TBX];
   // Lengths clamped to [0, P], read from LDS inside the loop: a global load
   // there would make the compiler wait for every ring copy in flight.
   __shared__ int lens[kMaxBatch];
 
-  const int w = uniform(threadIdx.x >> 6);
+  const int wv = uniform(threadIdx.x >> 6);
   const int lane = opaque_lane();
-  const int hk = blockIdx.x % (2 * p.H);
-  const int split = blockIdx.x / (2 * p.H);
-  const int h = hk >> 1, kind = hk & 1;
+  const int h = blockIdx.x % p.H;
+  const int split = blockIdx.x / p.H;
+  const int kind = wv >> 2, w = wv & 3;  // keys or values; this wave's 32 of the 128 rows
   const int T = (p.P + kTile - 1) / kTile;
 
   // This wave's rows of W^T: dim 32 w + lane % 32, k = 16 ks + 8 (lane / 32).
@@ -55,14 +58,14 @@ __global__ void __launch_bounds__(256) expand_kernel(ExpandParams p) {
     for (int ks = 0; ks < KS; ++ks) wf[ks] = *(const bf16x8*)(wsrc + 16 * ks);
   }
 
-  for (int b = threadIdx.x; b < p.B; b += 256) lens[b] = min(max(p.seq_lens[b], 0), p.P);
+  for (int b = threadIdx.x; b < p.B; b += kXWaves * 64) lens[b] = min(max(p.seq_lens[b], 0), p.P);
   __syncthreads();
 
   // The tiles to compute, over all sequences: tile j of sequence b while
   // 32 j < L_b.  This work-group takes a contiguous share of them.
   int ntot = 0;
   for (int b = 0; b < p.B; ++b) ntot += (lens[b] + kTile - 1) / kTile;
-  const int ns = gridDim.x / (2 * p.H);
+  const int ns = gridDim.x / p.H;
   const int f0 = (int)((int64_t)ntot * split / ns), f1 = (int)((int64_t)ntot * (split + 1) / ns);
   if (f0 >= f1) return;
 
@@ -96,15 +99,15 @@ __global__ void __launch_bounds__(256) expand_kernel(ExpandParams p) {
 
   const uint32_t rec = (uint32_t)(DC + 64) * 2;
   const uint32_t ring_lds = lds_offset(ring);
-  // Tile (b, j) into ring slot s: instruction q of wave w fills granule rows
-  // 2 (4 q + w) and +1; lane l brings position 32 j + (l % 32 ^ 4 (l / 32)).
+  // Tile (b, j) into ring slot s: instruction q of wave wv fills granule rows
+  // 2 (8 q + wv) and +1; lane l brings position 32 j + (l % 32 ^ 4 (l / 32)).
   const int slot_tok = (lane & 31) ^ (4 * (lane >> 5));
   auto issue = [&](const Cursor& c, int s) {
     const char* base = (const char*)(p.ckr + (int64_t)c.b * p.P * (DC + 64));
     const uint32_t voff = (uint32_t)min(c.j * kTile + slot_tok, c.L - 1) * rec + 16u * (lane >> 5);
 #pragma unroll
     for (int q = 0; q < NI; ++q) {
-      const int g0 = 2 * (4 * q + w);
+      const int g0 = 2 * (kXWaves * q + wv);
       lds_dma16(base + 16 * g0, voff, ring_lds + s * TBX + g0 * kRow);
     }
   };
@@ -160,10 +163,9 @@ __global__ void __launch_bounds__(256) expand_kernel(ExpandParams p) {
 
 template <int DC>
 hipError_t launch_dc(const ExpandParams& p, hipStream_t stream) {
-  // Enough (head, kind, share) work-groups to give every CU one.
-  const int pairs = 2 * p.H;
-  const int ns = (256 + pairs - 1) / pairs;
-  hipLaunchKernelGGL(expand_kernel<DC>, dim3(pairs * ns), dim3(256), 0, stream, p);
+  // Enough (head, share) work-groups to give every CU one.
+  const int ns = (256 + p.H - 1) / p.H;
+  hipLaunchKernelGGL(expand_kernel<DC>, dim3(p.H * ns), dim3(kXWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 
