@@ -846,9 +846,16 @@ prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) char tiles[kPfBuf * TB];
 
   const int w = uniform(threadIdx.x >> 6);
-  const int b = blockIdx.z, h = blockIdx.y;
+  // XCD-aware placement: work item u = (sequence, head, query tile), longest
+  // rows first; the grid (a multiple of 8) is dealt so that consecutive work
+  // items land on the same XCD, which keeps each head's keys and values in
+  // one L2 while its query tiles, all starting from key tile 0, re-read them.
   const int ntile = (p.P + kPfRows - 1) / kPfRows;
-  const int qt = ntile - 1 - (int)blockIdx.x;  // longest rows first
+  const int u = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
+  if (u >= ntile * p.H * p.B) return;
+  const int pair = u / ntile;
+  const int b = pair / p.H, h = pair % p.H;
+  const int qt = ntile - 1 - u % ntile;  // longest rows first
   const int L = min(p.seq_lens[b], p.P);
   const int q0 = qt * kPfRows;
   if (q0 >= L) return;
@@ -980,7 +987,8 @@ hipError_t launch_decode(const DecodeParams& p, int d_latent, bool fp8, hipStrea
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   if (p.B <= 0 || p.P <= 0) return hipSuccess;
-  const dim3 grid((p.P + kPfRows - 1) / kPfRows, p.H, p.B);
+  const int64_t items = (int64_t)((p.P + kPfRows - 1) / kPfRows) * p.H * p.B;
+  const dim3 grid((unsigned)((items + 7) / 8 * 8));
   hipLaunchKernelGGL(prefill_kernel, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
