@@ -60,7 +60,7 @@ def algorithmic(w, seq_lens):
                 step_flops=attn_flops + proj_flops, record_bytes=rec, tokens=sum(L))
 
 
-KERNEL_SOURCES = ("decode.hip", "mla_device.h", "mla_kernels.h")
+KERNEL_SOURCES = ("decode.hip", "tile_ops.h", "mla_device.h", "mla_kernels.h")
 
 
 def kernel_source_hash() -> str:

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmla_absorbed.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["decode.hip", "combine.hip", "head_gemm.hip", "append.hip", "prefill_expand.hip", "tpla.hip", "gqa.hip", "mla_api.cpp"]
+SOURCES = ["decode.hip", "combine.hip", "head_gemm.hip", "append.hip", "prefill.hip", "prefill_expand.hip", "tpla.hip", "gqa.hip", "mla_api.cpp"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
