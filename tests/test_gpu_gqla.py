@@ -51,3 +51,16 @@ def test_gqa_path_full_workload_sampled():
     ref = oracle.gqa_decode(gi, batches=batches, heads=heads)
     tol_abs, tol_rel = tolerances(w)
     compare("out sampled", out[batches][:, :, heads], ref["out"], tol_abs, tol_rel)
+
+
+def test_gqa_path_fp32_out():
+    from dataclasses import replace
+
+    w = replace(SMALL, out_dtype="fp32")
+    gi = make_gqa_inputs(w, 8)
+    print("[case] gqa path fp32 out", flush=True)
+    st = _run(gi)
+    assert str(st.out.dtype) == "torch.float32"
+    ref = oracle.gqa_decode(gi)
+    tol_abs, tol_rel = tolerances(w)
+    compare("out", to_np(st.out), ref["out"], tol_abs, tol_rel)

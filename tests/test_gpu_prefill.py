@@ -18,6 +18,8 @@ CASES = {
     "h8_idle": (small_workload("deepseek_v3", batch=2, heads=8, seq_len=(1, 97), forced_lens=(0, 97)), 97),
     "dc256_h16": (small_workload("tpla_shard", batch=2, heads=16, seq_len=(33, 160), forced_lens=(160, 33)), 160),
     "h128_p96": (small_workload("deepseek_v3", batch=1, heads=128, seq_len=(96, 96)), 96),
+    # a prompt shorter than one key tile, and single-position prompts
+    "h8_p20": (small_workload("deepseek_v3", batch=3, heads=8, seq_len=(1, 20), forced_lens=(20, 1, 13)), 20),
 }
 
 

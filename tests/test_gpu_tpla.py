@@ -147,3 +147,19 @@ def test_tpla_headline_sampled():
     ref = oracle.tpla_decode(inputs, 2, True, batches=batches, heads=heads)
     tol_abs, tol_rel = tolerances(w)
     compare("out sampled", out[batches][:, :, heads], ref["out"], 2 * tol_abs, 2 * tol_rel)
+
+
+def test_tpla_fp8_cache_plain_split():
+    """The split in the plain basis over an e4m3 cache (per-token scales apply
+    to the whole record, so every shard's slice keeps its token's scale)."""
+    import torch
+
+    w = small_workload("kimi_k2_fp8", batch=3, heads=16, seq_len=(4, 200), max_seq_len=256, forced_lens=(200, 4, 0))
+    inputs = make_inputs(w)
+    print(f"[case] tpla fp8 plain lens={list(inputs['seq_lens'])}", flush=True)
+    st = _step(inputs, 2, False)
+    st.run()
+    torch.cuda.synchronize()
+    ref = oracle.tpla_decode(inputs, 2, False)
+    tol_abs, tol_rel = tolerances(w)
+    compare("out", to_np(st.out), ref["out"], 2 * tol_abs, 2 * tol_rel)
