@@ -130,6 +130,156 @@ def cpu_baseline(inputs, budget_s: float):
     return dict(value=tokens * rec / dt / 1e12, unit="TB/s", seconds=dt, sequences=done, tokens=tokens)
 
 
+def leg_prefill(torch, np, stream, K):
+    """The MLA-form prefill of a prompt batch (keys and values expanded per
+    head, then causal attention), each call timed with events."""
+    from head_latent_attention_absorbed_amd import PrefillStep
+    from workloads import make_prefill_inputs, prefill_workload
+    pw, P = prefill_workload()
+    pf = make_prefill_inputs(pw, P)
+    pst = PrefillStep(pf)
+    for _ in range(2):
+        pst.run()
+    torch.cuda.synchronize()
+    KP = max(3, min(K, 10))
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(KP)]
+    for i in range(KP):
+        pev[i][0].record(stream)
+        pst.kv()
+        pev[i][1].record(stream)
+        pst.attention()
+        pev[i][2].record(stream)
+    torch.cuda.synchronize()
+    pkv_us = float(np.median([e[0].elapsed_time(e[1]) * 1e3 for e in pev]))
+    pat_us = float(np.median([e[1].elapsed_time(e[2]) * 1e3 for e in pev]))
+    plens = [int(v) for v in pf["seq_lens"]]
+    p_tokens = sum(plens)
+    p_attn_flops = pw.heads * (pw.d_nope + pw.d_rope + pw.d_v) * 2 * sum(L * (L + 1) // 2 for L in plens)
+    p_kv_flops = p_tokens * pw.heads * pw.d_latent * (pw.d_nope + pw.d_v) * 2
+    return {
+        "what": "mla_prefill_kv (K_nope, V per head from the records) + mla_prefill_attention (causal)",
+        "workload": pw.name, "batch": pw.batch, "prompt_len": P, "seq_lens": plens, "heads": pw.heads,
+        "tokens_per_s": round(p_tokens / ((pkv_us + pat_us) * 1e-6), 1),
+        "kv_us_median": round(pkv_us, 2),
+        "attention_us_median": round(pat_us, 2),
+        "roofline": {"kernel": "prefill_kernel (mla_prefill_attention)", "bound": "mfma",
+                     "achieved": round(p_attn_flops / (pat_us * 1e-6) / 1e12, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(p_attn_flops / (pat_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "algorithmic_flops_per_launch": p_attn_flops},
+        "kv_roofline": {"bound": "mfma", "achieved": round(p_kv_flops / (pkv_us * 1e-6) / 1e12, 1),
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(p_kv_flops / (pkv_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "algorithmic_flops_per_call": p_kv_flops},
+    }
+
+
+def leg_tpla(torch, np, stream, K, args, w, inputs, alg, step0):
+    """The TPLA latent split on one device: two Hadamard-basis shards of the
+    measured decode (each over half the latent and the whole RoPE key),
+    summed; each call timed with events, and the split's error against the
+    MLA decode on the same inputs with and without the basis change."""
+    from head_latent_attention_absorbed_amd import TplaStep, combine_up_supported, mla_tpla_rotate_cache
+    if w.cache_dtype != "bf16" or not combine_up_supported(w.d_latent // 2, w.d_v):
+        return None
+    step0.run()
+    torch.cuda.synchronize()
+    mla_out = step0.out.float().clone()
+    tp_err, tst, plain = {}, None, None
+    for had in (False, True):
+        t = TplaStep(inputs, 2, had, partial=args.partial)
+        t.prepare()
+        t.run()
+        torch.cuda.synchronize()
+        tp_err["hadamard" if had else "plain"] = float((t.out.float() - mla_out).norm() / mla_out.norm())
+        if had:
+            tst = t
+        else:
+            plain = t
+    KT = max(3, min(K, 10))
+    names = ("absorb", "decode", "combine_up")
+    tev = [[torch.cuda.Event(enable_timing=True) for _ in range(3 * tst.n + 2)] for _ in range(KT)]
+    for i in range(KT):
+        e = tev[i]
+        e[0].record(stream)
+        for sh in range(tst.n):
+            for j, nm in enumerate(names):
+                getattr(tst, nm)(sh)
+                e[1 + 3 * sh + j].record(stream)
+        tst.reduce()
+        e[-1].record(stream)
+    torch.cuda.synchronize()
+    tp_step = float(np.median([e[0].elapsed_time(e[-1]) * 1e3 for e in tev]))
+    tp_dec = float(np.median([e[1 + 3 * sh].elapsed_time(e[2 + 3 * sh]) * 1e3 for e in tev for sh in range(tst.n)]))
+    sh_bytes = alg["tokens"] * (tst.dcs + w.d_rope) * 2 + w.batch * w.q_len * w.heads * (tst.dcs + w.d_rope) * 2
+    # the basis change of the whole cache (latent of every slot, read and written once)
+    rev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    b0 = plain.base
+    for i in range(3):
+        rev[i].record(stream)
+        mla_tpla_rotate_cache(b0.shape, b0.cache, b0.token_stride, b0.block_stride, plain.num_pages)
+    rev[3].record(stream)
+    torch.cuda.synchronize()
+    rot_us = float(np.median([rev[i].elapsed_time(rev[i + 1]) * 1e3 for i in range(3)]))
+    rot_bytes = 2 * plain.num_pages * w.block_size * w.d_latent * 2
+    return {
+        "what": "TPLA latent split on one GPU: 2 Hadamard-basis shards (absorb + decode + merge/up-proj "
+                "at d_c/2 each) + mla_tpla_reduce",
+        "n_shards": tst.n, "us_per_step": round(tp_step, 2), "shard_decode_us_median": round(tp_dec, 2),
+        "rel_l2_vs_mla": {k: round(v, 5) for k, v in tp_err.items()},
+        "roofline": {"kernel": "decode_kernel (one shard, d_latent %d)" % tst.dcs, "bound": "hbm",
+                     "achieved": round(sh_bytes / (tp_dec * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(sh_bytes / (tp_dec * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_launch": sh_bytes},
+        "rotate_cache": {"us": round(rot_us, 2), "bytes": rot_bytes,
+                         "achieved_gbs": round(rot_bytes / (rot_us * 1e-6) / 1e9, 1),
+                         "frac": round(rot_bytes / (rot_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+
+
+def leg_gqla(torch, np, stream, K, args):
+    """GQLA's two decoding paths at s_q = 2 on a LLaMA-3-8B-shaped model
+    (H = 32 in 8 groups, B = 16, context 8192): the absorbed MQA path over the
+    latent and the GQA path over the per-group expanded cache, each call
+    timed with events."""
+    from head_latent_attention_absorbed_amd import DecodeStep, GqaStep
+    from workloads import GQLA_GROUPS, get_workload, make_gqa_inputs, make_inputs
+    gw = get_workload("gqla_gqa")
+    g_in = make_inputs(gw)
+    g_mla = DecodeStep(g_in, partial=args.partial)
+    g_gqa = GqaStep(make_gqa_inputs(gw, GQLA_GROUPS), partial=args.partial)
+    for _ in range(2):
+        g_mla.run()
+        g_gqa.run()
+    torch.cuda.synchronize()
+    KT = max(3, min(K, 10))
+    paths = {"mqa_absorb": (g_mla, ("absorb", "decode", "combine_up")),
+             "gqa": (g_gqa, ("queries", "decode", "combine", "output"))}
+    g_res = {}
+    for name, (st, calls) in paths.items():
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(KT)]
+        for i in range(KT):
+            ev[i][0].record(stream)
+            for j, c in enumerate(calls):
+                getattr(st, c)()
+                ev[i][j + 1].record(stream)
+        torch.cuda.synchronize()
+        g_res[name] = {c: float(np.median([e[j].elapsed_time(e[j + 1]) * 1e3 for e in ev])) for j, c in
+                       enumerate(calls)}
+        g_res[name]["step"] = float(np.median([e[0].elapsed_time(e[-1]) * 1e3 for e in ev]))
+    g_tokens = int(sum(int(x) for x in g_in["seq_lens"]))
+    g_bytes = {"mqa_absorb": g_tokens * gw.record_elems * 2,
+               "gqa": g_tokens * GQLA_GROUPS * (gw.d_nope + gw.d_v + gw.d_rope) * 2}
+    return {
+        "what": "GQLA's two decoding paths at s_q = 2, H = 32 in 8 groups, B = 16, context 8192: absorbed MQA "
+                "over the latent vs GQA over per-group [K_nope | V | k_rope] records",
+        "paths": {k: {"us_median": {c: round(t, 2) for c, t in v.items()}, "cache_bytes": g_bytes[k],
+                      "decode_gbs": round(g_bytes[k] / (v["decode"] * 1e-6) / 1e9, 1),
+                      "decode_frac": round(g_bytes[k] / (v["decode"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                  for k, v in g_res.items()},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +297,9 @@ def main():
     ap.add_argument("--graph-steps", type=int, default=0,
                     help="steps per graph replay (consecutive replicas, like the layers of one forward "
                          "pass); 0 = all replicas, 1 = one step per replay")
+    ap.add_argument("--legs", dest="legs", action="store_true", default=None,
+                    help="also time the prefill, TPLA-split and GQLA legs (default: with the headline workload)")
+    ap.add_argument("--decode-only", dest="legs", action="store_false", help="time the decode step only")
     ap.add_argument("--unfused", action="store_true",
                     help="merge (mla_combine_lse) and up-project (mla_up_v) in two launches")
     args = ap.parse_args()
@@ -281,112 +434,10 @@ def main():
     M = w.batch * w.q_len
     app_bytes = w.d_model * (w.d_latent + w.d_rope) * 2 + M * w.d_model * 2 + M * alg["record_bytes"]
 
-    # The MLA-form prefill of a prompt batch (keys and values expanded per
-    # head, then causal attention), timed on its own: events around each call.
-    from head_latent_attention_absorbed_amd import PrefillStep
-    from workloads import make_prefill_inputs, prefill_workload
-    pw, P = prefill_workload()
-    pf = make_prefill_inputs(pw, P)
-    pst = PrefillStep(pf)
-    for _ in range(2):
-        pst.run()
-    torch.cuda.synchronize()
-    KP = max(3, min(K, 10))
-    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(KP)]
-    for i in range(KP):
-        pev[i][0].record(stream)
-        pst.kv()
-        pev[i][1].record(stream)
-        pst.attention()
-        pev[i][2].record(stream)
-    torch.cuda.synchronize()
-    pkv_us = float(np.median([e[0].elapsed_time(e[1]) * 1e3 for e in pev]))
-    pat_us = float(np.median([e[1].elapsed_time(e[2]) * 1e3 for e in pev]))
-    plens = [int(v) for v in pf["seq_lens"]]
-    p_tokens = sum(plens)
-    p_attn_flops = pw.heads * (pw.d_nope + pw.d_rope + pw.d_v) * 2 * sum(L * (L + 1) // 2 for L in plens)
-    p_kv_flops = p_tokens * pw.heads * pw.d_latent * (pw.d_nope + pw.d_v) * 2
-    del pst
-
-    # The TPLA latent split on one device: two Hadamard-basis shards of the
-    # same decode (each over half the latent and the whole RoPE key), summed.
-    # Each call is timed with events; the split's error against the MLA
-    # decode is measured on the same inputs, with and without the basis change.
-    from head_latent_attention_absorbed_amd import TplaStep
-    steps[0].run()
-    torch.cuda.synchronize()
-    mla_out = steps[0].out.float().clone()
-    tp_err, tst = {}, None
-    for had in (False, True):
-        t = TplaStep(inputs, 2, had, partial=args.partial)
-        t.prepare()
-        t.run()
-        torch.cuda.synchronize()
-        tp_err["hadamard" if had else "plain"] = float((t.out.float() - mla_out).norm() / mla_out.norm())
-        if had:
-            tst = t
-        else:
-            plain = t
-    KT = max(3, min(K, 10))
-    names = ("absorb", "decode", "combine_up")
-    tev = [[torch.cuda.Event(enable_timing=True) for _ in range(3 * tst.n + 2)] for _ in range(KT)]
-    for i in range(KT):
-        e = tev[i]
-        e[0].record(stream)
-        for sh in range(tst.n):
-            for j, nm in enumerate(names):
-                getattr(tst, nm)(sh)
-                e[1 + 3 * sh + j].record(stream)
-        tst.reduce()
-        e[-1].record(stream)
-    torch.cuda.synchronize()
-    tp_step = float(np.median([e[0].elapsed_time(e[-1]) * 1e3 for e in tev]))
-    tp_dec = float(np.median([e[1 + 3 * sh].elapsed_time(e[2 + 3 * sh]) * 1e3 for e in tev for sh in range(tst.n)]))
-    sh_bytes = alg["tokens"] * (tst.dcs + w.d_rope) * 2 + w.batch * w.q_len * w.heads * (tst.dcs + w.d_rope) * 2
-    # the basis change of the whole cache (latent of every slot, read and written once)
-    rev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    from head_latent_attention_absorbed_amd import mla_tpla_rotate_cache
-    b0 = plain.base
-    for i in range(3):
-        rev[i].record(stream)
-        mla_tpla_rotate_cache(b0.shape, b0.cache, b0.token_stride, b0.block_stride, plain.num_pages)
-    rev[3].record(stream)
-    torch.cuda.synchronize()
-    rot_us = float(np.median([rev[i].elapsed_time(rev[i + 1]) * 1e3 for i in range(3)]))
-    rot_bytes = 2 * plain.num_pages * w.block_size * w.d_latent * 2
-    del plain
-
-    # GQLA's two decoding paths at s_q = 2 on a LLaMA-3-8B-shaped model
-    # (H = 32 in 8 groups, B = 16, context 8192): the absorbed MQA path over
-    # the latent and the GQA path over the per-group expanded cache, each
-    # call timed with events.
-    from head_latent_attention_absorbed_amd import GqaStep
-    from workloads import GQLA_GROUPS, make_gqa_inputs
-    gw = get_workload("gqla_gqa")
-    g_mla = DecodeStep(make_inputs(gw), partial=args.partial)
-    g_gqa = GqaStep(make_gqa_inputs(gw, GQLA_GROUPS), partial=args.partial)
-    for _ in range(2):
-        g_mla.run()
-        g_gqa.run()
-    torch.cuda.synchronize()
-    paths = {"mqa_absorb": (g_mla, ("absorb", "decode", "combine_up")),
-             "gqa": (g_gqa, ("queries", "decode", "combine", "output"))}
-    g_res = {}
-    for name, (st, calls) in paths.items():
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(KT)]
-        for i in range(KT):
-            ev[i][0].record(stream)
-            for j, c in enumerate(calls):
-                getattr(st, c)()
-                ev[i][j + 1].record(stream)
-        torch.cuda.synchronize()
-        g_res[name] = {c: float(np.median([e[j].elapsed_time(e[j + 1]) * 1e3 for e in ev])) for j, c in
-                       enumerate(calls)}
-        g_res[name]["step"] = float(np.median([e[0].elapsed_time(e[-1]) * 1e3 for e in ev]))
-    g_tokens = int(sum(int(x) for x in make_inputs(gw)["seq_lens"]))
-    g_bytes = {"mqa_absorb": g_tokens * gw.record_elems * 2,
-               "gqa": g_tokens * GQLA_GROUPS * (gw.d_nope + gw.d_v + gw.d_rope) * 2}
-    del g_mla, g_gqa
+    run_legs = args.legs if args.legs is not None else (args.workload == "deepseek_v3")
+    prefill_res = leg_prefill(torch, np, stream, K) if run_legs else None
+    tpla_res = leg_tpla(torch, np, stream, K, args, w, inputs, alg, steps[0]) if run_legs else None
+    gqla_res = leg_gqla(torch, np, stream, K, args) if run_legs else None
 
     us_step = ms_per_step * 1e3
     value = alg["cache_bytes"] / (us_step * 1e-6) / 1e12
@@ -443,43 +494,9 @@ def main():
                          "frac": round(app_bytes / (app_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                          "algorithmic_bytes_per_call": app_bytes},
         },
-        "tpla": {
-            "what": "TPLA latent split on one GPU: 2 Hadamard-basis shards (absorb + decode + merge/up-proj "
-                    "at d_c/2 each) + mla_tpla_reduce",
-            "n_shards": tst.n, "us_per_step": round(tp_step, 2), "shard_decode_us_median": round(tp_dec, 2),
-            "rel_l2_vs_mla": {k: round(v, 5) for k, v in tp_err.items()},
-            "roofline": {"kernel": "decode_kernel (one shard, d_latent 256)", "bound": "hbm",
-                         "achieved": round(sh_bytes / (tp_dec * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(sh_bytes / (tp_dec * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                         "algorithmic_bytes_per_launch": sh_bytes},
-            "rotate_cache": {"us": round(rot_us, 2), "bytes": rot_bytes,
-                             "achieved_gbs": round(rot_bytes / (rot_us * 1e-6) / 1e9, 1),
-                             "frac": round(rot_bytes / (rot_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
-        },
-        "gqla": {
-            "what": "GQLA's two decoding paths at s_q = 2, H = 32 in 8 groups, B = 16, context 8192: absorbed MQA "
-                    "over the latent vs GQA over per-group [K_nope | V | k_rope] records",
-            "paths": {k: {"us_median": {c: round(t, 2) for c, t in v.items()}, "cache_bytes": g_bytes[k],
-                          "decode_gbs": round(g_bytes[k] / (v["decode"] * 1e-6) / 1e9, 1),
-                          "decode_frac": round(g_bytes[k] / (v["decode"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-                      for k, v in g_res.items()},
-        },
-        "prefill": {
-            "what": "mla_prefill_kv (K_nope, V per head from the records) + mla_prefill_attention (causal)",
-            "workload": pw.name, "batch": pw.batch, "prompt_len": P, "seq_lens": plens, "heads": pw.heads,
-            "tokens_per_s": round(p_tokens / ((pkv_us + pat_us) * 1e-6), 1),
-            "kv_us_median": round(pkv_us, 2),
-            "attention_us_median": round(pat_us, 2),
-            "roofline": {"kernel": "prefill_kernel (mla_prefill_attention)", "bound": "mfma",
-                         "achieved": round(p_attn_flops / (pat_us * 1e-6) / 1e12, 1),
-                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(p_attn_flops / (pat_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "algorithmic_flops_per_launch": p_attn_flops},
-            "kv_roofline": {"bound": "mfma", "achieved": round(p_kv_flops / (pkv_us * 1e-6) / 1e12, 1),
-                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": round(p_kv_flops / (pkv_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                            "algorithmic_flops_per_call": p_kv_flops},
-        },
+        "tpla": tpla_res,
+        "gqla": gqla_res,
+        "prefill": prefill_res,
     }
     if args.copy_probe_mb > 0:
         copy_probe(args.copy_probe_mb)

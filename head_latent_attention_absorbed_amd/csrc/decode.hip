@@ -116,42 +116,59 @@ __device__ __forceinline__ void zero_tail(char* tb, int nv, int tid) {
   }
 }
 
-// fp8 tile: 8 e4m3 bytes per bf16 granule, loaded into registers, decoded
-// exactly (every e4m3 value is a bf16 value) and written to the same layout;
-// tokens past the length are written as zeros.
-template <int DC, int NW>
-struct Fp8Stage {
-  static constexpr int NI = Geo<DC>::GPT / (2 * NW);  // granules per lane
-  static constexpr int CH = NI < 9 ? NI : 9;          // granules kept in flight
-  uint2 v[CH];
-
-  __device__ __forceinline__ void load_chunk(const DecodeParams& p, const char* run, uint32_t lane_off8, int c0,
-                                             int w) {
-#pragma unroll
-    for (int q = 0; q < CH; ++q) {
-      const int qq = c0 + q;
-      if (qq < NI) {
-        const int g0 = 2 * (qq * NW + w);
-        v[q] = *(const uint2*)(run + granule_offset<DC, 8>(p, g0) + lane_off8);
-      }
-    }
-  }
-  __device__ __forceinline__ void store_chunk(char* buf, int c0, int w, int lane, bool valid) {
-#pragma unroll
-    for (int q = 0; q < CH; ++q) {
-      const int qq = c0 + q;
-      if (qq < NI) {
-        bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[q].x, 1.0f, false);
-        bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[q].x, 1.0f, true);
-        bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[q].y, 1.0f, false);
-        bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[q].y, 1.0f, true);
-        bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-        if (!valid) r = bf16x8{};
-        *(bf16x8*)(buf + (qq * NW + w) * 1024 + lane * 16) = r;
-      }
-    }
-  }
+// fp8 tile: the records' e4m3 bytes are copied with global->LDS DMA into a
+// staging slot (row pair m = bytes 16m..16m+15 of the latent, then of the
+// RoPE key, of token t at byte (32 m + t) * 16), so nothing is held in
+// registers while the previous tile is computed; then every thread decodes
+// its share exactly (every e4m3 value is a bf16 value) into the bf16 tile
+// layout, tokens past the length as zeros.
+template <int DC>
+struct Fp8Geo {
+  static constexpr int NP = Geo<DC>::GPT / 2;      // row pairs of a tile
+  static constexpr int NINS = NP / 2;              // DMA instructions (two pairs each)
+  static constexpr int BYTES = NP * kTile * 16;    // staging slot
 };
+
+template <int DC, int NW>
+__device__ __forceinline__ void issue_fp8_dma(const DecodeParams& p, const char* run, uint32_t stage_lds, int w) {
+  using F = Fp8Geo<DC>;
+  const int ol = opaque_lane();
+  const uint32_t lane_off = (uint32_t)(ol & 31) * (uint32_t)p.token_stride + 16u * (ol >> 5);
+#pragma unroll
+  for (int q = 0; q < (F::NINS + NW - 1) / NW; ++q) {
+    const int ins = q * NW + w;
+    if (ins < F::NINS) {
+      const int m0 = 2 * ins;  // pairs m0, m0 + 1 never straddle the latent and the RoPE key
+      const int64_t off = m0 < Geo<DC>::GC / 2 ? (int64_t)m0 * 16 : p.rope_off + (int64_t)(m0 - Geo<DC>::GC / 2) * 16;
+      lds_dma16(run + off, lane_off, uniform(stage_lds + ins * 1024));
+    }
+  }
+}
+
+template <int DC, int NW>
+__device__ __forceinline__ void convert_fp8_tile(const char* stage, char* tb, int nv, int tid) {
+  using F = Fp8Geo<DC>;
+  for (int i = tid; i < F::NP * kTile; i += NW * kWave) {
+    const int m = i >> 5, t = i & 31;
+    const uint4 x = *(const uint4*)(stage + i * 16);
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true);
+    const bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.z, 1.0f, false);
+    const bf16x2 f = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.z, 1.0f, true);
+    const bf16x2 g = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.w, 1.0f, false);
+    const bf16x2 h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.w, 1.0f, true);
+    bf16x8 lo = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};  // granule row 2m
+    bf16x8 hi = {e[0], e[1], f[0], f[1], g[0], g[1], h[0], h[1]};  // granule row 2m + 1
+    if (t >= nv) {
+      lo = bf16x8{};
+      hi = bf16x8{};
+    }
+    *(bf16x8*)(tb + (2 * m) * kRow + (t << 4)) = lo;            // even row: slot t
+    *(bf16x8*)(tb + (2 * m + 1) * kRow + ((t ^ 4) << 4)) = hi;  // odd row: slot t ^ 4
+  }
+}
 
 // Write NBK accumulator blocks (32 latent columns each, starting at element
 // offset `base` of o_part) scaled by inv, as fp16 or fp32.
@@ -257,6 +274,7 @@ __global__ void __launch_bounds__(NW * kWave)
 
   __shared__ __attribute__((aligned(1024))) char tiles[NBUF * TB];
   __shared__ __attribute__((aligned(16))) float tscale[FP8 ? NBUF * kTile : 4];
+  __shared__ __attribute__((aligned(1024))) char f8stage[FP8 ? Fp8Geo<DC>::BYTES : 16];
   __shared__ int cu[kMaxBatch + 1];
   __shared__ int4 tab[kTab];
 
@@ -340,28 +358,21 @@ __global__ void __launch_bounds__(NW * kWave)
     if (kl < k1) locate();
   };
 
-  Fp8Stage<DC, NW> stage;
-  auto stage_finish = [&]() {  // fp8: decode the loaded tile kl into its ring slot
+  // fp8: tile kl's bytes are copied into the staging slot (and its tokens'
+  // scales loaded) one tile ahead; stage_finish decodes them into its ring slot.
+  float f8_scale = 0.0f;
+  auto stage_start = [&]() {
+    issue_fp8_dma<DC, NW>(p, src, lds_offset(f8stage), w);
+    if (w == 0 && lane < kTile) f8_scale = kv_scale[(int64_t)spage * p.block_size + (spos & (p.block_size - 1)) + lane];
+  };
+  auto stage_finish = [&]() {
     const int nbuf = (kl - k0) % NBUF;
-    const int ol = opaque_lane();
-    const uint32_t lane_off8 = (uint32_t)load_token(ol) * (uint32_t)p.token_stride + 8u * (ol >> 5);
-    const bool valid = load_token(ol) < snv;
-    stage.store_chunk(tiles + nbuf * TB, 0, w, ol, valid);
-    for (int c0 = Fp8Stage<DC, NW>::CH; c0 < Fp8Stage<DC, NW>::NI; c0 += Fp8Stage<DC, NW>::CH) {
-      stage.load_chunk(p, src, lane_off8, c0, w);
-      stage.store_chunk(tiles + nbuf * TB, c0, w, ol, valid);
-    }
-    if (w == 0 && lane < kTile) {
-      const float sc = kv_scale[(int64_t)spage * p.block_size + (spos & (p.block_size - 1)) + lane];
-      tscale[nbuf * kTile + lane] = lane < snv ? sc : 0.0f;
-    }
+    vm_wait<0>();
+    block_sync();  // every wave's copies have landed
+    convert_fp8_tile<DC, NW>(f8stage, tiles + nbuf * TB, snv, tid);
+    if (w == 0 && lane < kTile) tscale[nbuf * kTile + lane] = lane < snv ? f8_scale : 0.0f;
     ++kl;
     if (kl < k1) locate();
-  };
-  auto stage_start = [&]() {
-    const int ol = opaque_lane();
-    const uint32_t lane_off8 = (uint32_t)load_token(ol) * (uint32_t)p.token_stride + 8u * (ol >> 5);
-    stage.load_chunk(p, src, lane_off8, 0, w);
   };
 
   if constexpr (FP8) {
@@ -470,7 +481,7 @@ __global__ void __launch_bounds__(NW * kWave)
     // every row sees in full run branch-free; then the masked tail.
     one_tile(std::true_type{}, std::false_type{});
     const int kfull = min(kend, cub + lim_all / kTile);
-    while (k < kfull) one_tile(std::false_type{}, std::integral_constant<bool, !FP8>{});
+    while (k < kfull) one_tile(std::false_type{}, std::true_type{});
     while (k < kend) one_tile(std::false_type{}, std::false_type{});
 
     // ---- normalise and write this (sequence, part) partial

@@ -107,10 +107,12 @@ __device__ __forceinline__ f32x16 score_mfma(const char* tb, const bf16x8 (&qf)[
 // maximum grew by more than 2^kRebase).  Lane (col, half) holds row `col`,
 // tokens 8(i/4) + 4 half + i%4 of the tile in value i.
 //
-// `full` (bf16 only, wave-uniform) says every position of the tile is visible
-// to every row: then the maximum is taken over the raw scores (the scale is
-// positive) and each weight is exp2(s * scale - m) with one fused
-// multiply-add, with no masking and no guard (m is finite), in 10 steps.
+// `full` (wave-uniform) says every position of the tile is visible to every
+// row: then the maximum is taken over the raw scores (the scale is positive)
+// and each weight is exp2(s * scale - m) with one fused multiply-add, with no
+// masking and no guard (m is finite), in 10 steps.  For an e4m3 tile the raw
+// scores are first multiplied by their tokens' scales (the keys' scale), and
+// the weights by them again after the sum (the values' scale, carried by P).
 constexpr int kSoftmaxSteps = 13;
 template <bool FP8>
 struct Softmax {
@@ -126,7 +128,7 @@ struct Softmax {
   bf16x8 pf0, pf1;
 
   __device__ __forceinline__ void step(int j) {
-    if (!FP8 && full) {
+    if (full) {
       fast_step(j);
       return;
     }
@@ -188,10 +190,34 @@ struct Softmax {
   }
   __device__ __forceinline__ void fast_step(int j) {
     if (j == 0) {
+      if constexpr (FP8) {  // the tokens' scales apply to the keys: scale the raw scores first
+        const int half = opaque_lane() >> 5;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const f32x4 s4 = *(const f32x4*)(tsc + 8 * q + 4 * half);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            tsv[4 * q + c] = s4[c];
+            v[4 * q + c] *= s4[c];
+          }
+        }
+      }
       mt = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
 #pragma unroll
       for (int i = 4; i < 8; ++i) mt = fmaxf(mt, v[i]);
     } else if (j == 1) {
+      if constexpr (FP8) {
+        const int half = opaque_lane() >> 5;
+#pragma unroll
+        for (int q = 2; q < 4; ++q) {
+          const f32x4 s4 = *(const f32x4*)(tsc + 8 * q + 4 * half);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            tsv[4 * q + c] = s4[c];
+            v[4 * q + c] *= s4[c];
+          }
+        }
+      }
 #pragma unroll
       for (int i = 8; i < 16; ++i) mt = fmaxf(mt, v[i]);
     } else if (j == 2) {
@@ -211,6 +237,10 @@ struct Softmax {
       float t0 = v[0] + v[1], t1 = v[2] + v[3], t2 = v[4] + v[5], t3 = v[6] + v[7];
       float t4 = v[8] + v[9], t5 = v[10] + v[11], t6 = v[12] + v[13], t7 = v[14] + v[15];
       l_run += ((t0 + t1) + (t2 + t3)) + ((t4 + t5) + (t6 + t7));
+      if constexpr (FP8) {  // and to the values: P carries them into P.V
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] *= tsv[i];
+      }
     } else if (j == 8) {
       float w8[8];
 #pragma unroll
