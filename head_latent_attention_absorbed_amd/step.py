@@ -263,7 +263,9 @@ class TplaStep:
 
     def __init__(self, inputs: dict, n_shards: int = 2, hadamard: bool = True, device: str = "cuda",
                  partial: str = "fp16"):
-        torch = self.torch = __import__("torch")
+        import torch
+
+        self.torch = torch
         w = inputs["workload"]
         if w.d_latent % n_shards:
             raise ValueError("d_latent must split evenly over the shards")
@@ -343,7 +345,9 @@ class GqaStep:
     rows regrouped after (mla_gqa_output)."""
 
     def __init__(self, gi: dict, device: str = "cuda", partial: str = "fp16"):
-        torch = self.torch = __import__("torch")
+        import torch
+
+        self.torch = torch
         w = gi["workload"]
         G = int(gi["groups"])
         self.workload, self.groups = w, G
