@@ -359,6 +359,10 @@ mla_status_t check_prefill(const mla_shape_t* shape, int32_t prompt_len) {
   if (shape->d_nope != 128 || shape->d_v != 128)
     return fail(MLA_ERR_UNSUPPORTED, "prefill: d_nope %d, d_v %d (kernels exist for 128, 128)", shape->d_nope,
                 shape->d_v);
+  // The prompt's records and the outputs are bf16 only: a shape that says
+  // otherwise would have its buffers read or written in the wrong type.
+  if (shape->cache_dtype != MLA_BF16 || shape->out_dtype != MLA_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "prefill: records and outputs are bf16 (cache_dtype and out_dtype MLA_BF16)");
   if (prompt_len < 1 || prompt_len > (1 << 20) || (int64_t)shape->batch * prompt_len > (1 << 24))
     return fail(MLA_ERR_INVALID_ARG, "prefill: prompt_len %d out of range", prompt_len);
   return MLA_OK;

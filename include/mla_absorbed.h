@@ -271,7 +271,9 @@ mla_status_t mla_append_kv(const mla_shape_t* shape, int32_t d_model, const void
  *   out bf16 [B, P, H, d_v] and lse fp32 [B, P, H] for positions < seq_lens[b];
  *   the other positions are left untouched.
  * Kernels exist for d_nope = d_v = 128, d_rope = 64, d_latent 512 or 256,
- * and 1 <= P <= 2^20 with B P <= 2^24.  All tensors 16-byte aligned.
+ * and 1 <= P <= 2^20 with B P <= 2^24; shape->cache_dtype and
+ * shape->out_dtype must be MLA_BF16 (MLA_ERR_UNSUPPORTED otherwise).  All
+ * tensors 16-byte aligned.
  */
 mla_status_t mla_prefill_workspace_bytes(const mla_shape_t* shape, size_t* bytes);
 mla_status_t mla_prefill_kv_elems(const mla_shape_t* shape, int32_t prompt_len, int64_t* elems);

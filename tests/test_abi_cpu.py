@@ -231,6 +231,10 @@ def test_prefill_argument_checks():
     assert att(sh, out=None) == mla.MLA_ERR_INVALID_ARG
     assert att(sh, ckr=FAKE + 4) == mla.MLA_ERR_INVALID_ARG
     assert att(_shape(d_nope=192)) == mla.MLA_ERR_UNSUPPORTED
+    # records and outputs are bf16 only: other dtypes in the shape are refused
+    assert kv(_shape(cache_dtype=mla.MLA_FP8_E4M3)) == mla.MLA_ERR_UNSUPPORTED
+    assert att(_shape(out_dtype=mla.MLA_FP32)) == mla.MLA_ERR_UNSUPPORTED
+    assert att(_shape(cache_dtype=mla.MLA_FP8_E4M3)) == mla.MLA_ERR_UNSUPPORTED
 
 
 def test_tpla_argument_checks():
