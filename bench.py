@@ -13,7 +13,9 @@ times and the decode kernel's roofline come from an eager loop with HIP events
 between the calls.
 Consecutive steps rotate through independent replicas of all inputs whose
 total exceeds three times the 256 MB Infinity Cache, so each step reads its
-cache and weights from HBM.
+cache and weights from HBM.  With the headline workload the line also
+carries the cache append, the prefill, the TPLA split, GQLA's two paths and
+the decode step on every other decode workload (``configs``).
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload deepseek_v3]
 """
@@ -280,6 +282,73 @@ def leg_gqla(torch, np, stream, K, args):
     }
 
 
+DECODE_WORKLOADS = ("tiny", "deepseek_v3", "gqa7b", "tpla_shard", "kimi_k2_fp8")
+
+
+def leg_configs(torch, np, stream, K, args, exclude):
+    """The decode step on every other decode workload, with HIP events
+    between the calls of an eager loop (absorb, decode, merge with the
+    up-projection).  Consecutive steps rotate through input replicas that
+    together exceed three times the Infinity Cache where that takes at most
+    16 replicas (``cold``); the 1.2 MB tiny workload cannot leave it, so its
+    figures are warm."""
+    from head_latent_attention_absorbed_amd import DecodeStep
+    from workloads import get_workload, make_inputs
+
+    res = {}
+    for name in DECODE_WORKLOADS:
+        if name == exclude:
+            continue
+        w = get_workload(name)
+        inputs = make_inputs(w)
+        alg = algorithmic(w, inputs["seq_lens"])
+        need = math.ceil(3 * INFINITY_CACHE_BYTES / max(alg["step_bytes"], 1)) + 1
+        nrep = min(16, max(3, need))
+        steps = [DecodeStep(inputs, partial=args.partial) for _ in range(nrep)]
+        for i in range(args.warmup):
+            steps[i % nrep].run()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+        for i in range(K):
+            st, e = steps[i % nrep], ev[i]
+            e[0].record(stream)
+            st.absorb()
+            e[1].record(stream)
+            st.decode()
+            e[2].record(stream)
+            if st.fused:
+                st.combine_up()
+            else:
+                st.combine()
+                st.up()
+            e[3].record(stream)
+        torch.cuda.synchronize()
+        t = np.array([[e[j].elapsed_time(e[j + 1]) * 1e3 for j in range(3)] for e in ev])
+        step = t.sum(axis=1)
+        dec_mean = float(t[:, 1].mean())
+        med = np.median(t, axis=0)
+        achieved = alg["decode_bytes"] / (dec_mean * 1e-6) / 1e9
+        res[name] = {
+            "batch": w.batch, "heads": w.heads, "q_len": w.q_len, "d_latent": w.d_latent, "cache": w.cache_dtype,
+            "tokens": alg["tokens"], "cache_bytes": alg["cache_bytes"], "replicas": nrep, "cold": nrep >= need,
+            "us_per_step": {"median": round(float(np.median(step)), 2),
+                            "p10": round(float(np.percentile(step, 10)), 2),
+                            "p90": round(float(np.percentile(step, 90)), 2)},
+            "per_call_us_median": {"absorb": round(float(med[0]), 2), "decode": round(float(med[1]), 2),
+                                   "merge_up": round(float(med[2]), 2)},
+            "tbs_decode_merge": round(alg["cache_bytes"] / ((med[1] + med[2]) * 1e-6) / 1e12, 4),
+            "tbs_step": round(alg["cache_bytes"] / (float(np.median(step)) * 1e-6) / 1e12, 4),
+            "decode_roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                                "mfma_frac": round(alg["attn_flops"] / (dec_mean * 1e-6) / 1e12
+                                                   / MFMA_BF16_PEAK_TFLOPS, 4)},
+        }
+        log(f"configs: {name} step {res[name]['us_per_step']['median']} us, decode {med[1]:.1f} us")
+        del steps, inputs
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -298,7 +367,8 @@ def main():
                     help="steps per graph replay (consecutive replicas, like the layers of one forward "
                          "pass); 0 = all replicas, 1 = one step per replay")
     ap.add_argument("--legs", dest="legs", action="store_true", default=None,
-                    help="also time the prefill, TPLA-split and GQLA legs (default: with the headline workload)")
+                    help="also time the prefill, TPLA-split and GQLA legs and the other decode workloads "
+                         "(default: with the headline workload)")
     ap.add_argument("--decode-only", dest="legs", action="store_false", help="time the decode step only")
     ap.add_argument("--unfused", action="store_true",
                     help="merge (mla_combine_lse) and up-project (mla_up_v) in two launches")
@@ -438,6 +508,7 @@ def main():
     prefill_res = leg_prefill(torch, np, stream, K) if run_legs else None
     tpla_res = leg_tpla(torch, np, stream, K, args, w, inputs, alg, steps[0]) if run_legs else None
     gqla_res = leg_gqla(torch, np, stream, K, args) if run_legs else None
+    configs_res = leg_configs(torch, np, stream, K, args, w.name) if run_legs else None
 
     us_step = ms_per_step * 1e3
     value = alg["cache_bytes"] / (us_step * 1e-6) / 1e12
@@ -470,6 +541,7 @@ def main():
         "graph_1step_us_per_step": round(graph1_ms * 1e3, 2) if graph1_ms is not None else None,
         "eager_us_per_step": round(eager_ms * 1e3, 2),
         "per_call_us_median": {k: round(v, 2) for k, v in med.items()},
+        "tbs_decode_merge": round(alg["cache_bytes"] / (sum(med[c] for c in calls[1:]) * 1e-6) / 1e12, 4),
         "step_hbm_frac": round(value * 1e3 / HBM_PEAK_GBS, 4),
         "roofline": {
             "kernel": "decode_kernel (mla_decode_paged)",
@@ -497,6 +569,7 @@ def main():
         "tpla": tpla_res,
         "gqla": gqla_res,
         "prefill": prefill_res,
+        "configs": configs_res,
     }
     if args.copy_probe_mb > 0:
         copy_probe(args.copy_probe_mb)
