@@ -414,6 +414,7 @@ def main():
     # the eager loop below instead.
     graph_ms = None
     graph1_ms = None
+    warm_ms = None
     R = nrep if args.graph_steps <= 0 else min(args.graph_steps, nrep)
     if not args.no_graph:
         from head_latent_attention_absorbed_amd import capture_steps
@@ -432,6 +433,14 @@ def main():
         g1.record(stream)
         torch.cuda.synchronize()
         graph1_ms = g0.elapsed_time(g1) / K
+        # Warm: one replica's graph over and over (its cache stays in the
+        # Infinity Cache when it fits; the headline cache does not, 236 MB).
+        g0.record(stream)
+        for i in range(K):
+            steps[0].replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        warm_ms = g0.elapsed_time(g1) / K
         # R consecutive replicas per replay, as the layers of one forward pass:
         # K // R such replays plus K % R single-step ones, K steps in all.
         graph_ms = graph1_ms
@@ -482,6 +491,7 @@ def main():
     per_call = {name: [ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(K)]
                 for j, name in enumerate(calls)}
     med = {k: float(np.median(v)) for k, v in per_call.items()}
+    eager_steps = np.sum([per_call[c] for c in calls], axis=0)
     dec_us = float(np.mean(per_call["decode"]))
 
     # The cache append (x . [W_DKV | W_KR] -> RoPE -> records in the pages),
@@ -540,6 +550,10 @@ def main():
                        if graph_ms is not None else "eager",
         "graph_1step_us_per_step": round(graph1_ms * 1e3, 2) if graph1_ms is not None else None,
         "eager_us_per_step": round(eager_ms * 1e3, 2),
+        "eager_step_us": {"median": round(float(np.median(eager_steps)), 2),
+                          "p10": round(float(np.percentile(eager_steps, 10)), 2),
+                          "p90": round(float(np.percentile(eager_steps, 90)), 2)},
+        "warm_graph_1step_us_per_step": round(warm_ms * 1e3, 2) if warm_ms is not None else None,
         "per_call_us_median": {k: round(v, 2) for k, v in med.items()},
         "tbs_decode_merge": round(alg["cache_bytes"] / (sum(med[c] for c in calls[1:]) * 1e-6) / 1e12, 4),
         "step_hbm_frac": round(value * 1e3 / HBM_PEAK_GBS, 4),
