@@ -370,6 +370,8 @@ def main():
                     help="also time the prefill, TPLA-split and GQLA legs and the other decode workloads "
                          "(default: with the headline workload)")
     ap.add_argument("--decode-only", dest="legs", action="store_false", help="time the decode step only")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="with the legs, leave out the decode step on the other decode workloads")
     ap.add_argument("--unfused", action="store_true",
                     help="merge (mla_combine_lse) and up-project (mla_up_v) in two launches")
     args = ap.parse_args()
@@ -518,7 +520,7 @@ def main():
     prefill_res = leg_prefill(torch, np, stream, K) if run_legs else None
     tpla_res = leg_tpla(torch, np, stream, K, args, w, inputs, alg, steps[0]) if run_legs else None
     gqla_res = leg_gqla(torch, np, stream, K, args) if run_legs else None
-    configs_res = leg_configs(torch, np, stream, K, args, w.name) if run_legs else None
+    configs_res = leg_configs(torch, np, stream, K, args, w.name) if run_legs and not args.no_configs else None
 
     us_step = ms_per_step * 1e3
     value = alg["cache_bytes"] / (us_step * 1e-6) / 1e12

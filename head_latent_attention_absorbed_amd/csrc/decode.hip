@@ -17,10 +17,11 @@
 // softmax is online (BLASST abstract on the same listing relies on the same
 // running state), with the max only re-based when it grows by more than 2^8
 // so the accumulator rescale is rare.  A work-group of NW waves shares each
-// tile; tiles stream through an LDS ring (direct global->LDS DMA for bf16,
-// register-staged e4m3->bf16 decode for fp8).  The token axis of the whole
-// batch is cut into G equal parts; each (part, sequence) pair writes one
-// normalised partial and its log-sum-exp.
+// tile; tiles stream through an LDS ring (direct global->LDS DMA for bf16;
+// for fp8 the same DMA into a staging slot, then an exact e4m3->bf16 decode
+// in LDS).  The token axis of the whole batch is cut into G equal parts;
+// each (part, sequence) pair writes one normalised partial and its
+// log-sum-exp.
 //
 // The tile products, the online softmax and the LDS tile layout are in
 // tile_ops.h (shared with the prefill).
