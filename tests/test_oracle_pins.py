@@ -438,6 +438,136 @@ def test_p16_prefill_sdpa():
     check_prefill_sdpa(oracle)
 
 
+# ------------------------------------------------------------------ P17-P19 e4m3 cache with per-token scale
+#
+# The e4m3 cache stores each token's record as OCP E4M3 codes plus one fp32
+# scale, and a cached value is code x scale (FP8 KV quantization named in the
+# TransMLA abstracts; one scale per token over the whole record is this
+# build's reading).  These pins fix how the scale enters, independently of
+# the oracle's own e4m3 branch.
+
+def _fp8_tiny(**kw):
+    base = dict(cache_dtype="fp8_e4m3", q_len=2, seq_len=(5, 14), heads=3)
+    base.update(kw)
+    return tiny(**base)
+
+
+def _e4m3_torch(codes):
+    """e4m3 bytes -> fp64 through torch's float8_e4m3fn (a library decoder)."""
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def _valid_slots(inp):
+    """(page, slot) of every cached position of every sequence."""
+    w = inp["workload"]
+    out = []
+    for b in range(w.batch):
+        for t in range(int(inp["seq_lens"][b])):
+            out.append((int(inp["block_table"][b, t // w.block_size]), t % w.block_size))
+    return out
+
+
+def check_e4m3_pow2_scales_equal_bf16_cache(o):
+    """Give every token a power-of-two scale 2^k (k != 0 for most tokens):
+    every e4m3 value times 2^k is then exactly a bf16 value, so decoding the
+    e4m3 cache must give, bit for bit, what decoding a bf16 cache holding
+    those products gives.  Dividing by the scale, dropping it, or taking it
+    from the wrong (page, slot) breaks the equality."""
+    inp = make_inputs(_fp8_tiny())
+    w = inp["workload"]
+    rng = np.random.default_rng(23)
+    kv_scale = inp["kv_scale"].copy()
+    bf = np.full(inp["cache"].shape, 0x7FC0, dtype=np.uint16)          # NaN where nothing is cached
+    for page, slot in _valid_slots(inp):
+        k = int(rng.choice([-5, -3, -2, -1, 1, 2, 3, 4]))
+        kv_scale[page, slot] = np.float32(2.0 ** k)
+        vals = _e4m3_torch(inp["cache"][page, slot]) * 2.0 ** k          # exact in fp64
+        bits = f32_to_bf16_bits(vals.astype(np.float32))
+        assert np.array_equal(f64(bits), vals), "e4m3 x 2^k must be a bf16 value"
+        bf[page, slot] = bits
+    inp["kv_scale"] = kv_scale
+    ref_inp = dict(inp)
+    ref_inp["workload"] = replace(w, cache_dtype="bf16")
+    ref_inp["cache"] = bf
+    ref_inp["kv_scale"] = None
+    got, ref = o.decode(inp), o.decode(ref_inp)
+    for key in ("out", "lse", "o_lat"):
+        assert np.array_equal(got[key], ref[key]), key
+
+
+def test_p17_e4m3_pow2_scales_equal_bf16_cache():
+    check_e4m3_pow2_scales_equal_bf16_cache(oracle)
+
+
+def check_e4m3_sdpa(o):
+    """The generated scales (amax / 448): keys and values rebuilt with torch
+    from the codes (torch's e4m3 decoder) times kv_scale[page][slot], attended
+    by torch's SDPA in fp64 with the causal tail as a mask."""
+    w = _fp8_tiny(q_len=3, heads=4, seq_len=(3, 15))
+    inp = make_inputs(w)
+    res = o.decode(inp)
+    qn, qr, wk, wv = (torch.from_numpy(f64(inp[k])) for k in ("q_nope", "q_rope", "w_uk", "w_uv"))
+    for b in range(w.batch):
+        L = int(inp["seq_lens"][b])
+        t = np.arange(L)
+        pages, slots = inp["block_table"][b, t // w.block_size], t % w.block_size
+        recs = torch.from_numpy(_e4m3_torch(inp["cache"][pages, slots]))
+        recs = recs * torch.from_numpy(inp["kv_scale"][pages, slots].astype(np.float64)).unsqueeze(1)
+        c, kr = recs[:, : w.d_latent], recs[:, w.d_latent:]
+        k = torch.cat([torch.einsum("hnc,tc->htn", wk, c), kr.unsqueeze(0).expand(w.heads, L, w.d_rope)], dim=2)
+        v = torch.einsum("tc,hcv->htv", c, wv)
+        q = torch.cat([qn[b], qr[b]], dim=2).permute(1, 0, 2)
+        mask = torch.zeros(w.q_len, L, dtype=torch.bool)
+        for s in range(w.q_len):
+            mask[s, : L - w.q_len + 1 + s] = True
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=w.softmax_scale)
+        close(res["out"][b], ref.permute(1, 0, 2).numpy())
+
+
+def test_p18_e4m3_sdpa():
+    check_e4m3_sdpa(oracle)
+
+
+def check_e4m3_brute_force(o):
+    """Pure-Python scalar loops over an e4m3 record: each code is looked up in
+    torch's table of the 256 e4m3 values, times the token's scale as a Python
+    float; keys, values, softmax and output in scalar arithmetic."""
+    w = Workload(name="bf8", batch=1, heads=2, q_len=2, d_latent=8, seq_len=(6, 6), paged=True,
+                 cache_dtype="fp8_e4m3", out_dtype="bf16", weight_var=0.25, seed=98, d_nope=4, d_rope=2,
+                 d_v=4, block_size=2, spare_blocks=1)
+    inp = make_inputs(w)
+    res = o.decode(inp)
+    table = _e4m3_torch(np.arange(256, dtype=np.uint8)).tolist()
+    bt = inp["block_table"].tolist()
+    codes, scales = inp["cache"].tolist(), inp["kv_scale"].tolist()
+    qn, qr = f64(inp["q_nope"]).tolist(), f64(inp["q_rope"]).tolist()
+    wk, wv = f64(inp["w_uk"]).tolist(), f64(inp["w_uv"]).tolist()
+    L = int(inp["seq_lens"][0])
+    scale = 1.0 / math.sqrt(w.d_nope + w.d_rope)
+    for h in range(w.heads):
+        for s in range(w.q_len):
+            zs, vs = [], []
+            for t in range(L - w.q_len + 1 + s):
+                page, slot = bt[0][t // w.block_size], t % w.block_size
+                rec = [table[x] * scales[page][slot] for x in codes[page][slot]]
+                c, kr = rec[: w.d_latent], rec[w.d_latent:]
+                key = [sum(wk[h][n][i] * c[i] for i in range(w.d_latent)) for n in range(w.d_nope)] + kr
+                val = [sum(c[i] * wv[h][i][j] for i in range(w.d_latent)) for j in range(w.d_v)]
+                qv = qn[0][s][h] + qr[0][s][h]
+                zs.append(scale * sum(a * b for a, b in zip(qv, key)))
+                vs.append(val)
+            m = max(zs)
+            es = [math.exp(z - m) for z in zs]
+            tot = sum(es)
+            out = [sum(es[i] * vs[i][j] for i in range(len(es))) / tot for j in range(w.d_v)]
+            close(res["out"][0, s, h], out)
+            close([res["lse"][0, s, h]], [m + math.log(tot)])
+
+
+def test_p19_e4m3_brute_force():
+    check_e4m3_brute_force(oracle)
+
+
 # ------------------------------------------------------------------ planted mistakes
 
 def _mutant(**patches):
@@ -478,6 +608,38 @@ def _bad_combine(o_parts, lse_parts):
     return np.einsum("k...,k...d->...d", wts, o_parts), m  # forgets to normalise
 
 
+def _e4m3_values(inputs):
+    return om.e4m3_to_f64(inputs["cache"])
+
+
+def _cache_values_scale_dropped(inputs):
+    if inputs["workload"].cache_dtype == "bf16":
+        return om.bf16_to_f64(inputs["cache"])
+    return _e4m3_values(inputs)
+
+
+def _cache_values_scale_divided(inputs):
+    if inputs["workload"].cache_dtype == "bf16":
+        return om.bf16_to_f64(inputs["cache"])
+    return _e4m3_values(inputs) / inputs["kv_scale"].astype(np.float64)[..., None]
+
+
+def _cache_values_scale_slot_major(inputs):
+    """The scale array read as [slot][page] instead of [page][slot]."""
+    if inputs["workload"].cache_dtype == "bf16":
+        return om.bf16_to_f64(inputs["cache"])
+    ks = inputs["kv_scale"]
+    wrong = ks.reshape(-1).reshape(ks.shape[1], ks.shape[0]).T
+    return _e4m3_values(inputs) * wrong.astype(np.float64)[..., None]
+
+
+def _cache_values_scale_per_page(inputs):
+    """One scale per page (its first slot's) broadcast over the page."""
+    if inputs["workload"].cache_dtype == "bf16":
+        return om.bf16_to_f64(inputs["cache"])
+    return _e4m3_values(inputs) * inputs["kv_scale"].astype(np.float64)[:, :1, None]
+
+
 def _sign_flip_absorb(q_nope, w_uk):
     return -om.absorb_q(q_nope, w_uk)
 
@@ -492,6 +654,18 @@ def _sign_flip_absorb(q_nope, w_uk):
     (dict(combine=_bad_combine), check_split_merge),
     (dict(absorb_q=_sign_flip_absorb), check_absorb_identity),
     (dict(reconstruct_kv=_no_rope_kv), check_prefill_sdpa),
+    (dict(cache_values=_cache_values_scale_dropped), check_e4m3_pow2_scales_equal_bf16_cache),
+    (dict(cache_values=_cache_values_scale_divided), check_e4m3_pow2_scales_equal_bf16_cache),
+    (dict(cache_values=_cache_values_scale_slot_major), check_e4m3_pow2_scales_equal_bf16_cache),
+    (dict(cache_values=_cache_values_scale_per_page), check_e4m3_pow2_scales_equal_bf16_cache),
+    (dict(cache_values=_cache_values_scale_dropped), check_e4m3_sdpa),
+    (dict(cache_values=_cache_values_scale_divided), check_e4m3_sdpa),
+    (dict(cache_values=_cache_values_scale_slot_major), check_e4m3_sdpa),
+    (dict(cache_values=_cache_values_scale_per_page), check_e4m3_sdpa),
+    (dict(cache_values=_cache_values_scale_dropped), check_e4m3_brute_force),
+    (dict(cache_values=_cache_values_scale_divided), check_e4m3_brute_force),
+    (dict(cache_values=_cache_values_scale_slot_major), check_e4m3_brute_force),
+    (dict(e4m3_to_f64=_e4m3_bias8), check_e4m3_sdpa),
 ])
 def test_planted_mistakes_are_caught(patch, check):
     with pytest.raises(AssertionError):
