@@ -60,6 +60,10 @@ mla_status_t check_shape(const mla_shape_t* s) {
       s->d_v < 1 || s->block_size < 1 || s->max_blocks_per_seq < 1)
     return fail(MLA_ERR_INVALID_ARG, "shape has a non-positive size");
   if (!std::isfinite(s->softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  // The kernels take a tile's maximum over the raw scores and scale it
+  // afterwards, which is the maximum of the scaled scores only for a
+  // positive scale.
+  if (!(s->softmax_scale > 0.0f)) return fail(MLA_ERR_UNSUPPORTED, "softmax_scale %g (must be > 0)", s->softmax_scale);
   if (s->cache_dtype != MLA_BF16 && s->cache_dtype != MLA_FP8_E4M3)
     return fail(MLA_ERR_INVALID_ARG, "cache_dtype must be MLA_BF16 or MLA_FP8_E4M3");
   if (s->out_dtype != MLA_BF16 && s->out_dtype != MLA_FP32)

@@ -68,6 +68,8 @@ FAKE = 1 << 40  # a 16-byte aligned address; never dereferenced by failing calls
     (dict(batch=0), mla.MLA_ERR_INVALID_ARG),
     (dict(num_heads=-1), mla.MLA_ERR_INVALID_ARG),
     (dict(softmax_scale=math.inf), mla.MLA_ERR_INVALID_ARG),
+    (dict(softmax_scale=-0.07), mla.MLA_ERR_UNSUPPORTED),
+    (dict(softmax_scale=0.0), mla.MLA_ERR_UNSUPPORTED),
     (dict(cache_dtype=7), mla.MLA_ERR_INVALID_ARG),
     (dict(out_dtype=mla.MLA_FP8_E4M3), mla.MLA_ERR_INVALID_ARG),
     (dict(partial_dtype=mla.MLA_BF16), mla.MLA_ERR_INVALID_ARG),
