@@ -29,6 +29,8 @@ from .binding import (  # noqa: F401
     mla_combine_up_v,
     mla_append_kv,
     mla_append_kv_workspace_bytes,
+    mla_append_kv_noalloc,
+    MLA_APPEND_NOALLOC_MAX_BYTES,
     mla_prefill_workspace_bytes,
     mla_prefill_kv_elems,
     mla_prefill_kv,

@@ -81,6 +81,7 @@ def library() -> ctypes.CDLL:
     lib.mla_combine_up_v.argtypes = [SP, I32, P, P, P, P, P, P, P]
     lib.mla_append_kv_workspace_bytes.argtypes = [SP, I32, ctypes.POINTER(ctypes.c_size_t)]
     lib.mla_append_kv.argtypes = [SP, I32, P, P, F, P, P, I64, I64, P, P, P, P, ctypes.c_size_t, P]
+    lib.mla_append_kv_noalloc.argtypes = [SP, I32, P, P, F, P, P, I64, I64, P, P, P, P]
     lib.mla_prefill_workspace_bytes.argtypes = [SP, ctypes.POINTER(ctypes.c_size_t)]
     lib.mla_prefill_kv_elems.argtypes = [SP, I32, ctypes.POINTER(ctypes.c_int64)]
     lib.mla_prefill_kv.argtypes = [SP, I32, P, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -91,7 +92,8 @@ def library() -> ctypes.CDLL:
     lib.mla_gqa_queries.argtypes = [SP, I32, P, P, P, P, P]
     lib.mla_gqa_output.argtypes = [SP, I32, P, P, P, P, P]
     for fn in ("mla_absorb_q", "mla_decode_num_parts", "mla_decode_paged", "mla_combine_lse", "mla_up_v",
-               "mla_combine_up_v", "mla_append_kv_workspace_bytes", "mla_append_kv", "mla_prefill_workspace_bytes",
+               "mla_combine_up_v", "mla_append_kv_workspace_bytes", "mla_append_kv", "mla_append_kv_noalloc",
+               "mla_prefill_workspace_bytes",
                "mla_prefill_kv_elems", "mla_prefill_kv", "mla_prefill_attention", "mla_tpla_split_weights",
                "mla_tpla_rotate_cache", "mla_tpla_reduce", "mla_gqa_queries", "mla_gqa_output"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -193,6 +195,17 @@ def mla_append_kv(shape: MlaShape, d_model: int, x, w_dkv, rope_base: float, c_k
                                    _ptr(c_kv), _ptr(k_rope), int(token_stride), int(block_stride), _ptr(kv_scale),
                                    _ptr(block_table), _ptr(seq_lens), _ptr(workspace), int(workspace_bytes),
                                    _stream(stream)), "mla_append_kv")
+
+
+MLA_APPEND_NOALLOC_MAX_BYTES = 8 << 20
+
+
+def mla_append_kv_noalloc(shape: MlaShape, d_model: int, x, w_dkv, rope_base: float, c_kv, k_rope, token_stride: int,
+                          block_stride: int, kv_scale, block_table, seq_lens, stream=None) -> None:
+    _check(library().mla_append_kv_noalloc(ctypes.byref(shape), int(d_model), _ptr(x), _ptr(w_dkv), float(rope_base),
+                                           _ptr(c_kv), _ptr(k_rope), int(token_stride), int(block_stride),
+                                           _ptr(kv_scale), _ptr(block_table), _ptr(seq_lens), _stream(stream)),
+           "mla_append_kv_noalloc")
 
 
 def mla_prefill_workspace_bytes(shape: MlaShape) -> int:

@@ -17,10 +17,41 @@
 // (nearest even) or as e4m3 bytes of v / scale with one fp32 scale per token,
 // scale = max|v| / 448 over the record.  The new tokens are the last S_q
 // positions of each sequence; an idle slot (length 0) is left alone.
+#include <atomic>
+
+#include "mla_absorbed.h"
 #include "mla_device.h"
 #include "mla_kernels.h"
 
+// Device memory of mla_append_kv_noalloc: the split-K partial products live
+// here instead of in a caller workspace.  Every GPU that loads the library
+// holds its own copy until the process ends; in host code this name is only a
+// stand-in for the symbol, so its device address is looked up once per device
+// (append_scratch) and only that address is ever handed to a kernel.
+static __device__ __align__(256) char scratch[MLA_APPEND_NOALLOC_MAX_BYTES];
+
 namespace mla {
+
+hipError_t append_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // Resolved with the device current; two threads racing here both get
+    // the same address, so a plain store suffices.
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 namespace {
 
 constexpr int kFinishWaves = 8;

@@ -292,38 +292,53 @@ mla_status_t mla_append_kv_workspace_bytes(const mla_shape_t* shape, int32_t d_m
   return ok();
 }
 
-mla_status_t mla_append_kv(const mla_shape_t* shape, int32_t d_model, const void* x, const void* w_dkv,
-                           float rope_base, void* c_kv, void* k_rope, int64_t token_stride, int64_t block_stride,
-                           float* kv_scale, const int32_t* block_table, const int32_t* seq_lens, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// Checks and launches of mla_append_kv; `workspace == nullptr` asks for the
+// library's own scratch array (mla_append_kv_noalloc), which is looked up
+// only after every argument check has passed.
+mla_status_t append_impl(const char* who, const mla_shape_t* shape, int32_t d_model, const void* x,
+                         const void* w_dkv, float rope_base, void* c_kv, void* k_rope, int64_t token_stride,
+                         int64_t block_stride, float* kv_scale, const int32_t* block_table, const int32_t* seq_lens,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const bool own_scratch = workspace == nullptr;
   mla_status_t st = check_shape(shape);
   if (st != MLA_OK) return st;
   int ks = 0;
   st = append_slices(shape, d_model, &ks);
   if (st != MLA_OK) return st;
-  if (!x || !w_dkv || !c_kv || !k_rope || !block_table || !seq_lens || !workspace)
-    return fail(MLA_ERR_INVALID_ARG, "mla_append_kv: NULL tensor");
+  if (!x || !w_dkv || !c_kv || !k_rope || !block_table || !seq_lens)
+    return fail(MLA_ERR_INVALID_ARG, "%s: NULL tensor", who);
   if (!std::isfinite(rope_base) || rope_base <= 1.0f)
-    return fail(MLA_ERR_INVALID_ARG, "mla_append_kv: rope_base must be finite and > 1");
+    return fail(MLA_ERR_INVALID_ARG, "%s: rope_base must be finite and > 1", who);
   const bool fp8 = shape->cache_dtype == MLA_FP8_E4M3;
-  if (fp8 && !kv_scale) return fail(MLA_ERR_INVALID_ARG, "mla_append_kv: fp8 cache needs kv_scale");
-  if (!fp8 && kv_scale) return fail(MLA_ERR_INVALID_ARG, "mla_append_kv: kv_scale given for a bf16 cache");
+  if (fp8 && !kv_scale) return fail(MLA_ERR_INVALID_ARG, "%s: fp8 cache needs kv_scale", who);
+  if (!fp8 && kv_scale) return fail(MLA_ERR_INVALID_ARG, "%s: kv_scale given for a bf16 cache", who);
   if (!aligned16(x) || !aligned16(w_dkv) || !aligned16(workspace) || !aligned16(c_kv) || !aligned16(k_rope))
-    return fail(MLA_ERR_INVALID_ARG, "mla_append_kv: tensors must be 16-byte aligned");
+    return fail(MLA_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", who);
   const int elem = fp8 ? 1 : 2;
   const int64_t rope_off = static_cast<const char*>(k_rope) - static_cast<const char*>(c_kv);
   if (token_stride <= 0 || token_stride % 16 || block_stride % 16 ||
       block_stride < (int64_t)shape->block_size * token_stride)
     return fail(MLA_ERR_INVALID_ARG,
-                "mla_append_kv: token_stride/block_stride must be positive multiples of 16 with "
-                "block_stride >= block_size * token_stride");
+                "%s: token_stride/block_stride must be positive multiples of 16 with "
+                "block_stride >= block_size * token_stride", who);
   if (rope_off < (int64_t)shape->d_latent * elem || rope_off + (int64_t)shape->d_rope * elem > token_stride)
-    return fail(MLA_ERR_INVALID_ARG, "mla_append_kv: k_rope must follow the latent inside the record");
+    return fail(MLA_ERR_INVALID_ARG, "%s: k_rope must follow the latent inside the record", who);
   size_t need = 0;
   st = mla_append_kv_workspace_bytes(shape, d_model, &need);
   if (st != MLA_OK) return st;
-  if (workspace_bytes < need)
-    return fail(MLA_ERR_INVALID_ARG, "mla_append_kv: workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (own_scratch) {
+    if (need > (size_t)MLA_APPEND_NOALLOC_MAX_BYTES)
+      return fail(MLA_ERR_UNSUPPORTED,
+                  "%s: needs %zu bytes of partial products, more than the library's fixed %zu-byte scratch "
+                  "(use mla_append_kv with a workspace)", who, need, (size_t)MLA_APPEND_NOALLOC_MAX_BYTES);
+    hipError_t e = mla::append_scratch(&workspace);
+    if (e != hipSuccess) return hip_status(e, "mla_append_kv_noalloc scratch lookup");
+    workspace_bytes = MLA_APPEND_NOALLOC_MAX_BYTES;
+  } else if (workspace_bytes < need) {
+    return fail(MLA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes, need);
+  }
   const int M = shape->batch * shape->q_len;
   mla::HeadGemmParams g{};
   g.a = x;
@@ -334,7 +349,8 @@ mla_status_t mla_append_kv(const mla_shape_t* shape, int32_t d_model, const void
   g.K = mla::kAppendSlice;
   g.N = shape->d_latent + shape->d_rope;
   hipError_t e = mla::launch_head_gemm_partials(g, stream);
-  if (e != hipSuccess) return hip_status(e, "mla_append_kv product launch");
+  if (e != hipSuccess) return hip_status(e, own_scratch ? "mla_append_kv_noalloc product launch"
+                                                        : "mla_append_kv product launch");
   mla::AppendParams p{};
   p.part = static_cast<const float*>(workspace);
   p.KS = ks;
@@ -352,7 +368,27 @@ mla_status_t mla_append_kv(const mla_shape_t* shape, int32_t d_model, const void
   p.block_size = shape->block_size;
   p.log2_base = std::log2((double)rope_base);
   p.fp8 = fp8;
-  return hip_status(mla::launch_append_finish(p, stream), "mla_append_kv launch");
+  return hip_status(mla::launch_append_finish(p, stream),
+                    own_scratch ? "mla_append_kv_noalloc launch" : "mla_append_kv launch");
+}
+
+}  // namespace
+
+mla_status_t mla_append_kv(const mla_shape_t* shape, int32_t d_model, const void* x, const void* w_dkv,
+                           float rope_base, void* c_kv, void* k_rope, int64_t token_stride, int64_t block_stride,
+                           float* kv_scale, const int32_t* block_table, const int32_t* seq_lens, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace) return fail(MLA_ERR_INVALID_ARG, "mla_append_kv: NULL tensor (workspace)");
+  return append_impl("mla_append_kv", shape, d_model, x, w_dkv, rope_base, c_kv, k_rope, token_stride, block_stride,
+                     kv_scale, block_table, seq_lens, workspace, workspace_bytes, stream);
+}
+
+mla_status_t mla_append_kv_noalloc(const mla_shape_t* shape, int32_t d_model, const void* x, const void* w_dkv,
+                                   float rope_base, void* c_kv, void* k_rope, int64_t token_stride,
+                                   int64_t block_stride, float* kv_scale, const int32_t* block_table,
+                                   const int32_t* seq_lens, hipStream_t stream) {
+  return append_impl("mla_append_kv_noalloc", shape, d_model, x, w_dkv, rope_base, c_kv, k_rope, token_stride,
+                     block_stride, kv_scale, block_table, seq_lens, nullptr, 0, stream);
 }
 
 namespace {

@@ -175,5 +175,8 @@ struct AppendParams {
   int32_t fp8;
 };
 hipError_t launch_append_finish(const AppendParams& p, hipStream_t stream);
+// Device address, on the current device, of the fixed scratch array of
+// mla_append_kv_noalloc (MLA_APPEND_NOALLOC_MAX_BYTES bytes, 256-byte aligned).
+hipError_t append_scratch(void** ptr);
 
 }  // namespace mla

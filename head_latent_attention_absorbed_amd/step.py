@@ -12,7 +12,7 @@ import numpy as np
 
 from .binding import (
     MLA_BF16, MLA_FP8_E4M3, MLA_FP16, MLA_FP32, MLA_TILE_TOKENS, MlaShape,
-    mla_absorb_q, mla_append_kv, mla_append_kv_workspace_bytes, mla_decode_num_parts, mla_decode_paged,
+    mla_absorb_q, mla_append_kv, mla_append_kv_noalloc, mla_append_kv_workspace_bytes, mla_decode_num_parts, mla_decode_paged,
     mla_combine_lse, mla_combine_up_v, mla_prefill_attention, mla_prefill_kv, mla_prefill_kv_elems,
     mla_prefill_workspace_bytes, mla_tpla_reduce, mla_tpla_rotate_cache, mla_tpla_split_weights, mla_up_v,
     mla_gqa_output, mla_gqa_queries,
@@ -116,11 +116,18 @@ class DecodeStep:
         nbytes = mla_append_kv_workspace_bytes(self.shape, self.d_model)
         self.append_ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
 
-    def append(self, stream=None, cache=None, kv_scale=None):
-        """Write the new tokens' records [c_KV | k_rope] into the cache."""
+    def append(self, stream=None, cache=None, kv_scale=None, noalloc=False):
+        """Write the new tokens' records [c_KV | k_rope] into the cache;
+        ``noalloc`` uses mla_append_kv_noalloc (the library's fixed scratch
+        instead of this step's workspace)."""
         cache = self.cache if cache is None else cache
         kv_scale = self.kv_scale if kv_scale is None else kv_scale
         base = cache.data_ptr()
+        if noalloc:
+            mla_append_kv_noalloc(self.shape, self.d_model, self.x, self.w_dkv, self.rope_base, base,
+                                  base + self.workload.d_latent * self.elem, self.token_stride, self.block_stride,
+                                  kv_scale, self.block_table, self.seq_lens, stream)
+            return
         mla_append_kv(self.shape, self.d_model, self.x, self.w_dkv, self.rope_base, base,
                       base + self.workload.d_latent * self.elem, self.token_stride, self.block_stride, kv_scale,
                       self.block_table, self.seq_lens, self.append_ws, self.append_ws.numel(), stream)

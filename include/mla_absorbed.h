@@ -240,6 +240,35 @@ mla_status_t mla_append_kv(const mla_shape_t* shape, int32_t d_model, const void
                            const int32_t* seq_lens, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* Size of the library's fixed scratch array used by mla_append_kv_noalloc. */
+#define MLA_APPEND_NOALLOC_MAX_BYTES (8u << 20)
+
+/*
+ * mla_append_kv_noalloc -- mla_append_kv without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * checks and results as mla_append_kv; the split-K partial products go to a
+ * device array inside the library of MLA_APPEND_NOALLOC_MAX_BYTES (8 MiB),
+ * one per GPU, held from library load until the process ends.  The call
+ * allocates nothing (no hipMalloc / hipFree, no allocating library routine).
+ *   Limit: mla_append_kv_workspace_bytes(shape, d_model), i.e.
+ *   B * S_q * (d_model / 256) * (d_latent + d_rope) * 4 bytes, must not exceed
+ *   MLA_APPEND_NOALLOC_MAX_BYTES, else MLA_ERR_UNSUPPORTED is returned before
+ *   anything is enqueued (e.g. B * S_q up to 227 rows at d_model 4096, d_latent 512).
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (different streams, or threads without ordering) race on it and give
+ *   undefined records.  Nothing in the array needs to start at zero: each call
+ *   writes every partial product before reading it, so a later call never
+ *   sees an earlier call's contents.
+ * The first call on a device resolves the array's address on that device
+ * (a host-side runtime lookup, no device work); a failure there returns
+ * MLA_ERR_HIP.
+ */
+mla_status_t mla_append_kv_noalloc(const mla_shape_t* shape, int32_t d_model, const void* x, const void* w_dkv,
+                                   float rope_base, void* c_kv, void* k_rope, int64_t token_stride,
+                                   int64_t block_stride, float* kv_scale, const int32_t* block_table,
+                                   const int32_t* seq_lens, hipStream_t stream);
+
 /*
  * Prefill in the MLA form.  A prompt is compute-bound, so it is attended with
  * keys and values reconstructed per head from the latent (the form the

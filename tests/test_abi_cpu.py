@@ -22,6 +22,7 @@ def test_exports_every_declared_symbol():
     declared = mla.exported_symbols()
     assert set(declared) >= {"mla_absorb_q", "mla_decode_num_parts", "mla_decode_paged", "mla_combine_lse",
                              "mla_up_v", "mla_combine_up_v", "mla_append_kv", "mla_append_kv_workspace_bytes",
+                             "mla_append_kv_noalloc",
                              "mla_prefill_workspace_bytes", "mla_prefill_kv_elems", "mla_prefill_kv", "mla_prefill_attention",
                              "mla_tpla_split_weights", "mla_tpla_rotate_cache", "mla_tpla_reduce",
                              "mla_gqa_queries", "mla_gqa_output",
@@ -42,6 +43,7 @@ def test_struct_layout_matches_header(tmp_path):
         "#include <stdio.h>\n#include <stddef.h>\n#include \"mla_absorbed.h\"\n"
         "int main(void) {\n  printf(\"%zu\\n\", sizeof(mla_shape_t));\n"
         + "".join(f'  printf("%zu\\n", offsetof(mla_shape_t, {n}));\n' for n in names)
+        + '  printf("%zu\\n", (size_t)MLA_APPEND_NOALLOC_MAX_BYTES);\n'
         + "  return 0;\n}\n")
     exe = tmp_path / "layout"
     from head_latent_attention_absorbed_amd import binding
@@ -53,6 +55,7 @@ def test_struct_layout_matches_header(tmp_path):
     assert vals[0] == ctypes.sizeof(MlaShape)
     for n, off in zip(names, vals[1:]):
         assert getattr(MlaShape, n).offset == off, n
+    assert vals[-1] == mla.MLA_APPEND_NOALLOC_MAX_BYTES
 
 
 def _shape(**kw):
@@ -207,6 +210,39 @@ def test_append_argument_checks():
     st, _, need = _append(sh)
     assert _append(sh, ws_bytes=need - 4)[0] == mla.MLA_ERR_INVALID_ARG              # workspace too small
     assert "workspace" in mla.mla_last_error()
+
+
+def _append_noalloc(sh, d_model=4096, **kw):
+    lib = _lib()
+    a = dict(x=FAKE, w=FAKE, base=10000.0, c_kv=FAKE, k_rope=FAKE + 1024, ts=1152, bst=64 * 1152, kv_scale=None,
+             bt=FAKE, sl=FAKE)
+    a.update(kw)
+    return lib.mla_append_kv_noalloc(ctypes.byref(sh), d_model, a["x"], a["w"], a["base"], a["c_kv"], a["k_rope"],
+                                     a["ts"], a["bst"], a["kv_scale"], a["bt"], a["sl"], None)
+
+
+def test_append_noalloc_argument_checks():
+    """The no-allocation append checks its arguments like mla_append_kv, and
+    refuses, before touching the device, a request whose partial products do
+    not fit the library's fixed scratch array."""
+    sh = _shape()
+    for name in ("x", "w", "c_kv", "bt", "sl"):
+        assert _append_noalloc(sh, **{name: None}) == mla.MLA_ERR_INVALID_ARG, name
+    assert _append_noalloc(sh, x=FAKE + 2) == mla.MLA_ERR_INVALID_ARG
+    assert _append_noalloc(sh, base=1.0) == mla.MLA_ERR_INVALID_ARG
+    assert _append_noalloc(sh, k_rope=FAKE + 512) == mla.MLA_ERR_INVALID_ARG
+    assert _append_noalloc(sh, d_model=1000) == mla.MLA_ERR_UNSUPPORTED
+    # 228 rows x 16 slices x 576 values x 4 bytes > 8 MiB; 227 rows fit
+    lib = _lib()
+    for rows, fits in ((227, True), (228, False)):
+        big = _shape(batch=rows)
+        need = ctypes.c_size_t(0)
+        assert lib.mla_append_kv_workspace_bytes(ctypes.byref(big), 4096, ctypes.byref(need)) == mla.MLA_OK
+        assert (need.value <= mla.MLA_APPEND_NOALLOC_MAX_BYTES) == fits
+    assert _append_noalloc(_shape(batch=228)) == mla.MLA_ERR_UNSUPPORTED
+    assert "scratch" in mla.mla_last_error()
+    assert _append_noalloc(_shape(batch=57, q_len=4)) == mla.MLA_ERR_UNSUPPORTED   # 228 rows again
+    assert _append_noalloc(_shape(batch=16), d_model=65536) == mla.MLA_ERR_UNSUPPORTED  # 16 rows x 256 slices
 
 
 def test_prefill_argument_checks():
