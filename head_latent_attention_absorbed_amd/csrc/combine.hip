@@ -7,6 +7,7 @@
 //   lse = log sum_k e^{lse_k},  o = sum_k e^{lse_k - lse} o_k.
 #include "mla_device.h"
 #include "mla_kernels.h"
+#include "split_plan.h"
 
 namespace mla {
 namespace {
@@ -50,21 +51,9 @@ __device__ __forceinline__ float lane_value(float x, int j) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), j));
 }
 
-// The split range of sequence b: parts g0..g1 (slots b + g); empty (g1 < g0)
-// for an idle sequence.  cu is the tile prefix of the batch.
-__device__ __forceinline__ void split_range(const int* cu, int B, int G, int b, int& g0, int& g1) {
-  const int N = cu[B], cb = cu[b], ce = cu[b + 1];
-  g0 = 0;
-  g1 = -1;
-  if (ce > cb) {
-    const int Wt = (N + G - 1) / G;
-    g0 = cb / Wt;
-    g1 = (ce - 1) / Wt;
-  }
-}
-
-// Merge one query row (row r of sequence b) over its splits g0..g1: this
-// lane's E consecutive columns E*lane .. E*lane + E-1 of
+// Merge one query row (row r) over its sequence's slots s0 .. s0 + ns - 1
+// (the split plan of split_plan.h): this lane's E consecutive columns
+// E*lane .. E*lane + E-1 of
 //   o = sum_k e^{lse_k - lse} o_k,  lse = log sum_k e^{lse_k}
 // into acc (zeros and lse = -inf when the row sees no position).  The splits
 // are visited U at a time: lane j requests the lse of split j of the batch
@@ -72,19 +61,19 @@ __device__ __forceinline__ void split_range(const int* cu, int B, int G, int b, 
 // latency covers the whole batch (indices past the last split repeat it with
 // weight 0).
 template <int DC, bool HALF, int U = 16>
-__device__ __forceinline__ float merge_row(const void* o_part, const float* lse_part, int R, int b, int r, int g0,
-                                           int g1, int lane, float (&acc)[DC / 64]) {
+__device__ __forceinline__ float merge_row(const void* o_part, const float* lse_part, int R, int r, int s0, int ns,
+                                           int lane, float (&acc)[DC / 64]) {
   constexpr int E = DC / 64;
 #pragma unroll
   for (int i = 0; i < E; ++i) acc[i] = 0.0f;
   float m = -__builtin_inff(), tot = 0.0f;
-  for (int gb = g0; gb <= g1; gb += U) {
-    const int n = min(U, g1 - gb + 1);
-    const float lk = lane < n ? lse_part[((int64_t)b + gb + lane) * R + r] : -__builtin_inff();
+  for (int gb = 0; gb < ns; gb += U) {
+    const int n = min(U, ns - gb);
+    const float lk = lane < n ? lse_part[((int64_t)s0 + gb + lane) * R + r] : -__builtin_inff();
     PartRow<E, HALF> part[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int64_t slot = (int64_t)b + gb + min(j, n - 1);
+      const int64_t slot = (int64_t)s0 + gb + min(j, n - 1);
       part[j].load(o_part, (slot * R + r) * DC + E * lane);
     }
     // Keep every load above this point: the lse is waited for while the
@@ -120,17 +109,24 @@ __device__ __forceinline__ float merge_row(const void* o_part, const float* lse_
 template <int DC, bool HALF>
 __global__ void __launch_bounds__(256) combine_kernel(CombineParams p, const int32_t* __restrict__ seq_lens) {
   constexpr int E = DC / 64;
-  __shared__ int cu[kMaxBatch + 1];
+  __shared__ int slots[2];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.x;
-  if (w == 0) build_tile_prefix(seq_lens, p.B, cu, lane);
+  if (w == 0) {
+    WavePlan pl;
+    pl.build(seq_lens, p.B, p.P, lane);
+    int s_b, p_b;
+    pl.slots_of(b, lane, s_b, p_b);
+    if (lane == 0) {
+      slots[0] = s_b;
+      slots[1] = p_b;
+    }
+  }
   __syncthreads();
   const int row = blockIdx.y * 4 + w;
   if (row >= p.R) return;
-  int g0, g1;
-  split_range(cu, p.B, p.G, b, g0, g1);
   float acc[E];
-  const float lse = merge_row<DC, HALF>(p.o_part, p.lse_part, p.R, b, row, g0, g1, lane, acc);
+  const float lse = merge_row<DC, HALF>(p.o_part, p.lse_part, p.R, row, slots[0], slots[1], lane, acc);
   float* out = p.o_lat + ((int64_t)b * p.R + row) * DC + E * lane;
 #pragma unroll
   for (int i = 0; i < E; i += 4) *(f32x4*)(out + i) = f32x4{acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
@@ -178,7 +174,7 @@ struct UpGeometry {
   static_assert(NTW >= 1, "a wave takes whole 16-column tiles");
   static_assert(SLICE % 4096 == 0, "four waves issue equal shares of 1 KiB DMAs per slice");
   static_assert(4 * kUpRows * PITCH * 4 <= 4 * SLICE, "the reduction buffer reuses the W_UV slices");
-  static_assert((kMaxBatch + 1) * sizeof(int) <= (size_t)ATILE, "the tile prefix lives in the merged tile first");
+  static_assert((kMaxBatch + 1) * sizeof(int) <= (size_t)ATILE, "the slot prefix lives in the merged tile first");
 };
 
 // Byte offset of fp32 column c of merged row r: 16-byte granule c/4 at
@@ -196,7 +192,7 @@ __global__ void __launch_bounds__(1024) combine_up_kernel(CombineUpParams p) {
   constexpr int E = DC / 64;  // merged columns per lane
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* atile = smem + 4 * SLICE;
-  int* cu = (int*)atile;  // the tile prefix, until the merged rows overwrite it
+  int* sb = (int*)atile;  // the slot prefix of the split plan, until the merged rows overwrite it
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int kr = w & 3, nq = w >> 2;  // K part and output-column quarter of the product
@@ -204,8 +200,12 @@ __global__ void __launch_bounds__(1024) combine_up_kernel(CombineUpParams p) {
   const int h = blockIdx.x % H;
   const int m0 = (blockIdx.x / H) * kUpRows;
 
-  // Tile prefix first (wave 0), so that its loads are not queued behind the DMA.
-  if (w == 0) build_tile_prefix(p.seq_lens, p.B, cu, lane);
+  // Split plan first (wave 0), so that its loads are not queued behind the DMA.
+  if (w == 0) {
+    WavePlan pl;
+    pl.build(p.seq_lens, p.B, p.P, lane);
+    pl.write_slot_prefix(sb, lane);
+  }
 
   // W_UV[h] rows kr*KW .. kr*KW + KW-1 into slice kr: LDS granule position q
   // of row k holds global granule q ^ swz(k).  Wave (kr, nq) copies pieces
@@ -226,14 +226,13 @@ __global__ void __launch_bounds__(1024) combine_up_kernel(CombineUpParams p) {
   const int m = m0 + w;
   const int mc = min(m, M - 1);
   const int b = mc / p.S, r = (mc % p.S) * H + h;
-  int g0, g1;
-  split_range(cu, p.B, p.G, b, g0, g1);
-  if (m >= M) g1 = g0 - 1;  // rows past M merge nothing
-  block_sync();  // every read of cu is done before the merged rows overwrite it
+  const int s0 = sb[b];
+  const int ns = m < M ? sb[b + 1] - s0 : 0;  // rows past M merge nothing
+  block_sync();  // every read of the slot prefix is done before the merged rows overwrite it
   float acc[E];
   // 16 splits in flight per batch; 8 for fp32 rows of 512, which would not
   // fit the 128 registers a lane has at 16 waves per work-group.
-  const float lse = merge_row<DC, HALF, (HALF || DC < 512) ? 16 : 8>(p.o_part, p.lse_part, R, b, r, g0, g1, lane, acc);
+  const float lse = merge_row<DC, HALF, (HALF || DC < 512) ? 16 : 8>(p.o_part, p.lse_part, R, r, s0, ns, lane, acc);
   if (lane == 0 && m < M) p.lse[(int64_t)m * H + h] = lse;
 #pragma unroll
   for (int e = 0; e < E; e += 4)

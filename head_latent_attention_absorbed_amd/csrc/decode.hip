@@ -19,9 +19,9 @@
 // so the accumulator rescale is rare.  A work-group of NW waves shares each
 // tile; tiles stream through an LDS ring (direct global->LDS DMA for bf16;
 // for fp8 the same DMA into a staging slot, then an exact e4m3->bf16 decode
-// in LDS).  The token axis of the whole batch is cut into G equal parts;
-// each (part, sequence) pair writes one normalised partial and its
-// log-sum-exp.
+// in LDS).  Each sequence's token axis is cut into parts of W tiles (the
+// split plan of split_plan.h); each part writes one normalised partial and
+// its log-sum-exp.
 //
 // The tile products, the online softmax and the LDS tile layout are in
 // tile_ops.h (shared with the prefill).
@@ -30,6 +30,8 @@
 #include "mla_device.h"
 #include "mla_kernels.h"
 #include "tile_ops.h"
+#include "decode_common.h"
+#include "split_plan.h"
 
 namespace mla {
 namespace {
@@ -43,37 +45,6 @@ __device__ __forceinline__ int seq_of_tile(const int* cu, int B, int k) {
     if (cu[mid] <= k) lo = mid; else hi = mid - 1;
   }
   return lo;
-}
-
-template <int NI, int MAXLATER>
-__device__ __forceinline__ void wait_dma_groups(int later) {
-  // Tiles complete in issue order; `later` (<= MAXLATER) DMA groups of NI
-  // loads were issued after the one being waited for.
-  static_assert(NI * MAXLATER <= 63, "vmcnt range");
-  if constexpr (MAXLATER == 0) {
-    vm_wait<0>();
-  } else if constexpr (MAXLATER == 1) {
-    if (later <= 0) vm_wait<0>(); else vm_wait<NI>();
-  } else {
-    static_assert(MAXLATER == 2, "ring depth");
-    if (later <= 0) vm_wait<0>();
-    else if (later == 1) vm_wait<NI>();
-    else vm_wait<NI * 2>();
-  }
-}
-
-
-
-// The token a lane moves in every tile-load instruction: slot lane % 32 of
-// row 2m + lane / 32 holds token (lane % 32) ^ (4 * (lane / 32)).
-__device__ __forceinline__ int load_token(int lane) { return (lane & 31) ^ ((lane >> 5) << 2); }
-
-// Byte offset of granule row pair (g0, g0+1) inside a cache record (GB-byte
-// granules: 16 for bf16, 8 for e4m3).  g0 is even, so a pair never straddles
-// the latent and the RoPE key.
-template <int DC, int GB>
-__device__ __forceinline__ int64_t granule_offset(const DecodeParams& p, int g0) {
-  return g0 < Geo<DC>::GC ? (int64_t)g0 * GB : p.rope_off + (int64_t)(g0 - Geo<DC>::GC) * GB;
 }
 
 // Issue this wave's DMA loads of one tile.  `run` is the address of the
@@ -114,103 +85,6 @@ __device__ __forceinline__ void zero_tail(char* tb, int nv, int tid) {
   for (int i = tid; i < Geo<DC>::GPT * kTile; i += NW * kWave) {
     const int g = i >> 5, slot = i & 31;
     if ((slot ^ ((g & 1) << 2)) >= nv) *(uint4*)(tb + g * kRow + slot * 16) = uint4{0, 0, 0, 0};
-  }
-}
-
-// fp8 tile: the records' e4m3 bytes are copied with global->LDS DMA into a
-// staging slot (row pair m = bytes 16m..16m+15 of the latent, then of the
-// RoPE key, of token t at byte (32 m + t) * 16), so nothing is held in
-// registers while the previous tile is computed; then every thread decodes
-// its share exactly (every e4m3 value is a bf16 value) into the bf16 tile
-// layout, tokens past the length as zeros.
-template <int DC>
-struct Fp8Geo {
-  static constexpr int NP = Geo<DC>::GPT / 2;      // row pairs of a tile
-  static constexpr int NINS = NP / 2;              // DMA instructions (two pairs each)
-  static constexpr int BYTES = NP * kTile * 16;    // staging slot
-};
-
-template <int DC, int NW>
-__device__ __forceinline__ void issue_fp8_dma(const DecodeParams& p, const char* run, uint32_t stage_lds, int w) {
-  using F = Fp8Geo<DC>;
-  const int ol = opaque_lane();
-  const uint32_t lane_off = (uint32_t)(ol & 31) * (uint32_t)p.token_stride + 16u * (ol >> 5);
-#pragma unroll
-  for (int q = 0; q < (F::NINS + NW - 1) / NW; ++q) {
-    const int ins = q * NW + w;
-    if (ins < F::NINS) {
-      const int m0 = 2 * ins;  // pairs m0, m0 + 1 never straddle the latent and the RoPE key
-      const int64_t off = m0 < Geo<DC>::GC / 2 ? (int64_t)m0 * 16 : p.rope_off + (int64_t)(m0 - Geo<DC>::GC / 2) * 16;
-      lds_dma16(run + off, lane_off, uniform(stage_lds + ins * 1024));
-    }
-  }
-}
-
-template <int DC, int NW>
-__device__ __forceinline__ void convert_fp8_tile(const char* stage, char* tb, int nv, int tid) {
-  using F = Fp8Geo<DC>;
-  for (int i = tid; i < F::NP * kTile; i += NW * kWave) {
-    const int m = i >> 5, t = i & 31;
-    const uint4 x = *(const uint4*)(stage + i * 16);
-    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false);
-    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true);
-    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false);
-    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true);
-    const bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.z, 1.0f, false);
-    const bf16x2 f = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.z, 1.0f, true);
-    const bf16x2 g = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.w, 1.0f, false);
-    const bf16x2 h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.w, 1.0f, true);
-    bf16x8 lo = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};  // granule row 2m
-    bf16x8 hi = {e[0], e[1], f[0], f[1], g[0], g[1], h[0], h[1]};  // granule row 2m + 1
-    if (t >= nv) {
-      lo = bf16x8{};
-      hi = bf16x8{};
-    }
-    *(bf16x8*)(tb + (2 * m) * kRow + (t << 4)) = lo;            // even row: slot t
-    *(bf16x8*)(tb + (2 * m + 1) * kRow + ((t ^ 4) << 4)) = hi;  // odd row: slot t ^ 4
-  }
-}
-
-// Write NBK accumulator blocks (32 latent columns each, starting at element
-// offset `base` of o_part) scaled by inv, as fp16 or fp32.
-template <int NBK>
-__device__ __forceinline__ void store_partial(const DecodeParams& p, const f32x16* O, float inv, int64_t base,
-                                              int half) {
-  if (p.o_half) {
-    // Lane pair (l, l + 32) swaps packed halves so that each lane stores 8
-    // consecutive columns: with column quarters q0..q3 of an 8-column group
-    // split 4 + 4 over the pair, the swap gives the lower lane the odd group
-    // and the upper lane the even one.
-    _Float16* dst = (_Float16*)p.o_part + base + 8 * (1 - half);
-#pragma unroll
-    for (int nb = 0; nb < NBK; ++nb) {
-      uint32_t h[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const f16x2 v = {(_Float16)(O[nb][2 * j] * inv), (_Float16)(O[nb][2 * j + 1] * inv)};
-        h[j] = __builtin_bit_cast(uint32_t, v);
-      }
-#pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {  // 8-column groups (2pr, 2pr + 1)
-        const auto r0 = __builtin_amdgcn_permlane32_swap(h[4 * pr + 2], h[4 * pr], false, false);
-        const auto r1 = __builtin_amdgcn_permlane32_swap(h[4 * pr + 3], h[4 * pr + 1], false, false);
-        const uint4 v = {r0[0], r1[0], r0[1], r1[1]};
-        *(uint4*)(dst + 32 * nb + 16 * pr) = v;
-      }
-      __builtin_amdgcn_sched_barrier(0);  // one accumulator block at a time
-    }
-  } else {
-    float* dst = (float*)p.o_part + base + 4 * half;
-#pragma unroll
-    for (int nb = 0; nb < NBK; ++nb) {
-#pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        const f32x4 v = {O[nb][4 * ig] * inv, O[nb][4 * ig + 1] * inv, O[nb][4 * ig + 2] * inv,
-                         O[nb][4 * ig + 3] * inv};
-        *(f32x4*)(dst + 32 * nb + 8 * ig) = v;
-      }
-      __builtin_amdgcn_sched_barrier(0);  // one accumulator block at a time
-    }
   }
 }
 
@@ -289,13 +163,26 @@ __global__ void __launch_bounds__(NW * kWave)
   if ((gridDim.x & 7) == 0) u = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   const int g = u / p.RG, rg = u % p.RG;
 
-  if (w == 0) build_tile_prefix(seq_lens, p.B, cu, lane);
+  // The split plan: part g is tiles [j W, min((j + 1) W, n_b)) of one
+  // sequence b; k0 .. k1 are those tiles in the batch-wide tile numbering.
+  __shared__ int plan[3];
+  if (w == 0) {
+    build_tile_prefix(seq_lens, p.B, cu, lane);
+    WavePlan pl;
+    pl.build(seq_lens, p.B, p.P, lane);
+    int b = -1, s_b = 0;
+    if (g < pl.total) pl.locate_slot(g, lane, b, s_b);
+    if (lane == 0) {
+      plan[0] = b;
+      plan[1] = (g - s_b) * pl.W;
+      plan[2] = pl.W;
+    }
+  }
   block_sync();
-  const int N = uniform(cu[p.B]);
-  const int Wt = (N + p.G - 1) / p.G;
-  const int k0 = g * Wt;
-  const int k1 = min(k0 + Wt, N);
-  if (k0 >= k1) return;
+  const int pb = uniform(plan[0]);
+  if (pb < 0) return;
+  const int k0 = uniform(cu[pb]) + uniform(plan[1]);
+  const int k1 = min(k0 + uniform(plan[2]), uniform(cu[pb + 1]));
 
   const int row = rg * (32 * NW) + 32 * w + col;  // this lane's query row (S^T column)
   const uint32_t tiles_lds = lds_offset(tiles);
@@ -489,7 +376,7 @@ __global__ void __launch_bounds__(NW * kWave)
     const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -__builtin_inff();
-    const int64_t slot = (int64_t)bc + g;
+    const int64_t slot = g;
     // The lse goes first: vector stores count in vmcnt, so any wait the
     // compiler places before a later store (a spilled address being reloaded)
     // would otherwise also wait for the whole partial to be written.
@@ -518,7 +405,7 @@ __global__ void __launch_bounds__(NW * kWave)
 
 template <int DC, bool FP8, int NW, int NBUF>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
-  const int grid = p.G * p.RG;
+  const int grid = p.P * p.RG;
   hipLaunchKernelGGL((decode_kernel<DC, FP8, NW, NBUF>), dim3(grid), dim3(NW * kWave), 0, stream, p,
                      p.seq_lens, p.block_table, p.kv_scale);
   return hipGetLastError();

@@ -136,7 +136,7 @@ mla_status_t mla_decode_num_parts(const mla_shape_t* shape, int32_t* num_parts) 
   const int R = shape->q_len * shape->num_heads;
   const int wgs = cus * mla::decode_wgs_per_cu(R, shape->d_latent);
   const int G = std::max(1, wgs / mla::decode_row_groups(R));
-  *num_parts = G + shape->batch - 1;
+  *num_parts = std::max(G, shape->batch);
   return ok();
 }
 
@@ -182,14 +182,14 @@ mla_status_t mla_decode_paged(const mla_shape_t* shape, const void* q_lat, const
   p.S = shape->q_len;
   p.R = shape->q_len * shape->num_heads;
   p.RG = mla::decode_row_groups(p.R);
-  p.G = num_parts - shape->batch + 1;
+  p.P = num_parts;
   p.block_size = shape->block_size;
   p.block_shift = __builtin_ctz((unsigned)shape->block_size);
   p.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
   p.o_part = o_part;
   p.o_half = shape->partial_dtype == MLA_FP16;
   p.lse_part = lse_part;
-  if ((int64_t)p.G * p.RG > (int64_t)1 << 30) return fail(MLA_ERR_UNSUPPORTED, "too many decode work-groups");
+  if ((int64_t)p.P * p.RG > (int64_t)1 << 30) return fail(MLA_ERR_UNSUPPORTED, "too many decode work-groups");
   return hip_status(mla::launch_decode(p, shape->d_latent, fp8, stream), "mla_decode_paged launch");
 }
 
@@ -210,7 +210,7 @@ mla_status_t mla_combine_lse(const mla_shape_t* shape, int32_t num_parts, const 
   p.seq_lens = seq_lens;
   p.B = shape->batch;
   p.R = shape->q_len * shape->num_heads;
-  p.G = num_parts - shape->batch + 1;
+  p.P = num_parts;
   p.DC = shape->d_latent;
   p.o_lat = o_lat;
   p.lse = lse;
@@ -263,7 +263,7 @@ mla_status_t mla_combine_up_v(const mla_shape_t* shape, int32_t num_parts, const
   p.B = shape->batch;
   p.S = shape->q_len;
   p.H = shape->num_heads;
-  p.G = num_parts - shape->batch + 1;
+  p.P = num_parts;
   p.DC = shape->d_latent;
   p.NV = shape->d_v;
   return hip_status(mla::launch_combine_up(p, stream), "mla_combine_up_v launch");

@@ -22,7 +22,7 @@ struct DecodeParams {
   int32_t bt_stride;         // entries per block_table row
   int32_t B, H, S, R;        // batch, heads, query tokens, rows = S * H
   int32_t RG;                // row groups (work-groups sharing one token range)
-  int32_t G;                 // token parts
+  int32_t P;                 // partial slots (the split plan's budget of parts)
   int32_t block_size;        // tokens per page: 32 * 2^k
   int32_t block_shift;       // log2(block_size)
   float scale_log2;          // softmax_scale * log2(e)
@@ -115,7 +115,7 @@ struct CombineParams {
   int32_t o_half;
   const float* lse_part;
   const int32_t* seq_lens;
-  int32_t B, R, G, DC;
+  int32_t B, R, P, DC;       // P: partial slots, as given to the decode
   float* o_lat;              // fp32 [B, R, DC]
   float* lse;                // fp32 [B, R]
 };
@@ -133,7 +133,7 @@ struct CombineUpParams {
   void* out;                 // bf16 or fp32 [B*S, H, NV]
   int32_t out_f32;
   float* lse;                // fp32 [B*S, H]
-  int32_t B, S, H, G, DC, NV;
+  int32_t B, S, H, P, DC, NV;  // P: partial slots, as given to the decode
 };
 
 // Whether the fused kernel exists for this latent rank and value width.

@@ -26,26 +26,25 @@ def combine_up_supported(d_latent: int, d_v: int) -> bool:
 
 def split_plan(seq_lens, num_parts: int, tile: int = MLA_TILE_TOKENS):
     """The documented split plan of mla_decode_paged: a list of
-    (slot, sequence, first position, end position) for every partial written."""
+    (slot, sequence, first position, end position) for every partial written.
+    W is the fewest tiles per part for which the sequences' parts,
+    ceil(n_b / W) each, fit in num_parts slots; sequence b's parts take
+    consecutive slots in sequence order."""
     lens = [int(x) for x in seq_lens]
-    B = len(lens)
+    if num_parts < len(lens):
+        raise ValueError("num_parts must be at least the batch size")
     n = [(L + tile - 1) // tile if L > 0 else 0 for L in lens]
-    cu = [0]
-    for x in n:
-        cu.append(cu[-1] + x)
-    N = cu[-1]
-    G = num_parts - B + 1
-    if N == 0:
+    if sum(n) == 0:
         return []
-    W = (N + G - 1) // G
-    plan = []
-    for b in range(B):
-        if n[b] == 0:
-            continue
-        for g in range(cu[b] // W, (cu[b + 1] - 1) // W + 1):
-            lo = max(cu[b], g * W) - cu[b]
-            hi = min(cu[b + 1], (g + 1) * W) - cu[b]
-            plan.append((b + g, b, lo * tile, min(hi * tile, lens[b])))
+    W = 1
+    while sum((x + W - 1) // W for x in n) > num_parts:
+        W += 1
+    plan, slot = [], 0
+    for b, nb in enumerate(n):
+        for j in range((nb + W - 1) // W):
+            t0, t1 = j * W, min((j + 1) * W, nb)
+            plan.append((slot, b, t0 * tile, min(t1 * tile, lens[b])))
+            slot += 1
     return plan
 
 

@@ -107,8 +107,8 @@ mla_status_t mla_absorb_q(const mla_shape_t* shape, const void* q_nope, const vo
 /*
  * mla_decode_num_parts -- host query: how many partial slots mla_decode_paged
  * should use on the current device (o_part / lse_part are sized by it).  The
- * value is (token parts) + B - 1, where the token-part count fills the
- * device's compute units.  Any value >= B may be passed to the decode and
+ * value is max(B, the number of decode work-groups that fill the device's
+ * compute units once).  Any value >= B may be passed to the decode and
  * combine calls instead; it only changes how the token axis is split.
  */
 mla_status_t mla_decode_num_parts(const mla_shape_t* shape, int32_t* num_parts);
@@ -137,12 +137,13 @@ mla_status_t mla_decode_num_parts(const mla_shape_t* shape, int32_t* num_parts);
  *
  * Split plan (so that callers and tests can reproduce it; R = S_q * H rows,
  * row r = s*H + h):
- *   n_b = ceil(L_b / MLA_TILE_TOKENS), cu_0 = 0, cu_{b+1} = cu_b + n_b, N = cu_B
- *   G = num_parts - B + 1 token parts, W = ceil(N / G) tiles per part
- *   part g covers global tiles [g*W, min((g+1)*W, N)); for each sequence b it
- *   touches it writes slot (b + g): the partial over positions
- *   [max(cu_b, g*W) - cu_b, min(cu_{b+1}, (g+1)*W) - cu_b) * MLA_TILE_TOKENS,
- *   clipped to what each query may see.
+ *   n_b = ceil(L_b / MLA_TILE_TOKENS) tiles in sequence b (0 if idle)
+ *   W   = the smallest W >= 1 with sum_b ceil(n_b / W) <= num_parts
+ *   p_b = ceil(n_b / W) parts of sequence b, in slots s_b .. s_b + p_b - 1,
+ *         s_b = sum_{b' < b} p_{b'} (sequence order)
+ *   part j of sequence b (slot s_b + j) is the partial over positions
+ *   [j*W, min((j+1)*W, n_b)) * MLA_TILE_TOKENS, clipped to L_b and to what
+ *   each query may see.  A part never spans two sequences.
  * o_part   [num_parts, R, d_latent] in shape->partial_dtype: sum_t p_t c_t,
  *          normalised within the split (a convex combination of latent rows).
  *          MLA_FP16 (round to nearest even) halves the bytes written here and

@@ -158,6 +158,14 @@ def test_split_plan_covers_every_tile_once():
     lens = [0, 1, 31, 32, 33, 700, 0, 64]
     for parts in (8, 9, 12, 40, 300):
         plan = split_plan(lens, parts)
+        # parts never cross a sequence, take consecutive slots in sequence order,
+        # and W is the smallest tile count per part that fits the slots
+        assert [s for s, *_ in plan] == list(range(len(plan)))
+        assert [b for _, b, *_ in plan] == sorted(b for _, b, *_ in plan)
+        W = max((t1 - t0 + 31) // 32 for _, _, t0, t1 in plan)
+        n = [(L + 31) // 32 for L in lens]
+        assert sum(-(-x // W) for x in n) <= parts
+        assert W == 1 or sum(-(-x // (W - 1)) for x in n) > parts
         covered = {b: [] for b in range(len(lens))}
         slots = set()
         for slot, b, t0, t1 in plan:

@@ -111,7 +111,8 @@ def test_small_parity_fp32_partials(name, merge):
 @pytest.mark.parametrize("name", ["h128_ragged", "dc256", "fp8_sq4_h64", "h32"])
 @pytest.mark.parametrize("extra_parts", [0, 1, 5])
 def test_small_parity_few_splits(name, extra_parts, merge):
-    """Few token parts: each part runs many tiles and spans sequence boundaries."""
+    """Few token parts: each part runs many tiles (num_parts = B gives one
+    part per sequence, its whole length)."""
     inputs = make_inputs(SMALL_CASES[name])
     B = inputs["workload"].batch
     _announce(f"{name}+{extra_parts}/{merge}", inputs)
