@@ -113,14 +113,14 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineParams p, const int
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.x;
   if (w == 0) {
-    WavePlan pl;
-    pl.build(seq_lens, p.B, p.P, lane);
-    int s_b, p_b;
-    pl.slots_of(b, lane, s_b, p_b);
-    if (lane == 0) {
-      slots[0] = s_b;
-      slots[1] = p_b;
-    }
+    with_plan(seq_lens, p.B, p.P, lane, [&](const auto& pl) {
+      int s_b, p_b;
+      pl.slots_of(b, lane, s_b, p_b);
+      if (lane == 0) {
+        slots[0] = s_b;
+        slots[1] = p_b;
+      }
+    });
   }
   __syncthreads();
   const int row = blockIdx.y * 4 + w;
@@ -201,11 +201,7 @@ __global__ void __launch_bounds__(1024) combine_up_kernel(CombineUpParams p) {
   const int m0 = (blockIdx.x / H) * kUpRows;
 
   // Split plan first (wave 0), so that its loads are not queued behind the DMA.
-  if (w == 0) {
-    WavePlan pl;
-    pl.build(p.seq_lens, p.B, p.P, lane);
-    pl.write_slot_prefix(sb, lane);
-  }
+  if (w == 0) with_plan(p.seq_lens, p.B, p.P, lane, [&](const auto& pl) { pl.write_slot_prefix(sb, lane); });
 
   // W_UV[h] rows kr*KW .. kr*KW + KW-1 into slice kr: LDS granule position q
   // of row k holds global granule q ^ swz(k).  Wave (kr, nq) copies pieces

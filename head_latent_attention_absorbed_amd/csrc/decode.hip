@@ -168,15 +168,15 @@ __global__ void __launch_bounds__(NW * kWave)
   __shared__ int plan[3];
   if (w == 0) {
     build_tile_prefix(seq_lens, p.B, cu, lane);
-    WavePlan pl;
-    pl.build(seq_lens, p.B, p.P, lane);
-    int b = -1, s_b = 0;
-    if (g < pl.total) pl.locate_slot(g, lane, b, s_b);
-    if (lane == 0) {
-      plan[0] = b;
-      plan[1] = (g - s_b) * pl.W;
-      plan[2] = pl.W;
-    }
+    with_plan(seq_lens, p.B, p.P, lane, [&](const auto& pl) {
+      int b = -1, s_b = 0;
+      if (g < pl.total) pl.locate_slot(g, lane, b, s_b);
+      if (lane == 0) {
+        plan[0] = b;
+        plan[1] = (g - s_b) * pl.W;
+        plan[2] = pl.W;
+      }
+    });
   }
   block_sync();
   const int pb = uniform(plan[0]);
@@ -411,20 +411,12 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Four-wave groups (128 query rows) run one work-group per CU on a 4-tile
-// ring (bf16; 2 for the staged fp8 path).  One- and two-wave groups run two
-// work-groups per CU on a 2-tile ring.
+// One- and two-wave groups (up to 64 query rows) run two work-groups per CU
+// on a 2-tile ring; 128-row groups use decode_wide.hip.
 template <int DC, bool FP8>
 hipError_t launch_dc(const DecodeParams& p, int nw, hipStream_t stream) {
-  if constexpr (FP8) {
-    if (nw == 4) return launch_one<DC, FP8, 4, 2>(p, stream);
-    if (nw == 2) return launch_one<DC, FP8, 2, 2>(p, stream);
-    return launch_one<DC, FP8, 1, 2>(p, stream);
-  } else {
-    if (nw == 4) return launch_one<DC, FP8, 4, 4>(p, stream);
-    if (nw == 2) return launch_one<DC, FP8, 2, 2>(p, stream);
-    return launch_one<DC, FP8, 1, 2>(p, stream);
-  }
+  if (nw == 2) return launch_one<DC, FP8, 2, 2>(p, stream);
+  return launch_one<DC, FP8, 1, 2>(p, stream);
 }
 
 }  // namespace
@@ -441,6 +433,7 @@ int decode_wgs_per_cu(int R, int d_latent) {
 
 hipError_t launch_decode(const DecodeParams& p, int d_latent, bool fp8, hipStream_t stream) {
   const int nw = decode_waves(p.R);
+  if (nw == 4) return launch_decode_wide(p, d_latent, fp8, stream);
   if (d_latent == 512) return fp8 ? launch_dc<512, true>(p, nw, stream) : launch_dc<512, false>(p, nw, stream);
   return fp8 ? launch_dc<256, true>(p, nw, stream) : launch_dc<256, false>(p, nw, stream);
 }

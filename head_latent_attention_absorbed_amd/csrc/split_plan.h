@@ -28,10 +28,11 @@ __device__ __forceinline__ int wave_max(int x) {
 }
 
 // The plan as one wave sees it: lane l holds the tile counts of sequences
-// l, l + 64, ... (at most kMaxBatch / 64 of them).
-struct WavePlan {
-  static constexpr int CH = kMaxBatch / kWave;
-  int n[CH];
+// l, l + 64, ... (at most CH * 64 of them; WavePlanFor picks CH = 1 when
+// the batch fits one wave, which keeps the search short).
+template <int CH>
+struct WavePlanN {
+  int n[CH], len[CH];
   int B, nch, W, total;
 
   // Loads the lengths and finds W for P slots (P >= B).  All lanes of one wave.
@@ -42,9 +43,11 @@ struct WavePlan {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       n[c] = 0;
+      len[c] = 0;
       if (c < nch) {
         const int b = c * kWave + lane;
         const int L = b < B ? seq_lens[b] : 0;
+        len[c] = L;
         n[c] = L > 0 ? (L + kTile - 1) / kTile : 0;
         N += n[c];
         nmax = max(nmax, n[c]);
@@ -154,6 +157,15 @@ struct WavePlan {
     }
   }
 
+  // Length of sequence b (wave-uniform b).
+  __device__ int length(int b) const {
+    int v = 0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (c < nch && b >= c * kWave && b < (c + 1) * kWave) v = __shfl(len[c], b - c * kWave);
+    return v;
+  }
+
   // Tiles of sequence b (wave-uniform b).
   __device__ int tiles(int b, int lane) const {
     int v = 0;
@@ -164,5 +176,21 @@ struct WavePlan {
     return v;
   }
 };
+
+using WavePlan = WavePlanN<kMaxBatch / kWave>;
+
+// Runs f(plan) with the plan of the batch built by the calling wave.
+template <class F>
+__device__ __forceinline__ void with_plan(const int32_t* __restrict__ seq_lens, int B, int P, int lane, F&& f) {
+  if (B <= kWave) {
+    WavePlanN<1> pl;
+    pl.build(seq_lens, B, P, lane);
+    f(pl);
+  } else {
+    WavePlan pl;
+    pl.build(seq_lens, B, P, lane);
+    f(pl);
+  }
+}
 
 }  // namespace mla
