@@ -62,7 +62,91 @@ def algorithmic(w, seq_lens):
                 step_flops=attn_flops + proj_flops, record_bytes=rec, tokens=sum(L))
 
 
-KERNEL_SOURCES = ("decode.hip", "tile_ops.h", "mla_device.h", "mla_kernels.h")
+KERNEL_SOURCES = ("decode.hip", "decode_wide.hip", "decode_common.h", "split_plan.h", "tile_ops.h", "mla_device.h",
+                  "mla_kernels.h")
+RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # 312.5
+
+
+def decode_kernel_name(w) -> str:
+    return "decode_wide_kernel" if w.q_len * w.heads > 64 else "decode_kernel"
+
+
+def roofline_of(alg, us, measured=None):
+    """The decode launch against the roofline that bounds it: HBM when its
+    algorithmic flops per byte are below the ridge of the nominal peaks
+    (bf16 MFMA over HBM), bf16 MFMA above it (the e4m3 cache is decoded to
+    bf16, so its products run at the bf16 rate).  The other fraction is
+    given beside it, and each against the measured peaks when there are any."""
+    gbs = alg["decode_bytes"] / (us * 1e-6) / 1e9
+    tflops = alg["attn_flops"] / (us * 1e-6) / 1e12
+    ai = alg["attn_flops"] / alg["decode_bytes"]
+    r = {"flop_per_byte": round(ai, 1)}
+    if ai > RIDGE_FLOP_PER_BYTE:
+        r.update(bound="mfma", achieved=round(tflops, 1), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                 frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+    else:
+        r.update(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                 frac=round(gbs / HBM_PEAK_GBS, 4), mfma_frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4))
+    if measured:
+        r["frac_of_measured_hbm"] = round(gbs / measured["hbm_read_gbs"], 4)
+        r["frac_of_measured_mfma"] = round(tflops / measured["mfma_bf16_tflops"], 4)
+    return r
+
+
+def measured_peaks(torch, stream, reps: int = 5):
+    """Reference points measured on this GPU: a streaming read of 2 GiB (a
+    sum reduction of fp32, whose bytes are all reads) and a bf16 GEMM of
+    8192^3 on the device's BLAS; medians over reps, HIP events."""
+    import numpy as np
+
+    x = torch.ones((2 << 30) // 4, dtype=torch.float32, device="cuda")
+    a = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    b = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    for _ in range(2):
+        x.sum()
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    t_read, t_mm = [], []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        x.sum()
+        e[1].record(stream)
+        torch.matmul(a, b)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        t_read.append(e[0].elapsed_time(e[1]) * 1e-3)
+        t_mm.append(e[1].elapsed_time(e[2]) * 1e-3)
+    res = {"hbm_read_gbs": round(x.numel() * 4 / float(np.median(t_read)) / 1e9, 1),
+           "mfma_bf16_tflops": round(2 * 8192 ** 3 / float(np.median(t_mm)) / 1e12, 1),
+           "how": "torch sum over 2 GiB fp32 (read rate); torch.matmul bf16 8192x8192x8192 (hipBLASLt); "
+                  f"medians of {reps}"}
+    del x, a, b
+    torch.cuda.empty_cache()
+    return res
+
+
+def host_info():
+    """CPU model and the BLAS library numpy uses (for the CPU baseline)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
+            threads = max(int(i.get("num_threads", 1)) for i in info)
+    except Exception:
+        pass
+    return model, blas, threads
 
 
 def kernel_source_hash() -> str:
@@ -285,7 +369,7 @@ def leg_gqla(torch, np, stream, K, args):
 DECODE_WORKLOADS = ("tiny", "deepseek_v3", "gqa7b", "tpla_shard", "kimi_k2_fp8")
 
 
-def leg_configs(torch, np, stream, K, args, exclude):
+def leg_configs(torch, np, stream, K, args, exclude, measured=None):
     """The decode step on every other decode workload, with HIP events
     between the calls of an eager loop (absorb, decode, merge with the
     up-projection).  Consecutive steps rotate through input replicas that
@@ -327,7 +411,6 @@ def leg_configs(torch, np, stream, K, args, exclude):
         step = t.sum(axis=1)
         dec_mean = float(t[:, 1].mean())
         med = np.median(t, axis=0)
-        achieved = alg["decode_bytes"] / (dec_mean * 1e-6) / 1e9
         res[name] = {
             "batch": w.batch, "heads": w.heads, "q_len": w.q_len, "d_latent": w.d_latent, "cache": w.cache_dtype,
             "tokens": alg["tokens"], "cache_bytes": alg["cache_bytes"], "replicas": nrep, "cold": nrep >= need,
@@ -338,10 +421,7 @@ def leg_configs(torch, np, stream, K, args, exclude):
                                    "merge_up": round(float(med[2]), 2)},
             "tbs_decode_merge": round(alg["cache_bytes"] / ((med[1] + med[2]) * 1e-6) / 1e12, 4),
             "tbs_step": round(alg["cache_bytes"] / (float(np.median(step)) * 1e-6) / 1e12, 4),
-            "decode_roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                                "mfma_frac": round(alg["attn_flops"] / (dec_mean * 1e-6) / 1e12
-                                                   / MFMA_BF16_PEAK_TFLOPS, 4)},
+            "decode_roofline": dict(kernel=decode_kernel_name(w), **roofline_of(alg, dec_mean, measured)),
         }
         log(f"configs: {name} step {res[name]['us_per_step']['median']} us, decode {med[1]:.1f} us")
         del steps, inputs
@@ -520,11 +600,12 @@ def main():
     prefill_res = leg_prefill(torch, np, stream, K) if run_legs else None
     tpla_res = leg_tpla(torch, np, stream, K, args, w, inputs, alg, steps[0]) if run_legs else None
     gqla_res = leg_gqla(torch, np, stream, K, args) if run_legs else None
-    configs_res = leg_configs(torch, np, stream, K, args, w.name) if run_legs and not args.no_configs else None
+    measured = measured_peaks(torch, stream) if run_legs else None
+    configs_res = (leg_configs(torch, np, stream, K, args, w.name, measured)
+                   if run_legs and not args.no_configs else None)
 
     us_step = ms_per_step * 1e3
     value = alg["cache_bytes"] / (us_step * 1e-6) / 1e12
-    achieved = alg["decode_bytes"] / (dec_us * 1e-6) / 1e9
     result = {
         "metric": "decode-attn us/step + effective latent-cache TB/s, B=32 H=128 ctx 8K",
         "value": round(value, 4),
@@ -559,18 +640,15 @@ def main():
         "per_call_us_median": {k: round(v, 2) for k, v in med.items()},
         "tbs_decode_merge": round(alg["cache_bytes"] / (sum(med[c] for c in calls[1:]) * 1e-6) / 1e12, 4),
         "step_hbm_frac": round(value * 1e3 / HBM_PEAK_GBS, 4),
-        "roofline": {
-            "kernel": "decode_kernel (mla_decode_paged)",
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w.name) if args.partial == "fp16" else None,
-            "algorithmic_bytes_per_launch": alg["decode_bytes"],
-            "avg_launch_us": round(dec_us, 2),
-            "mfma_frac": round(alg["attn_flops"] / (dec_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-        },
+        "roofline": dict(
+            kernel=f"{decode_kernel_name(w)} (mla_decode_paged)",
+            **roofline_of(alg, dec_us, measured),
+            traffic=measured_traffic(w.name) if args.partial == "fp16" else None,
+            algorithmic_bytes_per_launch=alg["decode_bytes"],
+            algorithmic_flops_per_launch=alg["attn_flops"],
+            avg_launch_us=round(dec_us, 2),
+        ),
+        "measured_peaks": measured,
         "wall_s": round(wall, 3),
         "append": {
             "what": "mla_append_kv: new tokens' [c_KV | k_rope] records from x [B*S_q, d_model] "
@@ -591,15 +669,12 @@ def main():
         copy_probe(args.copy_probe_mb)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(inputs, args.cpu_budget)
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max(int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas")
-        except Exception:
-            threads = len(os.sched_getaffinity(0))
+        model, blas, threads = host_info()
         result["cpu_baseline"] = {
             "value": round(cb["value"], 8), "unit": "TB/s", "cores": threads, "kind": "oracle",
             "sample": f"{cb['sequences']} of {w.batch} sequences ({cb['tokens']} tokens, all {w.heads} heads) "
                       f"in {cb['seconds']:.1f}s, numpy fp64 explicit K/V reconstruction",
+            "cpu": model, "blas": blas,
         }
     print(json.dumps(result), flush=True)
 

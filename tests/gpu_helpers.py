@@ -50,17 +50,47 @@ def compare(name, got, ref, tol_abs, tol_rel, finite_only=False, scaled_abs=True
     return max_abs, rel
 
 
-def run_step(inputs, num_parts=None, poison=True, partial="fp16", fused=None):
+GUARD_ELEMS = 256  # guard elements before and after each output (>= 16 bytes, keeps alignment)
+
+
+def _guarded(t):
+    """A copy of tensor t's shape and dtype inside a larger allocation with
+    GUARD_ELEMS elements before and after it, filled with a sentinel pattern.
+    Returns (view, guards)."""
+    import torch
+
+    base = torch.empty(t.numel() + 2 * GUARD_ELEMS, dtype=t.dtype, device=t.device)
+    base.view(torch.uint8).fill_(0xA5)
+    view = base[GUARD_ELEMS: GUARD_ELEMS + t.numel()].view(t.shape)
+    return view, (base[:GUARD_ELEMS], base[GUARD_ELEMS + t.numel():])
+
+
+def run_step(inputs, num_parts=None, poison=True, partial="fp16", fused=None, guard=True):
     """One step through the C ABI; ``fused`` None takes the step's default
-    (merge and up-projection in one launch where a kernel exists)."""
+    (merge and up-projection in one launch where a kernel exists).  With
+    ``guard`` every buffer the step writes sits between two guard regions of
+    a sentinel byte pattern, which must be untouched afterwards (writes stay
+    inside their tensors)."""
     import torch
     from head_latent_attention_absorbed_amd import DecodeStep
 
     st = DecodeStep(inputs, num_parts=num_parts, partial=partial, fused=fused)
+    guards = {}
+    if guard:
+        for name in ("q_lat", "o_part", "lse_part", "o_lat", "lse", "out"):
+            t = getattr(st, name)
+            if t is not None:
+                view, g = _guarded(t)
+                setattr(st, name, view)
+                guards[name] = g
     if poison:
         for t in (st.q_lat, st.o_part, st.lse_part, st.o_lat, st.lse, st.out):
             if t is not None:
                 t.fill_(float("nan"))
     st.run()
     torch.cuda.synchronize()
+    for name, (lo, hi) in guards.items():
+        for side, g in (("before", lo), ("after", hi)):
+            bytes_ = g.view(torch.uint8).cpu().numpy()
+            assert np.all(bytes_ == 0xA5), f"{name}: {np.count_nonzero(bytes_ != 0xA5)} guard bytes {side} it changed"
     return st

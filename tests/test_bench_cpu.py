@@ -75,3 +75,22 @@ def test_traffic_counts_only_for_matching_sources(monkeypatch, tmp_path):
 @pytest.mark.parametrize("name", bench.KERNEL_SOURCES)
 def test_hashed_sources_exist(name):
     assert os.path.exists(os.path.join(ROOT, "head_latent_attention_absorbed_amd", "csrc", name))
+
+
+def test_roofline_bound_follows_the_ridge():
+    """The headline workload (about 242 flop/B) is reported against HBM, the
+    4-token e4m3 workload (about 960 flop/B) against the bf16 MFMA peak."""
+    from workloads.generate import make_inputs
+    for name, bound in (("deepseek_v3", "hbm"), ("kimi_k2_fp8", "mfma")):
+        w = get_workload(name)
+        a = bench.algorithmic(w, make_inputs(w, poison=False)["seq_lens"])
+        r = bench.roofline_of(a, 100.0, {"hbm_read_gbs": 6000.0, "mfma_bf16_tflops": 2000.0})
+        assert r["bound"] == bound, (name, r)
+        us = 100e-6
+        if bound == "hbm":
+            assert r["achieved"] == round(a["decode_bytes"] / us / 1e9, 1) and r["unit"] == "GB/s"
+            assert r["frac"] == round(r["achieved"] / bench.HBM_PEAK_GBS, 4)
+        else:
+            assert r["achieved"] == round(a["attn_flops"] / us / 1e12, 1) and r["unit"] == "TFLOP/s"
+            assert r["frac"] == round(r["achieved"] / bench.MFMA_BF16_PEAK_TFLOPS, 4)
+        assert r["frac_of_measured_hbm"] == round(a["decode_bytes"] / us / 1e9 / 6000.0, 4)
