@@ -433,24 +433,13 @@ __global__ void __launch_bounds__(256)
   // whose loop copies tile i + 2, tile 1 is copied after the first decode).
   int page_pf = 0;
   float sc0 = 0.0f, sc_next = 0.0f;  // fp8: wave 0's scales (lane < 32)
-  {
-    int pg[PRE];
+  // The page reads go out first and the query copies right behind them; the
+  // tile copies, which need the pages, are issued after the query's loads, so
+  // that the query's round trip overlaps the page read's.
+  int pg[PRE];
 #pragma unroll
-    for (int a = 0; a < PRE; ++a) pg[a] = a < n ? uniform(tile_page_load(p, bt, t0 + a)) : 0;
-    page_pf = PRE < n ? tile_page_load(p, bt, t0 + PRE) : 0;
-#pragma unroll
-    for (int a = 0; a < PRE; ++a) {
-      if (a < n) {
-        const TileSrc s = tile_src(p, pg[a], t0 + a, L);
-        if constexpr (!FP8) {
-          copy_tile<DC>(p, s, tiles_lds + a * TB, w);
-        } else {
-          copy_raw<DC>(p, s, raw_lds, w);
-          if (w == 0 && lane < kTile && lane < s.nv) sc0 = kv_scale[s.page_slot + lane];
-        }
-      }
-    }
-  }
+  for (int a = 0; a < PRE; ++a) pg[a] = a < n ? tile_page_load(p, bt, t0 + a) : 0;
+  page_pf = PRE < n ? tile_page_load(p, bt, t0 + PRE) : 0;
   {
     const int ol = opaque_lane();
     const int rr = ol / CPR, cs = ol % CPR;
@@ -473,6 +462,18 @@ __global__ void __launch_bounds__(256)
     for (int ks = KST; ks < DC / 16; ++ks) qf[ks] = ql[2 * ks];
 #pragma unroll
     for (int ks = DC / 16; ks < Gm::KS; ++ks) qf[ks] = qr[2 * (ks - DC / 16)];
+  }
+#pragma unroll
+  for (int a = 0; a < PRE; ++a) {
+    if (a < n) {
+      const TileSrc s = tile_src(p, uniform(pg[a]), t0 + a, L);
+      if constexpr (!FP8) {
+        copy_tile<DC>(p, s, tiles_lds + a * TB, w);
+      } else {
+        copy_raw<DC>(p, s, raw_lds, w);
+        if (w == 0 && lane < kTile && lane < s.nv) sc0 = kv_scale[s.page_slot + lane];
+      }
+    }
   }
   // The direct loads (and the scales) must be in registers before the loop;
   // the asm makes the compiler place that wait here, not inside the loop.

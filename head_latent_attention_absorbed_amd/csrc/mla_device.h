@@ -118,6 +118,35 @@ __device__ __forceinline__ float pair_sum(float x) {
 // bank groups (the transposing V-operand reads).
 __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
 
+// Wave-wide scans through DPP row shifts and row broadcasts (a few VALU
+// cycles each, where a shuffle through ds_bpermute waits on LDS): lane l gets
+// the inclusive scan of x over lanes 0..l.  Disabled lanes and sources past a
+// row's start keep the 0 passed as `old`, the identity of both operations
+// (the values scanned here are non-negative).
+template <class Op>
+__device__ __forceinline__ int wave_scan(int x, Op op) {
+  int v = x;
+  v = op(v, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = op(v, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = op(v, __builtin_amdgcn_update_dpp(0, x, 0x113, 0xf, 0xf, false));  // row_shr:3
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xe, false));  // row_shr:4, banks 1-3
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xc, false));  // row_shr:8, banks 2-3
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false));  // row_bcast:15, rows 1, 3
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false));  // row_bcast:31, rows 2, 3
+  return v;
+}
+struct AddOp {
+  __device__ __forceinline__ int operator()(int a, int b) const { return a + b; }
+};
+struct MaxOp {
+  __device__ __forceinline__ int operator()(int a, int b) const { return max(a, b); }
+};
+__device__ __forceinline__ int wave_incl_sum(int x) { return wave_scan(x, AddOp{}); }
+// Lane l's value of x, l wave-uniform (a scalar read, no LDS).
+__device__ __forceinline__ int lane_value(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+__device__ __forceinline__ int wave_sum(int x) { return lane_value(wave_scan(x, AddOp{}), kWave - 1); }
+__device__ __forceinline__ int wave_max(int x) { return lane_value(wave_scan(x, MaxOp{}), kWave - 1); }
+
 // Sequence tile bookkeeping shared by the decode and combine kernels: the
 // prefix sum cu[0..B] of ceil(seq_len / kTile) over the batch, built in LDS by
 // one wave.  Returns cu[B].
@@ -131,14 +160,9 @@ __device__ inline int build_tile_prefix(const int32_t* __restrict__ seq_lens, in
       int L = seq_lens[i];
       n = L > 0 ? (L + kTile - 1) / kTile : 0;
     }
-    int x = n;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      int y = __shfl_up(x, o);
-      if (lane >= o) x += y;
-    }
+    const int x = wave_incl_sum(n);
     if (i < B) cu[i + 1] = run + x;
-    run += __shfl(x, kWave - 1);
+    run += lane_value(x, kWave - 1);
   }
   return run;
 }

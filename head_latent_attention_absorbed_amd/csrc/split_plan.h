@@ -16,17 +16,6 @@
 
 namespace mla {
 
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-__device__ __forceinline__ int wave_max(int x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o));
-  return x;
-}
-
 // The plan as one wave sees it: lane l holds the tile counts of sequences
 // l, l + 64, ... (at most CH * 64 of them; WavePlanFor picks CH = 1 when
 // the batch fits one wave, which keeps the search short).
@@ -94,20 +83,15 @@ struct WavePlanN {
     for (int c = 0; c < CH; ++c) {
       if (c < nch && b < 0) {
         const int pc = (n[c] + W - 1) / W;
-        int x = pc;  // inclusive scan over the lanes
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const int y = __shfl_up(x, o);
-          if (lane >= o) x += y;
-        }
+        const int x = wave_incl_sum(pc);
         const int start = run + x - pc;
         const unsigned long long hit = __ballot(pc > 0 && g >= start && g < start + pc);
         if (hit) {
-          const int l = __ffsll((long long)hit) - 1;
+          const int l = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
           b = c * kWave + l;
-          s_b = __shfl(start, l);
+          s_b = lane_value(start, l);
         }
-        run += __shfl(x, kWave - 1);
+        run += lane_value(x, kWave - 1);
       }
     }
   }
@@ -121,18 +105,13 @@ struct WavePlanN {
     for (int c = 0; c < CH; ++c) {
       if (c < nch) {
         const int pc = (n[c] + W - 1) / W;
-        int x = pc;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const int y = __shfl_up(x, o);
-          if (lane >= o) x += y;
-        }
+        const int x = wave_incl_sum(pc);
         if (b >= c * kWave && b < (c + 1) * kWave) {
           const int l = b - c * kWave;
-          s_b = run + __shfl(x, l) - __shfl(pc, l);
-          p_b = __shfl(pc, l);
+          s_b = run + lane_value(x, l) - lane_value(pc, l);
+          p_b = lane_value(pc, l);
         }
-        run += __shfl(x, kWave - 1);
+        run += lane_value(x, kWave - 1);
       }
     }
   }
@@ -144,15 +123,10 @@ struct WavePlanN {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       if (c < nch) {
-        int x = (n[c] + W - 1) / W;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const int y = __shfl_up(x, o);
-          if (lane >= o) x += y;
-        }
+        const int x = wave_incl_sum((n[c] + W - 1) / W);
         const int b = c * kWave + lane;
         if (b < B) sb[b + 1] = run + x;
-        run += __shfl(x, kWave - 1);
+        run += lane_value(x, kWave - 1);
       }
     }
   }
@@ -162,7 +136,7 @@ struct WavePlanN {
     int v = 0;
 #pragma unroll
     for (int c = 0; c < CH; ++c)
-      if (c < nch && b >= c * kWave && b < (c + 1) * kWave) v = __shfl(len[c], b - c * kWave);
+      if (c < nch && b >= c * kWave && b < (c + 1) * kWave) v = lane_value(len[c], b - c * kWave);
     return v;
   }
 
@@ -171,7 +145,7 @@ struct WavePlanN {
     int v = 0;
 #pragma unroll
     for (int c = 0; c < CH; ++c)
-      if (c < nch && b >= c * kWave && b < (c + 1) * kWave) v = __shfl(n[c], b - c * kWave);
+      if (c < nch && b >= c * kWave && b < (c + 1) * kWave) v = lane_value(n[c], b - c * kWave);
     (void)lane;
     return v;
   }

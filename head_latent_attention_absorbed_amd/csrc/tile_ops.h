@@ -46,7 +46,9 @@ struct NoDma {
 // Score MFMAs with VGPR accumulators.  The hardware forwards an MFMA result
 // to the accumulator input of the next MFMA of the same chain; a VALU read of
 // the result needs wait states that the compiler cannot see through inline
-// asm, so every chain ends with mfma_v_drain before its values are used.
+// asm, so the last MFMA of every chain (mfma_v_last) carries them in the
+// same asm statement: a separate statement of nops would not order the
+// compiler's own copies of the result after it.
 // The other direction needs them too: an MFMA may read a VGPR only two wait
 // states after a VALU instruction wrote it, and the compiler may place such a
 // write (say a v_accvgpr_read bringing back an operand it parked in an AGPR)
@@ -57,8 +59,10 @@ __device__ __forceinline__ void mfma_v_first(f32x16& acc, bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void mfma_v_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void mfma_v_drain(f32x16& x) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
+__device__ __forceinline__ void mfma_v_last(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+v"(acc)
+               : "v"(a), "v"(b));
 }
 
 // S^T = K . Q^T of one 32-token tile (32 tokens x this wave's 32 rows):
@@ -90,9 +94,9 @@ __device__ __forceinline__ f32x16 score_mfma(const char* tb, const bf16x8 (&qf)[
       if (ks % (Gm::KS / NDMA) == 0) dma.issue(ks / (Gm::KS / NDMA));  // next tile's copy, spread out
     }
     if (ks == 0) mfma_v_first(sacc, kf[ks], qf[ks]);
-    else mfma_v_acc(sacc, kf[ks], qf[ks]);
+    else if (ks + 1 < Gm::KS) mfma_v_acc(sacc, kf[ks], qf[ks]);
+    else mfma_v_last(sacc, kf[ks], qf[ks]);
   }
-  mfma_v_drain(sacc);
   // The score product is its own scheduling region: nothing that follows
   // (the softmax, or the lagged P.V of the previous tile) is hoisted into it.
   __builtin_amdgcn_sched_barrier(0);
