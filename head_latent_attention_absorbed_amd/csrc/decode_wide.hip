@@ -23,13 +23,11 @@
 // grows by more than 2^8) the owning wave publishes the factor, and every
 // wave rescales those rows of its accumulators before adding the lagged P . V.
 //
-// Tiles of a part are copied global -> LDS by DMA one tile ahead (bf16),
-// spread over the MFMAs of the score product; an e4m3 tile's bytes are copied one tile ahead into a staging
-// slot and decoded exactly to bf16 in LDS at the start of the iteration
-// before the one that scores it (a second barrier then frees the staging
-// slot for the next copy).  Copy lanes past
-// a sequence's length re-read its first record, so a partial tile holds
-// finite values where the softmax gives weight 0.
+// Tiles of a part are copied global -> LDS by DMA one tile ahead, spread
+// over the MFMAs of the score product.  Copy lanes past a sequence's length
+// re-read its first record, so a partial tile holds finite values where the
+// softmax gives weight 0.  (The e4m3 cache has a kernel of its own,
+// decode_wide_fp8.hip, that keeps the tile's bytes as copied.)
 //
 // A part is one sequence's token range (split_plan.h); it writes one
 // normalised partial (fp16 or fp32) and its log-sum-exp.
@@ -40,11 +38,12 @@
 #include "mla_kernels.h"
 #include "split_plan.h"
 #include "tile_ops.h"
+#include "wide_common.h"
 
 namespace mla {
 namespace {
 
-template <int DC, bool FP8>
+template <int DC>
 struct Wide {
   using Gm = Geo<DC>;
   static constexpr int NW = 4;                // waves
@@ -52,43 +51,14 @@ struct Wide {
   static constexpr int NBW = Gm::NB / NW;     // 32-column blocks of O per wave
   static constexpr int TB = Gm::TILE_BYTES;   // bf16 tile image
   // bf16 images: the one being scored, the one whose P . V is pending, and
-  // the copies in flight (bf16) or the one being decoded (e4m3).
+  // the copy in flight.
   static constexpr int NBUF = 3;
-  static constexpr int AHEAD = 1;  // bf16 tiles copied ahead of the one scored
-  static constexpr int NI = Gm::GPT / (2 * NW);  // bf16 copy instructions per wave per tile
-  static constexpr int NRAW = 1;                 // e4m3 staging slots
-  static constexpr int RAW = Fp8Geo<DC>::BYTES;
+  static constexpr int AHEAD = 1;  // tiles copied ahead of the one scored
+  static constexpr int NI = Gm::GPT / (2 * NW);  // copy instructions per wave per tile
   static constexpr int PB = NW * 2 * 1024;       // P of one tile: [row block][k-step][lane] x 16 B
   static_assert(Gm::GPT % (2 * NW) == 0, "tile rows must split evenly over the waves");
   static_assert(Gm::NB % NW == 0, "latent blocks must split evenly over the waves");
 };
-
-// Address of tile t (sequence-local, 32 tokens) of the part's sequence and
-// its number of cached tokens.
-struct TileSrc {
-  const char* run;
-  int nv;
-  int page_slot;  // page * block_size + first slot (fp8 scales)
-};
-
-// The physical page of tile t, read one iteration before the copy that
-// needs it.  The read is made a vector load (the lane-dependent zero), so
-// that it is counted with the copies (vmcnt) and waited for together with
-// them at the next tile barrier; a scalar load would share its counter with
-// the LDS reads, whose waits would then also wait for it.
-__device__ __forceinline__ int tile_page_load(const DecodeParams& p, const int32_t* bt, int t) {
-  return bt[((t * kTile) >> p.block_shift) + (opaque_lane() >> 6)];
-}
-
-__device__ __forceinline__ TileSrc tile_src(const DecodeParams& p, int page, int t, int L) {
-  const int pos0 = t * kTile;
-  const int slot0 = pos0 & (p.block_size - 1);
-  TileSrc s;
-  s.run = p.c_kv + (int64_t)page * p.block_stride + (int64_t)slot0 * p.token_stride;
-  s.nv = min(L - pos0, kTile);
-  s.page_slot = page * p.block_size + slot0;
-  return s;
-}
 
 // The bf16 copy of one tile, one instruction at a time, for the score
 // product to spread over its MFMA stream (issue(q), q < NI); inactive when
@@ -136,182 +106,6 @@ __device__ __forceinline__ void copy_tile(const DecodeParams& p, const TileSrc& 
   }
 }
 
-// e4m3 tile copy into a staging slot (layout of convert_fp8_tile), lanes
-// past the length reading token 0.
-template <int DC>
-__device__ __forceinline__ void copy_raw(const DecodeParams& p, const TileSrc& s, uint32_t stage_lds, int w) {
-  using F = Fp8Geo<DC>;
-  constexpr int NW = 4;
-  const int ol = opaque_lane();
-  const int t = ol & 31;
-  const uint32_t lane_off = (uint32_t)(t < s.nv ? t : 0) * (uint32_t)p.token_stride + 16u * (ol >> 5);
-#pragma unroll
-  for (int q = 0; q < (F::NINS + NW - 1) / NW; ++q) {
-    const int ins = q * NW + w;
-    if (ins < F::NINS) {
-      const int m0 = 2 * ins;  // pairs m0, m0 + 1 never straddle the latent and the RoPE key
-      const int64_t off = m0 < Geo<DC>::GC / 2 ? (int64_t)m0 * 16 : p.rope_off + (int64_t)(m0 - Geo<DC>::GC / 2) * 16;
-      lds_dma16(s.run + off, lane_off, uniform(stage_lds + ins * 1024));
-    }
-  }
-}
-
-// Multiply rows of the accumulators by their factors (rare; see rescale in
-// tile_ops.h for the AGPR-constrained form and the wait states).
-template <int NBW>
-__device__ __forceinline__ void rescale_rows(f32x16 (&O)[4][NBW], const float (&a)[4]) {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-#pragma unroll
-    for (int cb = 0; cb < NBW; ++cb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = O[rb][cb][i];
-        float tmp;
-        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32_e32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                     : "+a"(x), "=&v"(tmp)
-                     : "v"(a[rb]));
-        O[rb][cb][i] = x;
-      }
-    }
-  }
-  asm volatile("s_nop 1" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// Online softmax of one tile's scores for the wave's 32 rows (one code path
-// for full and partly visible tiles), in steps that pv_rows spreads over its
-// MFMAs.  Lane (col, half) holds row col and tokens 8(i/4) + 4 half + i%4 in
-// value i; entry i is visible iff 8(i/4) + i%4 < rel, rel = (first position
-// the row may not see) - (tile start) - 4 half.  The maximum is taken over
-// the raw scores and scaled afterwards (the scale is positive); weights are
-// exp2(s * scale - m) with one fused multiply-add.  For an e4m3 tile the raw
-// scores are first multiplied by their tokens' scales (the keys' scale) and
-// the weights by them again after the sum (the values' scale, carried by P).
-template <bool FP8>
-struct WideSoftmax {
-  static constexpr int STEPS = 12;
-  f32x16 v;
-  const float* tsc;  // fp8: the tile's per-token scales (LDS)
-  int rel;
-  float slog2;
-  float& m_run;
-  float& l_run;
-  int half;
-  float m_new, mu, alpha;
-  bf16x8 pf0, pf1;
-
-  __device__ __forceinline__ void step(int j) {
-    if (j < 4) {  // scale (e4m3) and mask four entries
-      f32x4 s4 = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
-      if constexpr (FP8) s4 = *(const f32x4*)(tsc + 8 * j + 4 * half);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float x = v[4 * j + c];
-        if constexpr (FP8) x *= s4[c];
-        v[4 * j + c] = (8 * j + c < rel) ? x : -__builtin_inff();
-      }
-    } else if (j == 4) {
-      float a = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-      float b = fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7]));
-      float c = fmaxf(fmaxf(v[8], v[9]), fmaxf(v[10], v[11]));
-      float d = fmaxf(fmaxf(v[12], v[13]), fmaxf(v[14], v[15]));
-      m_new = fmaxf(fmaxf(a, b), fmaxf(c, d));
-    } else if (j == 5) {
-      const float mt = pair_max(m_new) * slog2;
-      const bool rebase = mt > m_run + kRebase;  // never for a tile this row sees nothing of (mt = -inf)
-      m_new = rebase ? mt : m_run;
-      alpha = rebase ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // 0 on the first visible tile
-      l_run *= alpha;
-      m_run = m_new;
-      // A row that has seen no position yet keeps m = -inf with every entry
-      // at -inf: exp2(-inf - 0) gives the weights 0 instead of NaN.
-      mu = m_new == -__builtin_inff() ? 0.0f : m_new;
-    } else if (j < 10) {  // weights, four at a time
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int i = 4 * (j - 6) + c;
-        v[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], slog2, -mu));
-      }
-    } else if (j == 10) {
-      float t0 = v[0] + v[1], t1 = v[2] + v[3], t2 = v[4] + v[5], t3 = v[6] + v[7];
-      float t4 = v[8] + v[9], t5 = v[10] + v[11], t6 = v[12] + v[13], t7 = v[14] + v[15];
-      l_run += ((t0 + t1) + (t2 + t3)) + ((t4 + t5) + (t6 + t7));
-      if constexpr (FP8) {  // the scales again (re-read rather than kept in registers)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 s4 = *(const f32x4*)(tsc + 8 * q + 4 * half);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) v[4 * q + c] *= s4[c];
-        }
-      }
-    } else if (j == 11) {
-      float w8[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w8[i] = v[i];
-      pf0 = pack_bf16x8(w8);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w8[i] = v[8 + i];
-      pf1 = pack_bf16x8(w8);
-    }
-  }
-  __device__ __forceinline__ void all() {
-#pragma unroll
-    for (int j = 0; j < STEPS; ++j) step(j);
-  }
-};
-
-// Exact e4m3 -> bf16 decode of a staged tile into its image (the layouts of
-// convert_fp8_tile), each thread's staged reads issued in groups of up to
-// three before their conversions.  Tokens from nv on are written as zeros.
-template <int DC>
-__device__ __forceinline__ void decode_tile(const char* stage, char* tb, int nv, int tid) {
-  using F = Fp8Geo<DC>;
-  constexpr int ITEMS = F::NP * kTile, PER = (ITEMS + 255) / 256, GRP = 3;
-#pragma unroll
-  for (int k0 = 0; k0 < PER; k0 += GRP) {
-    uint4 x[GRP];
-#pragma unroll
-    for (int k = k0; k < k0 + GRP && k < PER; ++k) {
-      const int i = tid + 256 * k;
-      x[k - k0] = (k + 1 < PER || i < ITEMS) ? *(const uint4*)(stage + i * 16) : uint4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int k = k0; k < k0 + GRP && k < PER; ++k) {
-      const int i = tid + 256 * k;
-      if (k + 1 < PER || i < ITEMS) {
-        const uint4 y = x[k - k0];
-        const int m = i >> 5, t = i & 31;
-        const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y.x, 1.0f, false);
-        const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y.x, 1.0f, true);
-        const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y.y, 1.0f, false);
-        const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y.y, 1.0f, true);
-        const bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y.z, 1.0f, false);
-        const bf16x2 f = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y.z, 1.0f, true);
-        const bf16x2 g = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y.w, 1.0f, false);
-        const bf16x2 h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y.w, 1.0f, true);
-        bf16x8 lo = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};  // granule row 2m
-        bf16x8 hi = {e[0], e[1], f[0], f[1], g[0], g[1], h[0], h[1]};  // granule row 2m + 1
-        if (t >= nv) {
-          lo = bf16x8{};
-          hi = bf16x8{};
-        }
-        *(bf16x8*)(tb + (2 * m) * kRow + (t << 4)) = lo;
-        *(bf16x8*)(tb + (2 * m + 1) * kRow + ((t ^ 4) << 4)) = hi;
-      }
-    }
-  }
-}
-
-// The step-less stand-in for pv_rows when no softmax rides along.
-struct NoSteps {
-  static constexpr int STEPS = 0;
-  __device__ __forceinline__ void step(int) {}
-};
-
-// P . V of one tile for this wave's column blocks over all four row blocks,
 // with the softmax steps of the next tile placed between the column blocks.
 // P comes from LDS (`pb`: [row block][k-step][lane] x 16 B), V^T through
 // transposing reads of the tile image `tb` (the pattern of pv_tile in
@@ -363,21 +157,18 @@ __device__ __forceinline__ void pv_rows(const char* tb, const char* pb, f32x16 (
   }
 }
 
-template <int DC, bool FP8>
+template <int DC>
 __global__ void __launch_bounds__(256)
-    decode_wide_kernel(DecodeParams p, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ block_table,
-                       const float* __restrict__ kv_scale) {
-  using Wd = Wide<DC, FP8>;
+    decode_wide_kernel(DecodeParams p, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ block_table) {
+  using Wd = Wide<DC>;
   using Gm = Geo<DC>;
   constexpr int NW = Wd::NW, ROWS = Wd::ROWS, NBW = Wd::NBW, TB = Wd::TB, NBUF = Wd::NBUF, AHEAD = Wd::AHEAD;
   constexpr int NI = Wd::NI, PB = Wd::PB;
 
   __shared__ __attribute__((aligned(1024))) char tiles[NBUF * TB];
-  __shared__ __attribute__((aligned(1024))) char raw[FP8 ? Wd::NRAW * Wd::RAW : 16];
   __shared__ __attribute__((aligned(1024))) char pbuf[2 * PB];
   __shared__ __attribute__((aligned(16))) float alph[2][ROWS];
   __shared__ __attribute__((aligned(16))) int rflag[2][NW];
-  __shared__ __attribute__((aligned(16))) float tsc[FP8 ? NBUF * kTile : 4];
   __shared__ float fin_l[ROWS];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -410,7 +201,6 @@ __global__ void __launch_bounds__(256)
   const int32_t* bt = block_table + (int64_t)b * p.bt_stride;
   const int rowbase = rg * ROWS;
   const uint32_t tiles_lds = lds_offset(tiles);
-  const uint32_t raw_lds = lds_offset(raw);
 
   // ---- prologue: the first copies and the query block; wait for both.
   // Query fragments: lane (col, half) needs row col's values 16 ks + 8 half
@@ -427,12 +217,10 @@ __global__ void __launch_bounds__(256)
   char* stg = tiles + TB + w * 32 * SROW;
   const int qrow0 = rowbase + 32 * w;     // this wave's first query row
   const char* qseq = (const char*)(p.q_lat + (int64_t)b * p.R * DC);
-  // Tiles copied before the loop: bf16 tiles 0 .. AHEAD-1; e4m3 tile 0.
-  constexpr int PRE = FP8 ? 1 : AHEAD;
-  // page_pf: the page of the next tile the loop copies (tile PRE; for e4m3,
-  // whose loop copies tile i + 2, tile 1 is copied after the first decode).
+  // Tiles copied before the loop: 0 .. AHEAD-1; page_pf: the page of the
+  // next tile the loop copies (tile AHEAD).
+  constexpr int PRE = AHEAD;
   int page_pf = 0;
-  float sc0 = 0.0f, sc_next = 0.0f;  // fp8: wave 0's scales (lane < 32)
   // The page reads go out first and the query copies right behind them; the
   // tile copies, which need the pages, are issued after the query's loads, so
   // that the query's round trip overlaps the page read's.
@@ -466,21 +254,14 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
   for (int a = 0; a < PRE; ++a) {
     if (a < n) {
-      const TileSrc s = tile_src(p, uniform(pg[a]), t0 + a, L);
-      if constexpr (!FP8) {
-        copy_tile<DC>(p, s, tiles_lds + a * TB, w);
-      } else {
-        copy_raw<DC>(p, s, raw_lds, w);
-        if (w == 0 && lane < kTile && lane < s.nv) sc0 = kv_scale[s.page_slot + lane];
-      }
+      copy_tile<DC>(p, tile_src(p, uniform(pg[a]), t0 + a, L), tiles_lds + a * TB, w);
     }
   }
-  // The direct loads (and the scales) must be in registers before the loop;
+  // The direct loads must be in registers before the loop;
   // the asm makes the compiler place that wait here, not inside the loop.
   // The copies were issued earlier, so they have landed too.
 #pragma unroll
   for (int ks = KST; ks < Gm::KS; ++ks) asm volatile("" ::"v"(qf[ks]));
-  asm volatile("" ::"v"(sc0));
   vm_wait<0>();
   {
     const int col_ = ln0 & 31, hf = ln0 >> 5;
@@ -496,19 +277,6 @@ __global__ void __launch_bounds__(256)
       for (int ks = 0; ks < Gm::KS; ++ks) qf[ks] = bf16x8{};
     }
   }
-  if constexpr (FP8) {
-    block_sync();  // raw tile 0 has landed for every wave
-    decode_tile<DC>(raw, tiles, min(L - t0 * kTile, kTile), tid);
-    if (w == 0 && lane < kTile) tsc[lane] = sc0;
-    block_sync();  // every wave is done with the staging slot
-    if (n > 1) {
-      const TileSrc s1 = tile_src(p, uniform(page_pf), t0 + 1, L);
-      copy_raw<DC>(p, s1, raw_lds, w);
-      if (w == 0 && lane < kTile && lane < s1.nv) sc_next = kv_scale[s1.page_slot + lane];
-      page_pf = n > 2 ? tile_page_load(p, bt, t0 + 2) : 0;
-    }
-  }
-
   const int my_row = rowbase + 32 * w + col;
   const int limit = min(L - p.S + 1 + my_row / p.H, L);  // first position this lane's row may not see
   float m_run = -__builtin_inff(), l_run = 0.0f;
@@ -520,9 +288,8 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
     for (int cb = 0; cb < NBW; ++cb) O[rb][cb] = f32x16{};
 
-  // One tile step: (a) tile i is in LDS (e4m3: tile i + 1's bytes have
-  // landed), P of tile i - 1 is visible, the slot the next copy or decode
-  // overwrites is free; (b) the next copy; (c) the scores and softmax of tile
+  // One tile step: (a) tile i is in LDS, P of tile i - 1 is visible, the
+  // slot the next copy overwrites is free; (b) the next copy; (c) the scores and softmax of tile
   // i with, from the second tile on (PV), the P . V of tile i - 1.  Iteration
   // 0 is a separate call, so the loop body has no branch on the tile index
   // (which would make the compiler peel it and keep copies of the
@@ -531,40 +298,21 @@ __global__ void __launch_bounds__(256)
     constexpr bool PV = decltype(pv_tag)::value;
     const int t = t0 + i;
     const int buf = i % NBUF;
-    vm_wait<0>();  // tile i (e4m3: tile i + 1's bytes) and the page index read with it
+    vm_wait<0>();  // tile i and the page index read with it
     block_sync();
     // the re-base flags of tile i - 1, read now and tested after the scores
     int4 fl = int4{0, 0, 0, 0};
     if constexpr (PV) fl = *(const int4*)rflag[(i - 1) & 1];
-    // bf16: the copy of tile i + AHEAD, spread over the score MFMAs;
-    // e4m3: decode tile i + 1 into the image slot of tile i - 2 (its P . V ran
-    // in the previous iteration), then copy tile i + 2 into the freed staging slot.
-    WideDma<DC> dma{};
-    if constexpr (!FP8) {
-      const bool more = i + AHEAD < n;
-      dma = wide_dma<DC>(p, tile_src(p, uniform(page_pf), t + AHEAD, L), tiles_lds + ((i + AHEAD) % NBUF) * TB, w,
-                         more);
-      if (i + AHEAD + 1 < n) page_pf = tile_page_load(p, bt, t + AHEAD + 1);
-    } else if (i + 1 < n) {
-      const int nbuf = (i + 1) % NBUF;
-      decode_tile<DC>(raw, tiles + nbuf * TB, min(L - (t + 1) * kTile, kTile), tid);
-      if (w == 0 && lane < kTile) tsc[nbuf * kTile + lane] = sc_next;
-      block_sync();
-      if (i + 2 < n) {
-        const TileSrc s = tile_src(p, uniform(page_pf), t + 2, L);
-        copy_raw<DC>(p, s, raw_lds, w);
-        float sc = 0.0f;  // its scales, kept in flight with the copy
-        if (w == 0 && lane < kTile && lane < s.nv) sc = kv_scale[s.page_slot + lane];
-        sc_next = sc;
-        if (i + 3 < n) page_pf = tile_page_load(p, bt, t + 3);
-      }
-    }
+    // the copy of tile i + AHEAD, spread over the score MFMAs
+    const WideDma<DC> dma = wide_dma<DC>(p, tile_src(p, uniform(page_pf), t + AHEAD, L),
+                                         tiles_lds + ((i + AHEAD) % NBUF) * TB, w, i + AHEAD < n);
+    if (i + AHEAD + 1 < n) page_pf = tile_page_load(p, bt, t + AHEAD + 1);
     // One code path for full and partly visible tiles (the masked softmax
     // steps): two inlined copies of the P . V would each get their own
     // assignment of the accumulators and a copy of all of them at the join.
     const int pos0 = t * kTile;
-    WideSoftmax<FP8> sm{score_mfma<DC, FP8 ? 0 : WideDma<DC>::NI>(tiles + buf * TB, qf, dma), tsc + buf * kTile,
-                        limit - pos0 - 4 * half, p.scale_log2, m_run, l_run, half};
+    WideSoftmax<false> sm{score_mfma<DC, WideDma<DC>::NI>(tiles + buf * TB, qf, dma), nullptr,
+                          limit - pos0 - 4 * half, p.scale_log2, m_run, l_run, half};
     if constexpr (PV) {
       // rows of the accumulators whose maximum moved at tile i - 1 (rare)
       if (fl.x | fl.y | fl.z | fl.w) {
@@ -623,18 +371,18 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-template <int DC, bool FP8>
+template <int DC>
 hipError_t launch_wide_one(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_wide_kernel<DC, FP8>), dim3(p.P * p.RG), dim3(256), 0, stream, p, p.seq_lens,
-                     p.block_table, p.kv_scale);
+  hipLaunchKernelGGL((decode_wide_kernel<DC>), dim3(p.P * p.RG), dim3(256), 0, stream, p, p.seq_lens,
+                     p.block_table);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode_wide(const DecodeParams& p, int d_latent, bool fp8, hipStream_t stream) {
-  if (d_latent == 512) return fp8 ? launch_wide_one<512, true>(p, stream) : launch_wide_one<512, false>(p, stream);
-  return fp8 ? launch_wide_one<256, true>(p, stream) : launch_wide_one<256, false>(p, stream);
+  if (fp8) return launch_decode_wide_fp8(p, d_latent, stream);
+  return d_latent == 512 ? launch_wide_one<512>(p, stream) : launch_wide_one<256>(p, stream);
 }
 
 }  // namespace mla

@@ -1,0 +1,400 @@
+// Split-K decode of absorbed MLA for 128 query rows per work-group over an
+// e4m3 cache with per-token fp32 scales (gfx950).
+//
+// The method and the division of a tile's work between the four waves are
+// those of decode_wide.hip (scores: wave w owns query rows 32w .. 32w+31;
+// P . V: wave w owns latent columns (DC/4) w .. for all 128 rows, P through
+// LDS, one tile late).  The difference is the tile image: the e4m3 bytes
+// stay in LDS as copied (row pair m = bytes 16m .. 16m+15 of the latent, then
+// of the RoPE key, token t at byte (32 m + t) 16) and each MFMA operand is
+// decoded in registers right before its MFMA, so there is no bf16 image, no
+// decode pass over the tile and no second barrier per tile:
+//   K fragment (score A operand): token col, bytes 16 ks + 8 half .. +8 of
+//     its record: one 8-byte LDS read, four e4m3 -> bf16 conversions;
+//   V^T fragment (P . V A operand): column c, the eight tokens of the P
+//     fragment it meets: one 8-bit transposing LDS read (each lane i of a
+//     16-lane group receives byte i % 8 of the words of lanes i / 8,
+//     i / 8 + 2, ..., i / 8 + 14, which address those tokens' halves of the
+//     column's row pair), four conversions.
+// Every e4m3 value is a bf16 value, so the conversions are exact (scale 1);
+// the keys' scale multiplies the raw scores and the values' scale is carried
+// by P (WideSoftmax<true>).  A tile is a quarter of a bf16 image's bytes in
+// LDS, so two tiles are kept in flight; their scales come with them by DMA.
+// Copy lanes past a sequence's length re-read its first record and scale.
+#include <type_traits>
+
+#include "decode_common.h"
+#include "mla_device.h"
+#include "mla_kernels.h"
+#include "split_plan.h"
+#include "tile_ops.h"
+#include "wide_common.h"
+
+namespace mla {
+namespace {
+
+template <int DC>
+struct F8Wide {
+  using Gm = Geo<DC>;
+  using F = Fp8Geo<DC>;
+  static constexpr int NW = 4, ROWS = 32 * NW, NBW = Gm::NB / NW;
+  static constexpr int AHEAD = 2;                    // tiles in flight
+  static constexpr int NBUF = AHEAD + 2;             // + the tile scored and the one in P . V
+  static constexpr int RAW = F::BYTES;               // one staged tile
+  static constexpr int NQ = (F::NINS + NW - 1) / NW;  // row-pair copies per wave per tile
+  static constexpr int NI = NQ + 1;                  // + the scales
+  static constexpr int PB = NW * 2 * 1024;           // P of one tile
+  static_assert(Gm::KS == F::NP, "one score k-step per row pair");
+  static_assert(Gm::KS % NI == 0, "the copy instructions divide the score k-steps");
+};
+
+// 4-byte global -> LDS copy (lane i writes LDS `lds` + 4 i), as lds_dma16.
+__device__ __forceinline__ void lds_dma4(const void* base_any, uint32_t voff, uint32_t lds) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base_any);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(dst)
+      : "memory", "m0");
+}
+
+// The copy of one tile: instruction q < NQ moves row pairs 2 ins, 2 ins + 1
+// (ins = q NW + w; the last round's surplus waves repeat an instruction of
+// that round, writing the same bytes, so that every wave issues the same
+// number of copies and one vmcnt value fits all); q = NQ moves the tile's
+// 32 scales (lanes 32 .. 63 repeat them into the slot's unused half).
+template <int DC>
+struct F8Dma {
+  using X = F8Wide<DC>;
+  const char* run;
+  int64_t rope_off;
+  const float* scl;
+  uint32_t lane_off, sc_off, raw_lds, sc_lds;
+  int w;
+  bool active;
+  __device__ __forceinline__ void issue(int q) const {
+    if (!active) return;
+    if (q < X::NQ) {
+      int ins = q * X::NW + w;
+      if (ins >= Fp8Geo<DC>::NINS) ins -= X::NW * X::NQ - Fp8Geo<DC>::NINS;
+      const int m0 = 2 * ins;  // pairs m0, m0 + 1 never straddle the latent and the RoPE key
+      const int64_t off = m0 < Geo<DC>::GC / 2 ? (int64_t)m0 * 16 : rope_off + (int64_t)(m0 - Geo<DC>::GC / 2) * 16;
+      lds_dma16(run + off, lane_off, uniform(raw_lds + ins * 1024));
+    } else {
+      lds_dma4(scl, sc_off, sc_lds);
+    }
+  }
+};
+
+// Eight e4m3 values (bytes 0..7 of lo | hi) as bf16, exactly.
+__device__ __forceinline__ bf16x8 e4m3x8(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+typedef __attribute__((address_space(3))) i32x2* lds_i32x2_ptr;
+
+// S^T = K . Q^T of one staged tile (the chain of score_mfma), each K
+// fragment decoded from 8 LDS bytes, with the next tile's copy spread over
+// the MFMAs.
+template <int DC>
+__device__ __forceinline__ f32x16 score_f8(const char* tb, const bf16x8 (&qf)[Geo<DC>::KS], const F8Dma<DC>& dma) {
+  constexpr int KS = Geo<DC>::KS, PD = kScoreAhead, NI = F8Wide<DC>::NI;
+  const int lane = opaque_lane();
+  const char* kb = tb + (lane & 31) * 16 + (lane >> 5) * 8;
+  uint2 kr[KS];
+#pragma unroll
+  for (int ks = 0; ks < PD; ++ks) kr[ks] = *(const uint2*)(kb + ks * 512);
+  f32x16 s;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (ks + PD < KS) kr[ks + PD] = *(const uint2*)(kb + (ks + PD) * 512);
+    if (ks % (KS / NI) == 0) dma.issue(ks / (KS / NI));
+    const bf16x8 a = e4m3x8(kr[ks].x, kr[ks].y);
+    if (ks == 0) mfma_v_first(s, a, qf[ks]);
+    else if (ks + 1 < KS) mfma_v_acc(s, a, qf[ks]);
+    else mfma_v_last(s, a, qf[ks]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  return s;
+}
+
+// The V^T fragment of column block nb, k-half j of a staged tile: lane
+// (G = lane / 16, i = lane % 16) gets column 32 nb + 16 (G % 2) + i of
+// tokens 16 j + 4 (G / 2) + {0, 1, 2, 3, 8, 9, 10, 11}, the token order of
+// the P fragments (the score MFMA's output layout, which P keeps).
+__device__ __forceinline__ bf16x8 v_frag_f8(const char* vb, int nb, int j) {
+  const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_ptr)(lds_void_ptr)(vb + nb * 1024 + j * 256));
+  return e4m3x8((uint32_t)r[0], (uint32_t)r[1]);
+}
+
+// P . V of one staged tile for this wave's column blocks over all four row
+// blocks (the order of pv_rows), with the softmax steps of the next tile
+// between the column blocks.  Source lane (G, s) of a transposing read
+// addresses bytes 8 (s % 2) .. +7 of row pair 2 nb + G % 2 of token
+// 16 j + 4 (G / 2) + e % 4 + 8 (e / 4), e = s / 2 (result byte e of the
+// receiving lanes).
+template <int DC, bool STEPS, class SM>
+__device__ __forceinline__ void pv_f8(const char* tb, const char* pb, f32x16 (&O)[4][Geo<DC>::NB / 4], int w, SM& sm) {
+  constexpr int NBW = Geo<DC>::NB / 4;
+  const int lane = opaque_lane();
+  const int G = lane >> 4, s = lane & 15;
+  const int e = s >> 1;
+  const char* vb = tb + (32 * (G & 1) + 4 * (G >> 1) + (e & 3) + 8 * (e >> 2)) * 16 + 8 * (s & 1);
+  bf16x8 pf[4][2];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) pf[rb][j] = *(const bf16x8*)(pb + (rb * 2 + j) * 1024 + lane * 16);
+  constexpr int SPB = (SM::STEPS + NBW - 1) / NBW;
+  bf16x8 c0 = v_frag_f8(vb, w * NBW, 0), c1 = v_frag_f8(vb, w * NBW, 1);
+#pragma unroll
+  for (int cb = 0; cb < NBW; ++cb) {
+    bf16x8 n0 = c0, n1 = c1;
+    if (cb + 1 < NBW) {
+      n0 = v_frag_f8(vb, w * NBW + cb + 1, 0);
+      n1 = v_frag_f8(vb, w * NBW + cb + 1, 1);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      O[rb][cb] = mfma32(c0, pf[rb][0], O[rb][cb]);
+      O[rb][cb] = mfma32(c1, pf[rb][1], O[rb][cb]);
+    }
+    if constexpr (STEPS) {
+#pragma unroll
+      for (int j = 0; j < SPB; ++j)
+        if (cb * SPB + j < SM::STEPS) sm.step(cb * SPB + j);
+    }
+    c0 = n0;
+    c1 = n1;
+  }
+}
+
+template <int DC>
+__global__ void __launch_bounds__(256)
+    decode_f8_kernel(DecodeParams p, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ block_table) {
+  using X = F8Wide<DC>;
+  using Gm = Geo<DC>;
+  constexpr int NW = X::NW, ROWS = X::ROWS, NBW = X::NBW, NBUF = X::NBUF, RAW = X::RAW, AHEAD = X::AHEAD;
+  constexpr int NI = X::NI, PB = X::PB;
+  constexpr int KST = DC / 32;            // query k-steps staged through LDS (half the latent)
+  constexpr int CPR = 2 * KST;            // staged 16-byte chunks per row
+  constexpr int SROW = CPR * 16;          // staged bytes per row
+  constexpr int RPI = 1024 / SROW;        // rows per copy instruction
+
+  __shared__ __attribute__((aligned(1024))) char raw[NBUF * RAW];
+  __shared__ __attribute__((aligned(1024))) char qstg[NW * 32 * SROW];
+  __shared__ __attribute__((aligned(1024))) char pbuf[2 * PB];
+  __shared__ __attribute__((aligned(16))) float tscale[NBUF][2 * kTile];
+  __shared__ __attribute__((aligned(16))) float alph[2][ROWS];
+  __shared__ __attribute__((aligned(16))) int rflag[2][NW];
+  __shared__ float fin_l[ROWS];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int half = lane >> 5, col = lane & 31;
+
+  // XCD-aware placement (as in decode_wide_kernel).
+  int u = blockIdx.x;
+  if ((gridDim.x & 7) == 0) u = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int g = u / p.RG, rg = u % p.RG;
+
+  int b = -1, t0 = 0, t1 = 0, L = 0;
+  with_plan(seq_lens, p.B, p.P, lane, [&](const auto& pl) {
+    int s_b = 0;
+    if (g < pl.total) pl.locate_slot(g, lane, b, s_b);
+    if (b >= 0) {
+      t0 = (g - s_b) * pl.W;
+      t1 = min(t0 + pl.W, pl.tiles(b, lane));
+      L = pl.length(b);
+    }
+  });
+  b = uniform(b);
+  if (b < 0) return;
+  t0 = uniform(t0);
+  const int n = uniform(t1) - t0;  // tiles of this part (>= 1)
+  L = uniform(L);
+  const int32_t* bt = block_table + (int64_t)b * p.bt_stride;
+  const int rowbase = rg * ROWS;
+  const uint32_t raw_lds = lds_offset(raw);
+
+  // The copy of part tile t from page `page` (lane-derived values recomputed
+  // per tile rather than kept live).
+  auto make_dma = [&](int t, int page, bool active) {
+    const TileSrc s = tile_src(p, page, t0 + t, L);
+    const int ol = opaque_lane();
+    const int tok = (ol & 31) < s.nv ? (ol & 31) : 0;
+    return F8Dma<DC>{s.run, p.rope_off, p.kv_scale + s.page_slot,
+                     (uint32_t)tok * (uint32_t)p.token_stride + 16u * (uint32_t)(ol >> 5), 4u * (uint32_t)tok,
+                     raw_lds + (t % NBUF) * RAW, lds_offset(tscale[t % NBUF]), w, active};
+  };
+
+  // ---- prologue: the pages of tiles 0 .. AHEAD, the query block (half
+  // staged through LDS as in decode_wide_kernel), tiles 0 and 1.
+  const int qrow0 = rowbase + 32 * w;
+  const char* qseq = (const char*)(p.q_lat + (int64_t)b * p.R * DC);
+  char* stg = qstg + w * 32 * SROW;
+  const int page0 = tile_page_load(p, bt, t0);
+  const int page1 = n > 1 ? tile_page_load(p, bt, t0 + 1) : 0;
+  int page_pf = AHEAD < n ? tile_page_load(p, bt, t0 + AHEAD) : 0;
+  {
+    const int ol = opaque_lane();
+    const int rr = ol / CPR, cs = ol % CPR;
+#pragma unroll
+    for (int j = 0; j < 32 / RPI; ++j) {
+      const int r = j * RPI + rr;
+      const int rg_ = min(qrow0 + r, p.R - 1);            // rows past R re-read row R-1 (discarded)
+      const int chunk = cs ^ (r & (CPR - 1) & 15);
+      lds_dma16(qseq, (uint32_t)(rg_ * DC * 2 + chunk * 16), lds_offset(stg + j * 1024));
+    }
+  }
+  bf16x8 qf[Gm::KS];
+  const int ln0 = opaque_lane();
+  const int qrow = qrow0 + (ln0 & 31);
+  {
+    const int qr_ = min(qrow, p.R - 1);
+    const bf16x8* ql = (const bf16x8*)(p.q_lat + ((int64_t)b * p.R + qr_) * DC + 8 * (ln0 >> 5));
+    const bf16x8* qr = (const bf16x8*)(p.q_rope + ((int64_t)b * p.R + qr_) * 64 + 8 * (ln0 >> 5));
+#pragma unroll
+    for (int ks = KST; ks < DC / 16; ++ks) qf[ks] = ql[2 * ks];
+#pragma unroll
+    for (int ks = DC / 16; ks < Gm::KS; ++ks) qf[ks] = qr[2 * (ks - DC / 16)];
+  }
+  {
+    const F8Dma<DC> d0 = make_dma(0, uniform(page0), true);
+#pragma unroll
+    for (int q = 0; q < NI; ++q) d0.issue(q);
+  }
+  if (n > 1) {
+    const F8Dma<DC> d1 = make_dma(1, uniform(page1), true);
+#pragma unroll
+    for (int q = 0; q < NI; ++q) d1.issue(q);
+  }
+#pragma unroll
+  for (int ks = KST; ks < Gm::KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+  asm volatile("" ::"v"(page_pf));
+  // everything but tile 1's copy (the last NI instructions, when it exists)
+  if (n > 1) vm_wait<NI>();
+  else vm_wait<0>();
+  block_sync();  // tile 0, its scales and the staged query are in LDS for every wave
+  {
+    const int col_ = ln0 & 31, hf = ln0 >> 5;
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks) {
+      const int c = 2 * ks + hf;
+      qf[ks] = *(const bf16x8*)(stg + col_ * SROW + ((c ^ (col_ & (CPR - 1) & 15)) << 4));
+    }
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks) asm volatile("" ::"v"(qf[ks]));
+    if (qrow >= p.R) {
+#pragma unroll
+      for (int ks = 0; ks < Gm::KS; ++ks) qf[ks] = bf16x8{};
+    }
+  }
+
+  const int my_row = rowbase + 32 * w + col;
+  const int limit = min(L - p.S + 1 + my_row / p.H, L);  // first position this lane's row may not see
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+  f32x16 O[4][NBW];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < NBW; ++cb) O[rb][cb] = f32x16{};
+
+  // One tile step: (a) tile i and its scales are in LDS (tile i + 1 may still
+  // be in flight), P of tile i - 1 is visible, every wave is done with tile
+  // i - 2 (whose slots take tile i + 2); (b) the copy of tile i + 2 spread
+  // over the scores of tile i; (c) the softmax of tile i with, from the
+  // second tile on (PV), the P . V of tile i - 1; (d) P and the factors of
+  // tile i published.
+  auto tile_step = [&](int i, auto pv_tag) {
+    constexpr bool PV = decltype(pv_tag)::value;
+    const int t = t0 + i;
+    if (i + 1 < n) vm_wait<NI>();  // tile i and the page read before tile i + 1's copy
+    else vm_wait<0>();
+    block_sync();
+    int4 fl = int4{0, 0, 0, 0};
+    if constexpr (PV) fl = *(const int4*)rflag[(i - 1) & 1];
+    // the page of tile i + AHEAD + 1, read before this step's copy is issued
+    const int page_cur = uniform(page_pf);
+    if (i + AHEAD + 1 < n) page_pf = tile_page_load(p, bt, t + AHEAD + 1);
+    const F8Dma<DC> dma = make_dma(i + AHEAD, page_cur, i + AHEAD < n);
+    const int pos0 = t * kTile;
+    WideSoftmax<true> sm{score_f8<DC>(raw + (i % NBUF) * RAW, qf, dma), tscale[i % NBUF], limit - pos0 - 4 * half,
+                         p.scale_log2, m_run, l_run, half};
+    if constexpr (PV) {
+      if (fl.x | fl.y | fl.z | fl.w) {
+        float a[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) a[rb] = alph[(i - 1) & 1][32 * rb + col];
+        rescale_rows<NBW>(O, a);
+      }
+      pv_f8<DC, true>(raw + ((i - 1) % NBUF) * RAW, pbuf + ((i - 1) & 1) * PB, O, w, sm);
+    } else {
+      sm.all();
+    }
+    const int ol = opaque_lane();
+    char* pw = pbuf + (i & 1) * PB + (w * 2) * 1024 + ol * 16;
+    *(bf16x8*)pw = sm.pf0;
+    *(bf16x8*)(pw + 1024) = sm.pf1;
+    if (ol < 32) alph[i & 1][32 * w + ol] = sm.alpha;
+    const bool any = PV && __any(sm.alpha != 1.0f);
+    if (ol == 0) rflag[i & 1][w] = any;
+  };
+  tile_step(0, std::false_type{});
+#pragma nounroll
+  for (int i = 1; i < n; ++i) tile_step(i, std::true_type{});
+  // ---- drain: P . V of the last tile
+  block_sync();
+  {
+    const int pbi = (n - 1) & 1;
+    if (rflag[pbi][0] | rflag[pbi][1] | rflag[pbi][2] | rflag[pbi][3]) {
+      float a[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) a[rb] = alph[pbi][32 * rb + col];
+      rescale_rows<NBW>(O, a);
+    }
+    NoSteps none;
+    pv_f8<DC, false>(raw + ((n - 1) % NBUF) * RAW, pbuf + pbi * PB, O, w, none);
+  }
+
+  // ---- normalise and write this part's partial and lse
+  const float l_tot = pair_sum(l_run);
+  if (half == 0) fin_l[32 * w + col] = l_tot;
+  if (half == 0 && my_row < p.R)
+    p.lse_part[(int64_t)g * p.R + my_row] =
+        l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -__builtin_inff();
+  block_sync();
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int ln = opaque_lane();
+    const int r = rowbase + 32 * rb + (ln & 31);
+    const float lt = fin_l[32 * rb + (ln & 31)];
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    if (r < p.R) store_partial<NBW>(p, O[rb], inv, ((int64_t)g * p.R + r) * DC + w * NBW * 32, ln >> 5);
+  }
+}
+
+template <int DC>
+hipError_t launch_f8_one(const DecodeParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_f8_kernel<DC>), dim3(p.P * p.RG), dim3(256), 0, stream, p, p.seq_lens, p.block_table);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_wide_fp8(const DecodeParams& p, int d_latent, hipStream_t stream) {
+  return d_latent == 512 ? launch_f8_one<512>(p, stream) : launch_f8_one<256>(p, stream);
+}
+
+}  // namespace mla

@@ -40,6 +40,8 @@ int decode_wgs_per_cu(int R, int d_latent);
 hipError_t launch_decode(const DecodeParams& p, int d_latent, bool fp8, hipStream_t stream);
 // The 128-row work-group form (decode_wide.hip), used when R > 64.
 hipError_t launch_decode_wide(const DecodeParams& p, int d_latent, bool fp8, hipStream_t stream);
+// Its e4m3 form (decode_wide_fp8.hip).
+hipError_t launch_decode_wide_fp8(const DecodeParams& p, int d_latent, hipStream_t stream);
 
 // Tile-native layout of the prefill's per-head keys and values: for
 // sequence b, head h and 32-position tile j, 16 granule rows g (elements
