@@ -90,39 +90,50 @@ def roofline_of(alg, us, measured=None):
         r.update(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                  frac=round(gbs / HBM_PEAK_GBS, 4), mfma_frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4))
     if measured:
-        r["frac_of_measured_hbm"] = round(gbs / measured["hbm_read_gbs"], 4)
+        r["frac_of_measured_hbm"] = round(gbs / measured["hbm_gbs"], 4)
         r["frac_of_measured_mfma"] = round(tflops / measured["mfma_bf16_tflops"], 4)
     return r
 
 
 def measured_peaks(torch, stream, reps: int = 5):
-    """Reference points measured on this GPU: a streaming read of 2 GiB (a
-    sum reduction of fp32, whose bytes are all reads) and a bf16 GEMM of
+    """Reference points measured on this GPU: a device copy of 1 GiB (HBM
+    bytes moved = 2 GiB, read + write; a reduction's read rate is lower than
+    a copy's here), a streaming read (fp32 sum over 2 GiB) and a bf16 GEMM of
     8192^3 on the device's BLAS; medians over reps, HIP events."""
     import numpy as np
 
     x = torch.ones((2 << 30) // 4, dtype=torch.float32, device="cuda")
+    src = x[: x.numel() // 2]
+    dst = torch.empty_like(src)
     a = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda")
     b = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda")
     for _ in range(2):
+        dst.copy_(src)
         x.sum()
         torch.matmul(a, b)
     torch.cuda.synchronize()
-    t_read, t_mm = [], []
+    t_copy, t_read, t_mm = [], [], []
     for _ in range(reps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         e[0].record(stream)
-        x.sum()
+        dst.copy_(src)
         e[1].record(stream)
-        torch.matmul(a, b)
+        x.sum()
         e[2].record(stream)
+        torch.matmul(a, b)
+        e[3].record(stream)
         torch.cuda.synchronize()
-        t_read.append(e[0].elapsed_time(e[1]) * 1e-3)
-        t_mm.append(e[1].elapsed_time(e[2]) * 1e-3)
-    res = {"hbm_read_gbs": round(x.numel() * 4 / float(np.median(t_read)) / 1e9, 1),
+        t_copy.append(e[0].elapsed_time(e[1]) * 1e-3)
+        t_read.append(e[1].elapsed_time(e[2]) * 1e-3)
+        t_mm.append(e[2].elapsed_time(e[3]) * 1e-3)
+    copy_gbs = 2 * src.numel() * 4 / float(np.median(t_copy)) / 1e9
+    read_gbs = x.numel() * 4 / float(np.median(t_read)) / 1e9
+    res = {"hbm_gbs": round(max(copy_gbs, read_gbs), 1), "hbm_copy_gbs": round(copy_gbs, 1),
+           "hbm_read_gbs": round(read_gbs, 1),
            "mfma_bf16_tflops": round(2 * 8192 ** 3 / float(np.median(t_mm)) / 1e12, 1),
-           "how": "torch sum over 2 GiB fp32 (read rate); torch.matmul bf16 8192x8192x8192 (hipBLASLt); "
-                  f"medians of {reps}"}
+           "how": "hbm_gbs = the higher of a 1 GiB fp32 device copy (read + write bytes) and an fp32 sum over "
+                  "2 GiB (read bytes); torch.matmul bf16 8192x8192x8192 (hipBLASLt); medians of " + str(reps)}
+    del src, dst
     del x, a, b
     torch.cuda.empty_cache()
     return res
@@ -160,11 +171,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, kernel: str):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, each scaled by a copy kernel's reading), or None
     when there is none or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -645,7 +656,7 @@ def main():
         "roofline": dict(
             kernel=f"{decode_kernel_name(w)} (mla_decode_paged)",
             **roofline_of(alg, dec_us, measured),
-            traffic=measured_traffic(w.name) if args.partial == "fp16" else None,
+            traffic=measured_traffic(w.name, decode_kernel_name(w)) if args.partial == "fp16" else None,
             algorithmic_bytes_per_launch=alg["decode_bytes"],
             algorithmic_flops_per_launch=alg["attn_flops"],
             avg_launch_us=round(dec_us, 2),

@@ -62,14 +62,15 @@ def test_more_than_one_gpu_is_refused():
 def test_traffic_counts_only_for_matching_sources(monkeypatch, tmp_path):
     prof = tmp_path / "profiles"
     prof.mkdir()
-    (prof / "decode_kernel_wl_traffic.txt").write_text(
+    (prof / "decode_wide_kernel_wl_traffic.txt").write_text(
         "# header\nhbm_bytes_per_launch: 12345\nkernel_source_sha256: abc\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "abc")
-    assert bench.measured_traffic("wl") == 12345
+    assert bench.measured_traffic("wl", "decode_wide_kernel") == 12345
+    assert bench.measured_traffic("wl", "decode_f8_kernel") is None
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "changed")
-    assert bench.measured_traffic("wl") is None
-    assert bench.measured_traffic("missing") is None
+    assert bench.measured_traffic("wl", "decode_wide_kernel") is None
+    assert bench.measured_traffic("missing", "decode_wide_kernel") is None
 
 
 @pytest.mark.parametrize("name", bench.KERNEL_SOURCES)
@@ -84,7 +85,7 @@ def test_roofline_bound_follows_the_ridge():
     for name, bound in (("deepseek_v3", "hbm"), ("kimi_k2_fp8", "mfma")):
         w = get_workload(name)
         a = bench.algorithmic(w, make_inputs(w, poison=False)["seq_lens"])
-        r = bench.roofline_of(a, 100.0, {"hbm_read_gbs": 6000.0, "mfma_bf16_tflops": 2000.0})
+        r = bench.roofline_of(a, 100.0, {"hbm_gbs": 6000.0, "mfma_bf16_tflops": 2000.0})
         assert r["bound"] == bound, (name, r)
         us = 100e-6
         if bound == "hbm":
