@@ -96,47 +96,86 @@ def roofline_of(alg, us, measured=None):
 
 
 def measured_peaks(torch, stream, reps: int = 5):
-    """Reference points measured on this GPU: a device copy of 1 GiB (HBM
-    bytes moved = 2 GiB, read + write; a reduction's read rate is lower than
-    a copy's here), a streaming read (fp32 sum over 2 GiB) and a bf16 GEMM of
-    8192^3 on the device's BLAS; medians over reps, HIP events."""
+    """Reference points measured on this GPU with the library's calibration
+    probes (HIP kernels, medians over reps, HIP events): the HBM read rate of
+    mla_probe_hbm_read over 2 GiB (16-byte loads from every CU) and the bf16
+    MFMA rate of mla_probe_mfma (independent 32x32x16 chains on every SIMD).
+    Beside them, for context: a 1 GiB torch device copy (read + write bytes)
+    and a bf16 GEMM of 8192^3 on the device's BLAS."""
     import numpy as np
+    from head_latent_attention_absorbed_amd import mla_probe_hbm_read, mla_probe_mfma
 
-    x = torch.ones((2 << 30) // 4, dtype=torch.float32, device="cuda")
+    nbytes = 2 << 30
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(16, dtype=torch.int32, device="cuda")
     src = x[: x.numel() // 2]
     dst = torch.empty_like(src)
     a = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda")
     b = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    iters = 20000
+    flops = 0
     for _ in range(2):
+        mla_probe_hbm_read(x, nbytes, sink, stream)
+        flops = mla_probe_mfma(iters, sink, stream)
         dst.copy_(src)
-        x.sum()
         torch.matmul(a, b)
     torch.cuda.synchronize()
-    t_copy, t_read, t_mm = [], [], []
+    t = {k: [] for k in ("read", "mfma", "copy", "mm")}
     for _ in range(reps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
         e[0].record(stream)
-        dst.copy_(src)
+        mla_probe_hbm_read(x, nbytes, sink, stream)
         e[1].record(stream)
-        x.sum()
+        mla_probe_mfma(iters, sink, stream)
         e[2].record(stream)
-        torch.matmul(a, b)
+        dst.copy_(src)
         e[3].record(stream)
+        torch.matmul(a, b)
+        e[4].record(stream)
         torch.cuda.synchronize()
-        t_copy.append(e[0].elapsed_time(e[1]) * 1e-3)
-        t_read.append(e[1].elapsed_time(e[2]) * 1e-3)
-        t_mm.append(e[2].elapsed_time(e[3]) * 1e-3)
-    copy_gbs = 2 * src.numel() * 4 / float(np.median(t_copy)) / 1e9
-    read_gbs = x.numel() * 4 / float(np.median(t_read)) / 1e9
-    res = {"hbm_gbs": round(max(copy_gbs, read_gbs), 1), "hbm_copy_gbs": round(copy_gbs, 1),
-           "hbm_read_gbs": round(read_gbs, 1),
-           "mfma_bf16_tflops": round(2 * 8192 ** 3 / float(np.median(t_mm)) / 1e12, 1),
-           "how": "hbm_gbs = the higher of a 1 GiB fp32 device copy (read + write bytes) and an fp32 sum over "
-                  "2 GiB (read bytes); torch.matmul bf16 8192x8192x8192 (hipBLASLt); medians of " + str(reps)}
-    del src, dst
-    del x, a, b
+        for k, (i, j) in zip(t, ((0, 1), (1, 2), (2, 3), (3, 4))):
+            t[k].append(e[i].elapsed_time(e[j]) * 1e-3)
+    med = {k: float(np.median(v)) for k, v in t.items()}
+    res = {"hbm_gbs": round(nbytes / med["read"] / 1e9, 1),
+           "mfma_bf16_tflops": round(flops / med["mfma"] / 1e12, 1),
+           "torch_copy_gbs": round(2 * src.numel() * 4 / med["copy"] / 1e9, 1),
+           "blas_bf16_tflops": round(2 * 8192 ** 3 / med["mm"] / 1e12, 1),
+           "how": "hbm_gbs: mla_probe_hbm_read over 2 GiB; mfma_bf16_tflops: mla_probe_mfma "
+                  f"({iters} rounds); torch_copy_gbs: a 1 GiB fp32 device copy, read + write bytes; "
+                  f"blas_bf16_tflops: torch.matmul bf16 8192^3; medians of {reps}"}
+    del x, src, dst, a, b, sink
     torch.cuda.empty_cache()
     return res
+
+
+def copy_pattern_gbs(torch, stream, st, alg, reps: int = 10):
+    """The decode's own copy pattern alone (mla_probe_tile_copy: the same
+    plan, grid and copy instructions over the same cache, no products):
+    the launch's cache bytes over its median time, GB/s; None where the
+    probe has no kernel (e4m3 cache, 64 query rows or fewer)."""
+    import numpy as np
+    from head_latent_attention_absorbed_amd import MlaError, mla_probe_tile_copy
+
+    w = st.workload
+    if w.cache_dtype != "bf16" or w.q_len * w.heads <= 64:
+        return None
+    sink = torch.zeros(16, dtype=torch.int32, device="cuda")
+    base = st.cache.data_ptr()
+    args = (st.shape, base, base + w.d_latent * st.elem, st.token_stride, st.block_stride, st.block_table,
+            st.seq_lens, st.num_parts, sink, stream)
+    try:
+        mla_probe_tile_copy(*args)
+    except MlaError:
+        return None
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        mla_probe_tile_copy(*args)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    return round(alg["cache_bytes"] / float(np.median(ts)) / 1e9, 1)
 
 
 def host_info():
@@ -614,6 +653,7 @@ def main():
     tpla_res = leg_tpla(torch, np, stream, K, args, w, inputs, alg, steps[0]) if run_legs else None
     gqla_res = leg_gqla(torch, np, stream, K, args) if run_legs else None
     measured = measured_peaks(torch, stream) if run_legs else None
+    copy_gbs = copy_pattern_gbs(torch, stream, steps[0], alg)
     configs_res = (leg_configs(torch, np, stream, K, args, w.name, measured)
                    if run_legs and not args.no_configs else None)
 
@@ -660,6 +700,9 @@ def main():
             algorithmic_bytes_per_launch=alg["decode_bytes"],
             algorithmic_flops_per_launch=alg["attn_flops"],
             avg_launch_us=round(dec_us, 2),
+            copy_pattern_gbs=copy_gbs,
+            frac_of_copy_pattern=(round(alg["decode_bytes"] / (dec_us * 1e-6) / 1e9 / copy_gbs, 4)
+                                  if copy_gbs else None),
         ),
         "measured_peaks": measured,
         "wall_s": round(wall, 3),

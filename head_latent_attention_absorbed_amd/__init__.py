@@ -40,6 +40,9 @@ from .binding import (  # noqa: F401
     mla_tpla_reduce,
     mla_gqa_queries,
     mla_gqa_output,
+    mla_probe_hbm_read,
+    mla_probe_mfma,
+    mla_probe_tile_copy,
     mla_status_string,
     mla_last_error,
 )

@@ -97,6 +97,9 @@ def library() -> ctypes.CDLL:
                "mla_prefill_kv_elems", "mla_prefill_kv", "mla_prefill_attention", "mla_tpla_split_weights",
                "mla_tpla_rotate_cache", "mla_tpla_reduce", "mla_gqa_queries", "mla_gqa_output"):
         getattr(lib, fn).restype = ctypes.c_int
+    lib.mla_probe_hbm_read.argtypes = [P, I64, P, P]
+    lib.mla_probe_mfma.argtypes = [I32, P, ctypes.POINTER(ctypes.c_int64), P]
+    lib.mla_probe_tile_copy.argtypes = [SP, P, P, I64, I64, P, P, I32, P, P]
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
@@ -206,6 +209,24 @@ def mla_append_kv_noalloc(shape: MlaShape, d_model: int, x, w_dkv, rope_base: fl
                                            _ptr(c_kv), _ptr(k_rope), int(token_stride), int(block_stride),
                                            _ptr(kv_scale), _ptr(block_table), _ptr(seq_lens), _stream(stream)),
            "mla_append_kv_noalloc")
+
+
+def mla_probe_hbm_read(buf, nbytes: int, sink, stream=None) -> None:
+    _check(library().mla_probe_hbm_read(_ptr(buf), int(nbytes), _ptr(sink), _stream(stream)), "mla_probe_hbm_read")
+
+
+def mla_probe_mfma(iters: int, sink, stream=None) -> int:
+    """Enqueues the MFMA probe; returns its flop count."""
+    flops = ctypes.c_int64(0)
+    _check(library().mla_probe_mfma(int(iters), _ptr(sink), ctypes.byref(flops), _stream(stream)), "mla_probe_mfma")
+    return flops.value
+
+
+def mla_probe_tile_copy(shape: MlaShape, c_kv, k_rope, token_stride: int, block_stride: int, block_table, seq_lens,
+                        num_parts: int, sink, stream=None) -> None:
+    _check(library().mla_probe_tile_copy(ctypes.byref(shape), _ptr(c_kv), _ptr(k_rope), int(token_stride),
+                                         int(block_stride), _ptr(block_table), _ptr(seq_lens), int(num_parts),
+                                         _ptr(sink), _stream(stream)), "mla_probe_tile_copy")
 
 
 def mla_prefill_workspace_bytes(shape: MlaShape) -> int:

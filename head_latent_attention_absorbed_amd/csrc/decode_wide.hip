@@ -371,6 +371,53 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// The copies of decode_wide_kernel alone: the same plan, grid and copy
+// instructions into the same three-image ring, one barrier per tile and one
+// tile in flight, no products.  Its time is what the decode's copy pattern
+// costs by itself over the launch's cache bytes.
+template <int DC>
+__global__ void __launch_bounds__(256)
+    tile_copy_probe_kernel(DecodeParams p, const int32_t* __restrict__ seq_lens,
+                           const int32_t* __restrict__ block_table, uint32_t* sink) {
+  using Wd = Wide<DC>;
+  constexpr int TB = Wd::TB, NBUF = Wd::NBUF;
+  __shared__ __attribute__((aligned(1024))) char tiles[NBUF * TB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  int u = blockIdx.x;
+  if ((gridDim.x & 7) == 0) u = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int g = u / p.RG;
+  int b = -1, t0 = 0, t1 = 0, L = 0;
+  with_plan(seq_lens, p.B, p.P, lane, [&](const auto& pl) {
+    int s_b = 0;
+    if (g < pl.total) pl.locate_slot(g, lane, b, s_b);
+    if (b >= 0) {
+      t0 = (g - s_b) * pl.W;
+      t1 = min(t0 + pl.W, pl.tiles(b, lane));
+      L = pl.length(b);
+    }
+  });
+  b = uniform(b);
+  if (b < 0) return;
+  t0 = uniform(t0);
+  const int n = uniform(t1) - t0;
+  L = uniform(L);
+  const int32_t* bt = block_table + (int64_t)b * p.bt_stride;
+  const uint32_t tiles_lds = lds_offset(tiles);
+  copy_tile<DC>(p, tile_src(p, uniform(tile_page_load(p, bt, t0)), t0, L), tiles_lds, w);
+  int page_pf = n > 1 ? tile_page_load(p, bt, t0 + 1) : 0;
+  for (int i = 0; i < n; ++i) {
+    vm_wait<0>();  // tile i and the page index read with it
+    block_sync();
+    if (i + 1 < n) {
+      copy_tile<DC>(p, tile_src(p, uniform(page_pf), t0 + i + 1, L), tiles_lds + ((i + 1) % NBUF) * TB, w);
+      if (i + 2 < n) page_pf = tile_page_load(p, bt, t0 + i + 2);
+    }
+  }
+  const uint32_t v = *(const uint32_t*)(tiles + ((n - 1) % NBUF) * TB + tid * 4);
+  if (v == 0x9e3779b9u) sink[0] = v;  // the copies feed a possible store, so they stay
+}
+
 template <int DC>
 hipError_t launch_wide_one(const DecodeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((decode_wide_kernel<DC>), dim3(p.P * p.RG), dim3(256), 0, stream, p, p.seq_lens,
@@ -383,6 +430,16 @@ hipError_t launch_wide_one(const DecodeParams& p, hipStream_t stream) {
 hipError_t launch_decode_wide(const DecodeParams& p, int d_latent, bool fp8, hipStream_t stream) {
   if (fp8) return launch_decode_wide_fp8(p, d_latent, stream);
   return d_latent == 512 ? launch_wide_one<512>(p, stream) : launch_wide_one<256>(p, stream);
+}
+
+hipError_t launch_probe_tile_copy(const DecodeParams& p, int d_latent, uint32_t* sink, hipStream_t stream) {
+  if (d_latent == 512)
+    hipLaunchKernelGGL((tile_copy_probe_kernel<512>), dim3(p.P * p.RG), dim3(256), 0, stream, p, p.seq_lens,
+                       p.block_table, sink);
+  else
+    hipLaunchKernelGGL((tile_copy_probe_kernel<256>), dim3(p.P * p.RG), dim3(256), 0, stream, p, p.seq_lens,
+                       p.block_table, sink);
+  return hipGetLastError();
 }
 
 }  // namespace mla

@@ -89,9 +89,85 @@ mla_status_t hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// The record layout checks shared by the decode and its copy probe: strides,
+// and the RoPE key inside the record after the latent (rope_off = its offset).
+mla_status_t check_cache_layout(const char* who, const mla_shape_t* shape, const void* c_kv, const void* k_rope,
+                                int64_t token_stride, int64_t block_stride, int64_t* rope_off) {
+  const int elem = shape->cache_dtype == MLA_FP8_E4M3 ? 1 : 2;
+  const int64_t off = static_cast<const char*>(k_rope) - static_cast<const char*>(c_kv);
+  if (token_stride <= 0 || token_stride % 16 || block_stride % 16 ||
+      block_stride < (int64_t)shape->block_size * token_stride || (int64_t)shape->block_size * token_stride > INT32_MAX)
+    return fail(MLA_ERR_INVALID_ARG,
+                "%s: token_stride/block_stride must be positive multiples of 16 with "
+                "block_stride >= block_size * token_stride",
+                who);
+  if (off < (int64_t)shape->d_latent * elem || off + (int64_t)shape->d_rope * elem > token_stride)
+    return fail(MLA_ERR_INVALID_ARG, "%s: k_rope must follow the latent inside the record (k_rope - c_kv = %lld bytes)",
+                who, (long long)off);
+  *rope_off = off;
+  return MLA_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
+
+mla_status_t mla_probe_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!buf || !sink) return fail(MLA_ERR_INVALID_ARG, "mla_probe_hbm_read: NULL pointer");
+  if (!aligned16(buf) || bytes <= 0 || bytes % 16)
+    return fail(MLA_ERR_INVALID_ARG, "mla_probe_hbm_read: buf must be 16-byte aligned and bytes a positive multiple of 16");
+  int cus = 0;
+  mla_status_t st = device_cus(&cus);
+  if (st != MLA_OK) return st;
+  return hip_status(mla::launch_probe_hbm_read(buf, bytes, sink, cus, stream), "mla_probe_hbm_read launch");
+}
+
+mla_status_t mla_probe_mfma(int32_t iters, float* sink, int64_t* flops, hipStream_t stream) {
+  if (!sink || !flops) return fail(MLA_ERR_INVALID_ARG, "mla_probe_mfma: NULL pointer");
+  if (iters <= 0) return fail(MLA_ERR_INVALID_ARG, "mla_probe_mfma: iters %d must be positive", iters);
+  int cus = 0;
+  mla_status_t st = device_cus(&cus);
+  if (st != MLA_OK) return st;
+  *flops = mla::probe_mfma_flops(iters, cus);
+  return hip_status(mla::launch_probe_mfma(iters, sink, cus, stream), "mla_probe_mfma launch");
+}
+
+mla_status_t mla_probe_tile_copy(const mla_shape_t* shape, const void* c_kv, const void* k_rope, int64_t token_stride,
+                                 int64_t block_stride, const int32_t* block_table, const int32_t* seq_lens,
+                                 int32_t num_parts, uint32_t* sink, hipStream_t stream) {
+  mla_status_t st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!c_kv || !k_rope || !block_table || !seq_lens || !sink)
+    return fail(MLA_ERR_INVALID_ARG, "mla_probe_tile_copy: NULL pointer");
+  if (shape->cache_dtype != MLA_BF16 || shape->q_len * shape->num_heads <= 64)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_probe_tile_copy: only the bf16 cache with more than 64 query rows");
+  if (!aligned16(c_kv) || !aligned16(k_rope))
+    return fail(MLA_ERR_INVALID_ARG, "mla_probe_tile_copy: c_kv and k_rope must be 16-byte aligned");
+  int64_t rope_off = 0;
+  st = check_cache_layout("mla_probe_tile_copy", shape, c_kv, k_rope, token_stride, block_stride, &rope_off);
+  if (st != MLA_OK) return st;
+  if (num_parts < shape->batch)
+    return fail(MLA_ERR_INVALID_ARG, "mla_probe_tile_copy: num_parts %d < batch %d", num_parts, shape->batch);
+  mla::DecodeParams p{};
+  p.c_kv = static_cast<const char*>(c_kv);
+  p.rope_off = rope_off;
+  p.token_stride = token_stride;
+  p.block_stride = block_stride;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.bt_stride = shape->max_blocks_per_seq;
+  p.B = shape->batch;
+  p.H = shape->num_heads;
+  p.S = shape->q_len;
+  p.R = shape->q_len * shape->num_heads;
+  p.RG = mla::decode_row_groups(p.R);
+  p.P = num_parts;
+  p.block_size = shape->block_size;
+  p.block_shift = __builtin_ctz((unsigned)shape->block_size);
+  if ((int64_t)p.P * p.RG > (int64_t)1 << 30) return fail(MLA_ERR_UNSUPPORTED, "too many work-groups");
+  return hip_status(mla::launch_probe_tile_copy(p, shape->d_latent, sink, stream), "mla_probe_tile_copy launch");
+}
 
 const char* mla_status_string(mla_status_t status) {
   switch (status) {
@@ -153,17 +229,9 @@ mla_status_t mla_decode_paged(const mla_shape_t* shape, const void* q_lat, const
   if (!fp8 && kv_scale) return fail(MLA_ERR_INVALID_ARG, "mla_decode_paged: kv_scale given for a bf16 cache");
   if (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(c_kv) || !aligned16(k_rope) || !aligned16(o_part))
     return fail(MLA_ERR_INVALID_ARG, "mla_decode_paged: tensors must be 16-byte aligned");
-  const int elem = fp8 ? 1 : 2;
-  const int64_t rope_off = static_cast<const char*>(k_rope) - static_cast<const char*>(c_kv);
-  if (token_stride <= 0 || token_stride % 16 || block_stride % 16 ||
-      block_stride < (int64_t)shape->block_size * token_stride || (int64_t)shape->block_size * token_stride > INT32_MAX)
-    return fail(MLA_ERR_INVALID_ARG,
-                "mla_decode_paged: token_stride/block_stride must be positive multiples of 16 with "
-                "block_stride >= block_size * token_stride");
-  if (rope_off < (int64_t)shape->d_latent * elem || rope_off + (int64_t)shape->d_rope * elem > token_stride)
-    return fail(MLA_ERR_INVALID_ARG,
-                "mla_decode_paged: k_rope must follow the latent inside the record (k_rope - c_kv = %lld bytes)",
-                (long long)rope_off);
+  int64_t rope_off = 0;
+  st = check_cache_layout("mla_decode_paged", shape, c_kv, k_rope, token_stride, block_stride, &rope_off);
+  if (st != MLA_OK) return st;
   if (num_parts < shape->batch)
     return fail(MLA_ERR_INVALID_ARG, "mla_decode_paged: num_parts %d < batch %d", num_parts, shape->batch);
   mla::DecodeParams p{};

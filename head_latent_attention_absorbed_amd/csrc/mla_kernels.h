@@ -42,6 +42,14 @@ hipError_t launch_decode(const DecodeParams& p, int d_latent, bool fp8, hipStrea
 hipError_t launch_decode_wide(const DecodeParams& p, int d_latent, bool fp8, hipStream_t stream);
 // Its e4m3 form (decode_wide_fp8.hip).
 hipError_t launch_decode_wide_fp8(const DecodeParams& p, int d_latent, hipStream_t stream);
+// The bf16 128-row decode's tile copies alone (same plan, grid and copy
+// instructions, one tile in flight, no products): a calibration probe.
+hipError_t launch_probe_tile_copy(const DecodeParams& p, int d_latent, uint32_t* sink, hipStream_t stream);
+
+// Calibration probes (probes.hip).
+hipError_t launch_probe_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, int cus, hipStream_t stream);
+int64_t probe_mfma_flops(int iters, int cus);
+hipError_t launch_probe_mfma(int iters, float* sink, int cus, hipStream_t stream);
 
 // Tile-native layout of the prefill's per-head keys and values: for
 // sequence b, head h and 32-position tile j, 16 granule rows g (elements

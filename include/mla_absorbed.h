@@ -381,6 +381,35 @@ mla_status_t mla_gqa_queries(const mla_shape_t* shape, int32_t groups, const voi
 mla_status_t mla_gqa_output(const mla_shape_t* shape, int32_t groups, const float* o_lat, const float* lse_g,
                             void* out, float* lse, hipStream_t stream);
 
+/*
+ * Calibration probes.  Not part of the decode: they measure the device's
+ * achievable rates, the reference points that roofline fractions are also
+ * reported against (nominal peaks: HBM 8 TB/s, bf16 MFMA 2.5 PFLOP/s).  Each
+ * enqueues one kernel on `stream` and returns; the caller times it (HIP
+ * events around the call).
+ *
+ * mla_probe_hbm_read -- streams `bytes` (a positive multiple of 16) of the
+ *   device buffer `buf` (16-byte aligned) through registers, 16-byte loads
+ *   from eight work-groups per CU, four loads in flight per lane.  Rate =
+ *   bytes / time.  `sink` (device, 4 bytes) is written only in the unlikely
+ *   case that the data XOR to a fixed value; it keeps the loads.
+ * mla_probe_mfma -- `iters` (> 0) rounds of four independent
+ *   v_mfma_f32_32x32x16_bf16 chains in two work-groups of four waves per CU;
+ *   *flops receives the launch's flop count (host value, set before the
+ *   launch).  `sink` (device, one float) receives work-group 0's sum.
+ * mla_probe_tile_copy -- the copies of the bf16 decode for more than 64 query
+ *   rows alone: the same split plan, grid, copy instructions and three-image
+ *   LDS ring as mla_decode_paged, one barrier per tile, no products, over the
+ *   cache described exactly as for mla_decode_paged (bf16 cache only,
+ *   q_len * num_heads > 64, else MLA_ERR_UNSUPPORTED).  Rate = the launch's
+ *   cache bytes / time.  `sink` as for mla_probe_hbm_read.
+ */
+mla_status_t mla_probe_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
+mla_status_t mla_probe_mfma(int32_t iters, float* sink, int64_t* flops, hipStream_t stream);
+mla_status_t mla_probe_tile_copy(const mla_shape_t* shape, const void* c_kv, const void* k_rope, int64_t token_stride,
+                                 int64_t block_stride, const int32_t* block_table, const int32_t* seq_lens,
+                                 int32_t num_parts, uint32_t* sink, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* mla_status_string(mla_status_t status);
 

@@ -84,6 +84,12 @@ int main() {
   mla_shape_t g = shape(4, 32, 2, 512);
   EXPECT(mla_gqa_queries(&g, 8, A(30), A(31), A(32), A(33), st), MLA_OK);
   EXPECT(mla_gqa_output(&g, 8, (float*)A(34), (float*)A(35), A(36), (float*)A(37), st), MLA_OK);
+  int64_t flops = 0;
+  EXPECT(mla_probe_hbm_read(A(39), 1 << 20, (uint32_t*)A(40), st), MLA_OK);
+  EXPECT(mla_probe_mfma(100, (float*)A(40), &flops, st), MLA_OK);
+  if (flops <= 0) { std::fprintf(stderr, "mfma probe reported %lld flops\n", (long long)flops); ++g_fail; }
+  EXPECT(mla_probe_tile_copy(&s, ckv, ckv + 1024, ts, bs, (int32_t*)A(7), (int32_t*)A(8), parts, (uint32_t*)A(40),
+                             st), MLA_OK);
   if (g_launches <= before) { std::fprintf(stderr, "valid calls launched nothing\n"); ++g_fail; }
 
   // invalid arguments are refused before anything is launched
@@ -121,6 +127,12 @@ int main() {
          MLA_ERR_INVALID_ARG);
   EXPECT(mla_tpla_split_weights(&s, 3, 1, A(3), A(13), A(26), A(27), st), MLA_ERR_UNSUPPORTED);
   EXPECT(mla_gqa_queries(&g, 5, A(30), A(31), A(32), A(33), st), MLA_ERR_INVALID_ARG);
+  EXPECT(mla_probe_hbm_read(A(39), 24, (uint32_t*)A(40), st), MLA_ERR_INVALID_ARG);
+  EXPECT(mla_probe_hbm_read((char*)A(39) + 8, 1 << 20, (uint32_t*)A(40), st), MLA_ERR_INVALID_ARG);
+  EXPECT(mla_probe_mfma(0, (float*)A(40), &flops, st), MLA_ERR_INVALID_ARG);
+  EXPECT(mla_probe_mfma(100, (float*)A(40), nullptr, st), MLA_ERR_INVALID_ARG);
+  EXPECT(mla_probe_tile_copy(&f8, ckv, ckv + 512, 576, 64 * 576, (int32_t*)A(7), (int32_t*)A(8), 16, (uint32_t*)A(40),
+                             st), MLA_ERR_UNSUPPORTED);
   if (g_launches != before) { std::fprintf(stderr, "an invalid call launched a kernel\n"); ++g_fail; }
 
   // every status has a name; messages are per thread

@@ -64,6 +64,14 @@ bool head_gemm_supported(int K, int N) { return K % 64 == 0 && K <= 512 && N % 6
 hipError_t launch_head_gemm(const HeadGemmParams& p, bool, bool, hipStream_t) { return launched(p.a && p.w && p.c); }
 hipError_t launch_head_gemm_partials(const HeadGemmParams& p, hipStream_t) { return launched(p.c != nullptr); }
 hipError_t launch_append_finish(const AppendParams& p, hipStream_t) { return launched(p.part && p.KS > 0); }
+hipError_t launch_probe_tile_copy(const DecodeParams& p, int, uint32_t* sink, hipStream_t) {
+  return launched(sink && p.P >= p.B && p.RG >= 1);
+}
+hipError_t launch_probe_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, int cus, hipStream_t) {
+  return launched(buf && sink && bytes >= 16 && cus > 0);
+}
+int64_t probe_mfma_flops(int iters, int cus) { return (int64_t)cus * 2 * 4 * 4 * iters * 32768; }
+hipError_t launch_probe_mfma(int iters, float* sink, int cus, hipStream_t) { return launched(sink && iters > 0 && cus > 0); }
 hipError_t append_scratch(void** ptr) {
   alignas(256) static char fake[16];
   *ptr = fake;

@@ -147,6 +147,36 @@ def test_decode_argument_checks():
     assert _decode(sh, q_lat=FAKE + 8) == mla.MLA_ERR_INVALID_ARG                # misaligned
 
 
+def _tile_copy(sh, **kw):
+    a = dict(c_kv=FAKE, k_rope=FAKE + 1024, token_stride=1152, block_stride=64 * 1152, block_table=FAKE,
+             seq_lens=FAKE, num_parts=8, sink=FAKE)
+    a.update(kw)
+    return _lib().mla_probe_tile_copy(ctypes.byref(sh), a["c_kv"], a["k_rope"], a["token_stride"],
+                                      a["block_stride"], a["block_table"], a["seq_lens"], a["num_parts"],
+                                      a["sink"], None)
+
+
+def test_probe_argument_checks():
+    lib = _lib()
+    flops = ctypes.c_int64(0)
+    assert lib.mla_probe_hbm_read(None, 1 << 20, FAKE, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_probe_hbm_read(FAKE, 1 << 20, None, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_probe_hbm_read(FAKE + 4, 1 << 20, FAKE, None) == mla.MLA_ERR_INVALID_ARG   # misaligned
+    assert lib.mla_probe_hbm_read(FAKE, 1000, FAKE, None) == mla.MLA_ERR_INVALID_ARG          # not x16
+    assert lib.mla_probe_hbm_read(FAKE, 0, FAKE, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_probe_mfma(0, FAKE, ctypes.byref(flops), None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_probe_mfma(10, None, ctypes.byref(flops), None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_probe_mfma(10, FAKE, None, None) == mla.MLA_ERR_INVALID_ARG
+    wide = _shape(num_heads=128)
+    assert _tile_copy(_shape()) == mla.MLA_ERR_UNSUPPORTED                    # 16 rows: no 128-row kernel
+    assert _tile_copy(_shape(num_heads=128, cache_dtype=mla.MLA_FP8_E4M3), k_rope=FAKE + 512, token_stride=576,
+                      block_stride=64 * 576) == mla.MLA_ERR_UNSUPPORTED      # bf16 only
+    assert _tile_copy(wide, sink=None) == mla.MLA_ERR_INVALID_ARG
+    assert _tile_copy(wide, k_rope=FAKE + 512) == mla.MLA_ERR_INVALID_ARG    # RoPE key overlaps the latent
+    assert _tile_copy(wide, num_parts=1) == mla.MLA_ERR_INVALID_ARG
+    assert _tile_copy(wide, c_kv=FAKE + 8, k_rope=FAKE + 1032) == mla.MLA_ERR_INVALID_ARG
+
+
 def test_status_strings():
     _lib()
     assert mla.mla_status_string(0) == "MLA_OK"
