@@ -106,47 +106,66 @@ __device__ __forceinline__ void copy_tile(const DecodeParams& p, const TileSrc& 
   }
 }
 
-// with the softmax steps of the next tile placed between the column blocks.
-// P comes from LDS (`pb`: [row block][k-step][lane] x 16 B), V^T through
-// transposing reads of the tile image `tb` (the pattern of pv_tile in
-// tile_ops.h).
-template <int DC, bool STEPS, class SM>
-__device__ __forceinline__ void pv_rows(const char* tb, const char* pb, f32x16 (&O)[4][Geo<DC>::NB / 4], int w,
-                                        SM& sm) {
-  constexpr int NBW = Geo<DC>::NB / 4;
-  const int lane = opaque_lane();
-  const int half = lane >> 5;
-  const int i16 = lane & 15, grp = lane >> 4;
-  const int jj = i16 >> 2, qq = i16 & 3, ch = grp & 1;
-  const int godd = qq >> 1;
-  const char* vb = tb + (2 * ch + godd) * kRow + (((4 * half + jj) ^ (godd << 2)) << 4) + ((qq & 1) << 3);
-  bf16x8 pf[4][2];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) pf[rb][j] = *(const bf16x8*)(pb + (rb * 2 + j) * 1024 + lane * 16);
+// Operands of the lagged P . V for this wave's column blocks over all four
+// row blocks: P from LDS (`pb`: [row block][k-step][lane] x 16 B), V^T
+// through transposing reads of the tile image `tb` (the pattern of pv_tile in
+// tile_ops.h).  load() reads P and the first column block's V; the score
+// chain calls it ten MFMAs before its end (score_mfma's read-ahead hook), so
+// that the first P . V MFMAs do not wait for LDS.
+template <int DC>
+struct PvOperands {
+  static constexpr int AT = Geo<DC>::KS - 10;
   struct VF { s16x4 x0, x1, y0, y1; };
-  auto vread = [&](int nb) {
-    const char* a = vb + nb * 4 * kRow;
+  const char* vb;
+  const char* pb;
+  bf16x8 pf[4][2];
+  VF v0;
+  __device__ __forceinline__ PvOperands(const char* tb, const char* pb_, int w) : pb(pb_) {
+    const int lane = opaque_lane();
+    const int half = lane >> 5;
+    const int i16 = lane & 15, grp = lane >> 4;
+    const int jj = i16 >> 2, qq = i16 & 3, ch = grp & 1;
+    const int godd = qq >> 1;
+    vb = tb + (2 * ch + godd) * kRow + (((4 * half + jj) ^ (godd << 2)) << 4) + ((qq & 1) << 3) +
+         w * (Geo<DC>::NB / 4) * 4 * kRow;
+  }
+  __device__ __forceinline__ VF vread(int cb) const {
+    const char* a = vb + cb * 4 * kRow;
     VF f;
     f.x0 = lds_read_tr16(a);
     f.x1 = lds_read_tr16(a + 8 * 16);
     f.y0 = lds_read_tr16(a + 16 * 16);
     f.y1 = lds_read_tr16(a + 24 * 16);
     return f;
-  };
+  }
+  __device__ __forceinline__ void load() {
+    const int lane = opaque_lane();
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) pf[rb][j] = *(const bf16x8*)(pb + (rb * 2 + j) * 1024 + lane * 16);
+    v0 = vread(0);
+  }
+};
+
+// P . V of one tile (operands from PvOperands, already loaded) with the
+// softmax steps of the next tile placed between the column blocks.
+template <int DC, bool STEPS, class SM>
+__device__ __forceinline__ void pv_rows(const PvOperands<DC>& op, f32x16 (&O)[4][Geo<DC>::NB / 4], SM& sm) {
+  constexpr int NBW = Geo<DC>::NB / 4;
+  using VF = typename PvOperands<DC>::VF;
   constexpr int SPB = (SM::STEPS + NBW - 1) / NBW;  // softmax steps per column block
-  VF cur = vread(w * NBW);
+  VF cur = op.v0;
 #pragma unroll
   for (int cb = 0; cb < NBW; ++cb) {
     VF nxt;
-    if (cb + 1 < NBW) nxt = vread(w * NBW + cb + 1);
+    if (cb + 1 < NBW) nxt = op.vread(cb + 1);
     const s16x8 a0 = {cur.x0[0], cur.x0[1], cur.x0[2], cur.x0[3], cur.x1[0], cur.x1[1], cur.x1[2], cur.x1[3]};
     const s16x8 a1 = {cur.y0[0], cur.y0[1], cur.y0[2], cur.y0[3], cur.y1[0], cur.y1[1], cur.y1[2], cur.y1[3]};
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      O[rb][cb] = mfma32((bf16x8)a0, pf[rb][0], O[rb][cb]);
-      O[rb][cb] = mfma32((bf16x8)a1, pf[rb][1], O[rb][cb]);
+      O[rb][cb] = mfma32((bf16x8)a0, op.pf[rb][0], O[rb][cb]);
+      O[rb][cb] = mfma32((bf16x8)a1, op.pf[rb][1], O[rb][cb]);
     }
     if constexpr (STEPS) {
 #pragma unroll
@@ -311,8 +330,10 @@ __global__ void __launch_bounds__(256)
     // steps): two inlined copies of the P . V would each get their own
     // assignment of the accumulators and a copy of all of them at the join.
     const int pos0 = t * kTile;
-    WideSoftmax<false> sm{score_mfma<DC, WideDma<DC>::NI>(tiles + buf * TB, qf, dma), nullptr,
-                          limit - pos0 - 4 * half, p.scale_log2, m_run, l_run, half};
+    PvOperands<DC> pv(tiles + ((i + NBUF - 1) % NBUF) * TB, pbuf + ((i - 1) & 1) * PB, w);
+    WideSoftmax<false> sm{PV ? score_mfma<DC, WideDma<DC>::NI>(tiles + buf * TB, qf, dma, pv)
+                             : score_mfma<DC, WideDma<DC>::NI>(tiles + buf * TB, qf, dma),
+                          nullptr, limit - pos0 - 4 * half, p.scale_log2, m_run, l_run, half};
     if constexpr (PV) {
       // rows of the accumulators whose maximum moved at tile i - 1 (rare)
       if (fl.x | fl.y | fl.z | fl.w) {
@@ -322,7 +343,7 @@ __global__ void __launch_bounds__(256)
         for (int rb = 0; rb < 4; ++rb) a[rb] = alph[pbi][32 * rb + col];
         rescale_rows<NBW>(O, a);
       }
-      pv_rows<DC, true>(tiles + ((i - 1) % NBUF) * TB, pbuf + ((i - 1) & 1) * PB, O, w, sm);
+      pv_rows<DC, true>(pv, O, sm);
     } else {
       sm.all();
     }
@@ -351,7 +372,9 @@ __global__ void __launch_bounds__(256)
       rescale_rows<NBW>(O, a);
     }
     NoSteps none;
-    pv_rows<DC, false>(vt, pbuf + pbi * PB, O, w, none);
+    PvOperands<DC> pv(vt, pbuf + pbi * PB, w);
+    pv.load();
+    pv_rows<DC, false>(pv, O, none);
   }
 
   // ---- normalise and write this part's partial and lse

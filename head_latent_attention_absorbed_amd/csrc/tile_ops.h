@@ -65,12 +65,20 @@ __device__ __forceinline__ void mfma_v_last(f32x16& acc, bf16x8 a, bf16x8 b) {
                : "v"(a), "v"(b));
 }
 
+// The no-op read-ahead hook of score_mfma.
+struct NoPre {
+  static constexpr int AT = -1;
+  __device__ __forceinline__ void load() {}
+};
+
 // S^T = K . Q^T of one 32-token tile (32 tokens x this wave's 32 rows):
 // A = token `col`, granule 2ks + half, from LDS; B = the query fragments.
 // NDMA > 0 spreads that many instructions of the next tile's copy over
-// the MFMA stream.
-template <int DC, int NDMA, class Dma>
-__device__ __forceinline__ f32x16 score_mfma(const char* tb, const bf16x8 (&qf)[Geo<DC>::KS], const Dma& dma) {
+// the MFMA stream; pre.load() runs before the MFMA of k-step Pre::AT (the
+// operand reads of whatever follows the chain, issued while it runs).
+template <int DC, int NDMA, class Dma, class Pre>
+__device__ __forceinline__ f32x16 score_mfma(const char* tb, const bf16x8 (&qf)[Geo<DC>::KS], const Dma& dma,
+                                             Pre& pre) {
   using Gm = Geo<DC>;
   constexpr int PD = kScoreAhead;  // k-steps of K fragments read ahead of their MFMA
   const int lane = opaque_lane();
@@ -93,6 +101,7 @@ __device__ __forceinline__ f32x16 score_mfma(const char* tb, const bf16x8 (&qf)[
     if constexpr (NDMA > 0) {
       if (ks % (Gm::KS / NDMA) == 0) dma.issue(ks / (Gm::KS / NDMA));  // next tile's copy, spread out
     }
+    if (ks == Pre::AT) pre.load();
     if (ks == 0) mfma_v_first(sacc, kf[ks], qf[ks]);
     else if (ks + 1 < Gm::KS) mfma_v_acc(sacc, kf[ks], qf[ks]);
     else mfma_v_last(sacc, kf[ks], qf[ks]);
@@ -101,6 +110,11 @@ __device__ __forceinline__ f32x16 score_mfma(const char* tb, const bf16x8 (&qf)[
   // (the softmax, or the lagged P.V of the previous tile) is hoisted into it.
   __builtin_amdgcn_sched_barrier(0);
   return sacc;
+}
+template <int DC, int NDMA, class Dma>
+__device__ __forceinline__ f32x16 score_mfma(const char* tb, const bf16x8 (&qf)[Geo<DC>::KS], const Dma& dma) {
+  NoPre none;
+  return score_mfma<DC, NDMA>(tb, qf, dma, none);
 }
 
 // Online-softmax update of one tile's scores, in kSoftmaxSteps steps that

@@ -150,7 +150,5 @@ struct NoSteps {
   __device__ __forceinline__ void step(int) {}
 };
 
-// P . V of one tile for this wave's column blocks over all four row blocks,
-
 }  // namespace
 }  // namespace mla
