@@ -98,7 +98,8 @@ def roofline_of(alg, us, measured=None):
 def measured_peaks(torch, stream, reps: int = 5):
     """Reference points measured on this GPU with the library's calibration
     probes (HIP kernels, medians over reps, HIP events): the HBM read rate of
-    mla_probe_hbm_read over 2 GiB (16-byte loads from every CU) and the bf16
+    mla_probe_hbm_read over 2 GiB (contiguous chunks per work-group,
+    non-temporal 16-byte loads from every CU) and the bf16
     MFMA rate of mla_probe_mfma (independent 32x32x16 chains on every SIMD).
     Beside them, for context: a 1 GiB torch device copy (read + write bytes)
     and a bf16 GEMM of 8192^3 on the device's BLAS."""
@@ -408,9 +409,16 @@ def leg_gqla(torch, np, stream, K, args):
     g_tokens = int(sum(int(x) for x in g_in["seq_lens"]))
     g_bytes = {"mqa_absorb": g_tokens * gw.record_elems * 2,
                "gqa": g_tokens * GQLA_GROUPS * (gw.d_nope + gw.d_v + gw.d_rope) * 2}
+    # The GQA records repeat the shared RoPE key in every group (the record
+    # layout used here; the method itself has one RoPE key per token): the
+    # bytes with a single shared RoPE stream are given beside the measured
+    # path's, so the comparison can be read without that inflation.
+    rope_shared = g_tokens * (GQLA_GROUPS * (gw.d_nope + gw.d_v) + gw.d_rope) * 2
     return {
         "what": "GQLA's two decoding paths at s_q = 2, H = 32 in 8 groups, B = 16, context 8192: absorbed MQA "
                 "over the latent vs GQA over per-group [K_nope | V | k_rope] records",
+        "gqa_cache_bytes_with_one_rope_stream": rope_shared,
+        "gqa_rope_repeat_factor": round(g_bytes["gqa"] / rope_shared, 4),
         "paths": {k: {"us_median": {c: round(t, 2) for c, t in v.items()}, "cache_bytes": g_bytes[k],
                       "decode_gbs": round(g_bytes[k] / (v["decode"] * 1e-6) / 1e9, 1),
                       "decode_frac": round(g_bytes[k] / (v["decode"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}

@@ -2,9 +2,10 @@
 // the decode's roofline fractions are also given against.  Not part of the
 // decode path.
 //
-//   hbm_read_kernel   streams a buffer through registers with 16-byte loads
-//                     from every CU, four loads in flight per lane (a
-//                     grid-stride loop): the achievable HBM read rate.
+//   hbm_read_kernel   streams a buffer through registers: each work-group
+//                     reads one contiguous chunk, sixteen non-temporal
+//                     16-byte loads in flight per lane: the achievable HBM
+//                     read rate.
 //   mfma_peak_kernel  four independent chains of v_mfma_f32_32x32x16_bf16 in
 //                     two waves per SIMD on every CU: the achievable bf16
 //                     MFMA rate.
@@ -18,24 +19,27 @@ namespace {
 
 constexpr uint32_t kNever = 0x9e3779b9u;  // a value the probes' sinks are written only if they produce
 
+// Work-group g streams the g-th contiguous chunk of the buffer; each lane
+// keeps 16 non-temporal 16-byte loads in flight (256 lanes x 16 B apart).
+// Contiguous chunks per work-group stream faster than a grid-stride walk,
+// which scatters each work-group's loads over the whole buffer.
 __global__ void __launch_bounds__(256) hbm_read_kernel(const uint4* __restrict__ p, int64_t n16, uint32_t* sink) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  uint4 acc = {0u, 0u, 0u, 0u};
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-    acc.x ^= a.x ^ b.x ^ c.x ^ d.x;
-    acc.y ^= a.y ^ b.y ^ c.y ^ d.y;
-    acc.z ^= a.z ^ b.z ^ c.z ^ d.z;
-    acc.w ^= a.w ^ b.w ^ c.w ^ d.w;
+  constexpr int U = 16;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t beg = (int64_t)blockIdx.x * per;
+  const int64_t end = beg + per < n16 ? beg + per : n16;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  int64_t i = beg + threadIdx.x;
+  for (; i + (U - 1) * 256 < end; i += U * 256) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(q + i + u * 256);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u];
   }
-  for (; i < n16; i += stride) {
-    const uint4 a = p[i];
-    acc.x ^= a.x;
-    acc.y ^= a.y;
-    acc.z ^= a.z;
-    acc.w ^= a.w;
-  }
+  for (; i < end; i += 256) acc ^= q[i];
   const uint32_t v = acc.x ^ acc.y ^ acc.z ^ acc.w;
   if (v == kNever) sink[0] = v;  // the loads feed a possible store, so they stay
 }

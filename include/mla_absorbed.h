@@ -389,9 +389,9 @@ mla_status_t mla_gqa_output(const mla_shape_t* shape, int32_t groups, const floa
  * events around the call).
  *
  * mla_probe_hbm_read -- streams `bytes` (a positive multiple of 16) of the
- *   device buffer `buf` (16-byte aligned) through registers, 16-byte loads
- *   from eight work-groups per CU, four loads in flight per lane.  Rate =
- *   bytes / time.  `sink` (device, 4 bytes) is written only in the unlikely
+ *   device buffer `buf` (16-byte aligned) through registers: eight
+ *   work-groups per CU, each streaming one contiguous chunk with sixteen
+ *   non-temporal 16-byte loads in flight per lane.  Rate = bytes / time.  `sink` (device, 4 bytes) is written only in the unlikely
  *   case that the data XOR to a fixed value; it keeps the loads.
  * mla_probe_mfma -- `iters` (> 0) rounds of four independent
  *   v_mfma_f32_32x32x16_bf16 chains in two work-groups of four waves per CU;
