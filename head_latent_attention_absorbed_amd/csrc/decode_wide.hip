@@ -148,13 +148,23 @@ struct PvOperands {
   }
 };
 
+// The no-op publication hook of pv_rows.
+struct NoPublish {
+  __device__ __forceinline__ void operator()() const {}
+};
+
 // P . V of one tile (operands from PvOperands, already loaded) with the
-// softmax steps of the next tile placed between the column blocks.
-template <int DC, bool STEPS, class SM>
-__device__ __forceinline__ void pv_rows(const PvOperands<DC>& op, f32x16 (&O)[4][Geo<DC>::NB / 4], SM& sm) {
+// softmax steps of the next tile placed between the column blocks.  The
+// steps are front-loaded (the last column block gets none), and pub() runs
+// right after the last step, so that the softmax's tail and the publication
+// of its results run under the remaining MFMAs instead of after them.
+template <int DC, bool STEPS, class SM, class Pub = NoPublish>
+__device__ __forceinline__ void pv_rows(const PvOperands<DC>& op, f32x16 (&O)[4][Geo<DC>::NB / 4], SM& sm,
+                                        const Pub& pub = Pub{}) {
   constexpr int NBW = Geo<DC>::NB / 4;
   using VF = typename PvOperands<DC>::VF;
-  constexpr int SPB = (SM::STEPS + NBW - 1) / NBW;  // softmax steps per column block
+  // softmax steps per column block: ceil(2 STEPS / (2 NBW - 1))
+  constexpr int SPB = (2 * SM::STEPS + 2 * NBW - 2) / (2 * NBW - 1);
   VF cur = op.v0;
 #pragma unroll
   for (int cb = 0; cb < NBW; ++cb) {
@@ -171,6 +181,7 @@ __device__ __forceinline__ void pv_rows(const PvOperands<DC>& op, f32x16 (&O)[4]
 #pragma unroll
       for (int j = 0; j < SPB; ++j)
         if (cb * SPB + j < SM::STEPS) sm.step(cb * SPB + j);
+      if (cb * SPB < SM::STEPS && (cb + 1) * SPB >= SM::STEPS) pub();
     }
     if (cb + 1 < NBW) cur = nxt;
   }
@@ -343,19 +354,25 @@ __global__ void __launch_bounds__(256)
         for (int rb = 0; rb < 4; ++rb) a[rb] = alph[pbi][32 * rb + col];
         rescale_rows<NBW>(O, a);
       }
-      pv_rows<DC, true>(pv, O, sm);
+    }
+    // Publish P and the rescale factor of tile i (the first tile's factor is
+    // 0 against an initial maximum of -inf, but the accumulators are still
+    // zero then: no rescale).  Their buffers [i & 1] were last read in
+    // iteration i - 1, before this iteration's barrier.
+    auto publish = [&]() {
+      char* pw = pbuf + (i & 1) * PB + (w * 2) * 1024 + lane * 16;
+      *(bf16x8*)pw = sm.pf0;
+      *(bf16x8*)(pw + 1024) = sm.pf1;
+      if (half == 0) alph[i & 1][32 * w + col] = sm.alpha;
+      const bool any = PV && __any(sm.alpha != 1.0f);
+      if (lane == 0) rflag[i & 1][w] = any;
+    };
+    if constexpr (PV) {
+      pv_rows<DC, true>(pv, O, sm, publish);
     } else {
       sm.all();
+      publish();
     }
-    // publish P and the rescale factor of tile i (the first tile's factor is
-    // 0 against an initial maximum of -inf, but the accumulators are still
-    // zero then: no rescale)
-    char* pw = pbuf + (i & 1) * PB + (w * 2) * 1024 + lane * 16;
-    *(bf16x8*)pw = sm.pf0;
-    *(bf16x8*)(pw + 1024) = sm.pf1;
-    if (half == 0) alph[i & 1][32 * w + col] = sm.alpha;
-    const bool any = PV && __any(sm.alpha != 1.0f);
-    if (lane == 0) rflag[i & 1][w] = any;
   };
   tile_step(0, std::false_type{});
 #pragma nounroll
