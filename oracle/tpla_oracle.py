@@ -35,7 +35,8 @@ from dataclasses import replace
 
 import numpy as np
 
-from .mla_oracle import _heads, cache_values, decode_one
+from .append_oracle import f64_to_bf16_bits
+from .mla_oracle import _heads, bf16_to_f64, cache_values, decode_one
 
 
 def hadamard(d: int) -> np.ndarray:
@@ -74,15 +75,31 @@ def aggregate(shard_out: np.ndarray) -> np.ndarray:
     return shard_out.sum(axis=0)
 
 
-def tpla_decode(inputs: dict, n_shards: int, rotate: bool, batches=None, heads=None):
+def stored_bf16(x: np.ndarray) -> np.ndarray:
+    """x as it is kept in bf16 storage: rounded to the nearest bf16 value
+    (ties to even), back in fp64."""
+    return bf16_to_f64(f64_to_bf16_bits(x))
+
+
+def tpla_decode(inputs: dict, n_shards: int, rotate: bool, batches=None, heads=None, stored: bool = False):
     """TPLA decode of every sequence (or ``batches``) and head (or ``heads``)
     with ``n_shards`` latent shards.  Returns dict(out [B, S_q, nh, d_v] summed
-    over shards, shard_out [n, B, S_q, nh, d_v], shard_lse [n, B, S_q, nh])."""
+    over shards, shard_out [n, B, S_q, nh, d_v], shard_lse [n, B, S_q, nh]).
+
+    With ``stored`` the rotated latent channels and weight slices are first
+    rounded to bf16, the precision the cache and the weights are kept in
+    (the rotated cache replaces the cached latent in place, and the shards'
+    weight slices are bf16 like the weights they come from); without it the
+    basis change is exact."""
     w = inputs["workload"]
     if w.d_latent % n_shards:
         raise ValueError("d_latent must split evenly")
     dcs = w.d_latent // n_shards
     values, w_uk, w_uv = rotated(inputs, rotate)
+    if stored:
+        values = values.copy()
+        values[..., : w.d_latent] = stored_bf16(values[..., : w.d_latent])
+        w_uk, w_uv = stored_bf16(w_uk), stored_bf16(w_uv)
     q_nope, q_rope, _, _, _ = _heads(inputs)
     batches = list(range(w.batch)) if batches is None else list(batches)
     nh = w.heads if heads is None else len(list(heads))

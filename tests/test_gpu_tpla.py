@@ -111,6 +111,29 @@ def test_tpla_decode(n, hadamard):
                 finite_only=True)
 
 
+@pytest.mark.parametrize("hadamard", [True, False])
+def test_tpla_decode_against_stored_model(hadamard):
+    """The tighter companion check: against the oracle's TPLA decode on the
+    rotated latent and weight slices rounded to bf16 (the precision the path
+    keeps them in), the summed output and every shard meet the plain decode's
+    bounds, not twice them."""
+    import torch
+
+    n = 2
+    inputs = make_inputs(SMALL)
+    print(f"[case] tpla decode stored model n={n} hadamard={hadamard}", flush=True)
+    st = _step(inputs, n, hadamard)
+    st.run()
+    torch.cuda.synchronize()
+    ref = oracle.tpla_decode(inputs, n, hadamard, stored=True)
+    tol_abs, tol_rel = tolerances(SMALL)
+    compare("out", to_np(st.out), ref["out"], tol_abs, tol_rel)
+    parts = to_np(st.parts)
+    for i in range(n):
+        compare(f"shard {i} out", parts[i], ref["shard_out"][i], tol_abs, tol_rel)
+        compare(f"shard {i} lse", to_np(st.shard_lse[i]), ref["shard_lse"][i], tol_abs, tol_rel, finite_only=True)
+
+
 def test_one_plain_shard_is_the_decode():
     """n = 1 without the basis change runs the decode's own kernels on the same
     values: the result must match the fused decode step bit for bit."""

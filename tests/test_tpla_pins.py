@@ -119,3 +119,34 @@ def test_planted_unrotated_values_fail(monkeypatch):
     inp = _inputs()
     got = oracle.tpla_decode(inp, 1, True)
     assert not _close(got["out"], oracle.decode(inp)["out"], 1e-6)
+
+
+def test_stored_rounding_is_exact_without_rotation():
+    """Without the basis change the latent and the weights are bf16 values
+    already: the stored-precision model must change nothing."""
+    inp = _inputs()
+    a = oracle.tpla_decode(inp, 2, False)
+    b = oracle.tpla_decode(inp, 2, False, stored=True)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["shard_lse"], b["shard_lse"])
+
+
+def test_stored_rounding_is_nearest_bf16():
+    """Every rounded value is a bf16 value within half a bf16 step of the
+    exact one (8 significant bits: half a step is 2^-9 of the magnitude's
+    binade), rounding twice changes nothing, and the rounded rotated decode
+    stays close to the exact one."""
+    inp = _inputs()
+    w = inp["workload"]
+    values, w_uk, _ = tpla.rotated(inp, True)
+    x = np.concatenate([values[..., : w.d_latent].ravel(), w_uk.ravel()])
+    x = x[np.isfinite(x)]  # unused cache slots hold NaN by construction
+    r = tpla.stored_bf16(x)
+    nz = x != 0
+    half_step = 2.0 ** (np.floor(np.log2(np.abs(x[nz]))) - 8)
+    assert np.all(np.abs(r[nz] - x[nz]) <= half_step * (1 + 1e-12))
+    assert np.array_equal(tpla.stored_bf16(r), r)
+    assert np.array_equal(r[~nz], x[~nz])
+    exact = oracle.tpla_decode(inp, 2, True)["out"]
+    kept = oracle.tpla_decode(inp, 2, True, stored=True)["out"]
+    assert not np.array_equal(exact, kept)
+    assert _close(exact, kept, 2e-2)
