@@ -80,6 +80,12 @@ SMALL_CASES = {
     # fp8 with 32 rows (one wave) and d_c = 512
     "fp8_h32": replace(small_workload("gqa7b", batch=2, seq_len=(3, 200), max_seq_len=256, forced_lens=(3, 161)),
                        cache_dtype="fp8_e4m3"),
+    # 3-token tail over 40 heads, bf16: 120 rows, one 128-row group with 8 rows past the end
+    "bf16_sq3_h40": replace(small_workload("kimi_k2_fp8", batch=2, heads=40, seq_len=(3, 300), max_seq_len=320,
+                                           forced_lens=(3, 290)), q_len=3, cache_dtype="bf16"),
+    # 4-token tail over 40 heads, e4m3: 160 rows, the second 128-row group 32 rows deep
+    "fp8_sq4_h40": small_workload("kimi_k2_fp8", batch=2, heads=40, seq_len=(4, 300), max_seq_len=320,
+                                  forced_lens=(4, 257)),
 }
 
 
