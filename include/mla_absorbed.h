@@ -68,7 +68,7 @@ extern "C" {
 typedef enum {
   MLA_OK = 0,
   MLA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad stride or alignment  */
-  MLA_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for                 */
+  MLA_ERR_UNSUPPORTED = 2, /* valid request the library has no kernel for              */
   MLA_ERR_HIP = 3          /* a HIP runtime call (device query or launch) failed         */
 } mla_status_t;
 
