@@ -43,6 +43,7 @@ from .binding import (  # noqa: F401
     mla_probe_hbm_read,
     mla_probe_mfma,
     mla_probe_tile_copy,
+    mla_validate_decode_inputs,
     mla_status_string,
     mla_last_error,
 )

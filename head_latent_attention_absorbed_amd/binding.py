@@ -100,6 +100,7 @@ def library() -> ctypes.CDLL:
     lib.mla_probe_hbm_read.argtypes = [P, I64, P, P]
     lib.mla_probe_mfma.argtypes = [I32, P, ctypes.POINTER(ctypes.c_int64), P]
     lib.mla_probe_tile_copy.argtypes = [SP, P, P, I64, I64, P, P, I32, P, P]
+    lib.mla_validate_decode_inputs.argtypes = [SP, P, P, I64, P, P]
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
@@ -227,6 +228,15 @@ def mla_probe_tile_copy(shape: MlaShape, c_kv, k_rope, token_stride: int, block_
     _check(library().mla_probe_tile_copy(ctypes.byref(shape), _ptr(c_kv), _ptr(k_rope), int(token_stride),
                                          int(block_stride), _ptr(block_table), _ptr(seq_lens), int(num_parts),
                                          _ptr(sink), _stream(stream)), "mla_probe_tile_copy")
+
+
+def mla_validate_decode_inputs(shape: MlaShape, block_table, seq_lens, num_pages: int, violations,
+                               stream=None) -> None:
+    """Enqueue the device check of the decode's lengths and block table;
+    ``violations`` (device int32) holds the count once the stream has run."""
+    _check(library().mla_validate_decode_inputs(ctypes.byref(shape), _ptr(block_table), _ptr(seq_lens),
+                                                int(num_pages), _ptr(violations), _stream(stream)),
+           "mla_validate_decode_inputs")
 
 
 def mla_prefill_workspace_bytes(shape: MlaShape) -> int:

@@ -169,6 +169,29 @@ mla_status_t mla_probe_tile_copy(const mla_shape_t* shape, const void* c_kv, con
   return hip_status(mla::launch_probe_tile_copy(p, shape->d_latent, sink, stream), "mla_probe_tile_copy launch");
 }
 
+mla_status_t mla_validate_decode_inputs(const mla_shape_t* shape, const int32_t* block_table, const int32_t* seq_lens,
+                                        int64_t num_pages, int32_t* violations, hipStream_t stream) {
+  mla_status_t st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!block_table || !seq_lens || !violations)
+    return fail(MLA_ERR_INVALID_ARG, "mla_validate_decode_inputs: NULL pointer");
+  if (num_pages <= 0)
+    return fail(MLA_ERR_INVALID_ARG, "mla_validate_decode_inputs: num_pages %lld must be positive",
+                (long long)num_pages);
+  if (reinterpret_cast<uintptr_t>(violations) % 4)
+    return fail(MLA_ERR_INVALID_ARG, "mla_validate_decode_inputs: violations must be 4-byte aligned");
+  mla::ValidateParams p{};
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.num_pages = num_pages;
+  p.B = shape->batch;
+  p.S = shape->q_len;
+  p.MB = shape->max_blocks_per_seq;
+  p.block_size = shape->block_size;
+  p.out = violations;
+  return hip_status(mla::launch_validate(p, stream), "mla_validate_decode_inputs launch");
+}
+
 const char* mla_status_string(mla_status_t status) {
   switch (status) {
     case MLA_OK: return "MLA_OK";

@@ -51,6 +51,16 @@ hipError_t launch_probe_hbm_read(const void* buf, int64_t bytes, uint32_t* sink,
 int64_t probe_mfma_flops(int iters, int cus);
 hipError_t launch_probe_mfma(int iters, float* sink, int cus, hipStream_t stream);
 
+// Input validation (validate.hip).
+struct ValidateParams {
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int64_t num_pages;
+  int B, S, MB, block_size;
+  int32_t* out;
+};
+hipError_t launch_validate(const ValidateParams& p, hipStream_t stream);
+
 // Tile-native layout of the prefill's per-head keys and values: for
 // sequence b, head h and 32-position tile j, 16 granule rows g (elements
 // 8g..8g+7) of 32 slots; position 32 j + t sits in slot t ^ (4 (g & 1)).

@@ -411,6 +411,29 @@ mla_status_t mla_probe_tile_copy(const mla_shape_t* shape, const void* c_kv, con
                                  int32_t num_parts, uint32_t* sink, hipStream_t stream);
 
 /* Static description of a status code. */
+/*
+ * Input validation.
+ *
+ * mla_validate_decode_inputs -- counts, on the device, the violations of the
+ *   conditions mla_decode_paged (and the merges after it) assume of the
+ *   per-sequence inputs it reads from device memory and cannot check on the
+ *   host: for every sequence b, seq_lens[b] is 0 (an idle slot) or lies in
+ *   [S_q, max_blocks_per_seq * block_size]; and each of its first
+ *   ceil(seq_lens[b] / block_size) entries block_table[b][i] is a page id in
+ *   [0, num_pages) (the paged record cache of mla_decode_paged: pages of
+ *   block_size records, a row of physical page ids per sequence).  Entries
+ *   past those are not read; a sequence whose length fails counts once and
+ *   its entries are not examined.
+ *   violations (device, one int32, 4-byte aligned) receives the count, 0 when
+ *   every condition holds.  The call is enqueued on `stream` like the others
+ *   and the caller reads the count after synchronizing.  One work-group: a
+ *   check for debug runs and tests, not for the decode's hot path.
+ *   Errors (MLA_ERR_INVALID_ARG): NULL pointers, num_pages <= 0, a misaligned
+ *   violations pointer, or a shape the decode would reject.
+ */
+mla_status_t mla_validate_decode_inputs(const mla_shape_t* shape, const int32_t* block_table, const int32_t* seq_lens,
+                                        int64_t num_pages, int32_t* violations, hipStream_t stream);
+
 const char* mla_status_string(mla_status_t status);
 
 /* Message for the calling thread's most recent non-OK status ("" if none). */

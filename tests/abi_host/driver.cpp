@@ -90,6 +90,7 @@ int main() {
   if (flops <= 0) { std::fprintf(stderr, "mfma probe reported %lld flops\n", (long long)flops); ++g_fail; }
   EXPECT(mla_probe_tile_copy(&s, ckv, ckv + 1024, ts, bs, (int32_t*)A(7), (int32_t*)A(8), parts, (uint32_t*)A(40),
                              st), MLA_OK);
+  EXPECT(mla_validate_decode_inputs(&s, (int32_t*)A(7), (int32_t*)A(8), 1000, (int32_t*)A(41), st), MLA_OK);
   if (g_launches <= before) { std::fprintf(stderr, "valid calls launched nothing\n"); ++g_fail; }
 
   // invalid arguments are refused before anything is launched
@@ -130,6 +131,10 @@ int main() {
   EXPECT(mla_probe_hbm_read(A(39), 24, (uint32_t*)A(40), st), MLA_ERR_INVALID_ARG);
   EXPECT(mla_probe_hbm_read((char*)A(39) + 8, 1 << 20, (uint32_t*)A(40), st), MLA_ERR_INVALID_ARG);
   EXPECT(mla_probe_mfma(0, (float*)A(40), &flops, st), MLA_ERR_INVALID_ARG);
+  EXPECT(mla_validate_decode_inputs(&s, (int32_t*)A(7), (int32_t*)A(8), 0, (int32_t*)A(41), st), MLA_ERR_INVALID_ARG);
+  EXPECT(mla_validate_decode_inputs(&s, nullptr, (int32_t*)A(8), 10, (int32_t*)A(41), st), MLA_ERR_INVALID_ARG);
+  EXPECT(mla_validate_decode_inputs(&s, (int32_t*)A(7), (int32_t*)A(8), 10, (int32_t*)((char*)A(41) + 2), st),
+         MLA_ERR_INVALID_ARG);
   EXPECT(mla_probe_mfma(100, (float*)A(40), nullptr, st), MLA_ERR_INVALID_ARG);
   EXPECT(mla_probe_tile_copy(&f8, ckv, ckv + 512, 576, 64 * 576, (int32_t*)A(7), (int32_t*)A(8), 16, (uint32_t*)A(40),
                              st), MLA_ERR_UNSUPPORTED);

@@ -72,6 +72,9 @@ hipError_t launch_probe_hbm_read(const void* buf, int64_t bytes, uint32_t* sink,
 }
 int64_t probe_mfma_flops(int iters, int cus) { return (int64_t)cus * 2 * 4 * 4 * iters * 32768; }
 hipError_t launch_probe_mfma(int iters, float* sink, int cus, hipStream_t) { return launched(sink && iters > 0 && cus > 0); }
+hipError_t launch_validate(const ValidateParams& p, hipStream_t) {
+  return launched(p.block_table && p.seq_lens && p.out && p.num_pages > 0 && p.B > 0);
+}
 hipError_t append_scratch(void** ptr) {
   alignas(256) static char fake[16];
   *ptr = fake;

@@ -177,6 +177,19 @@ def test_probe_argument_checks():
     assert _tile_copy(wide, c_kv=FAKE + 8, k_rope=FAKE + 1032) == mla.MLA_ERR_INVALID_ARG
 
 
+def test_validate_argument_checks():
+    lib = _lib()
+    s = _shape()
+    sp = ctypes.byref(s)
+    assert lib.mla_validate_decode_inputs(sp, None, FAKE, 100, FAKE, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_validate_decode_inputs(sp, FAKE, None, 100, FAKE, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_validate_decode_inputs(sp, FAKE, FAKE, 100, None, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_validate_decode_inputs(sp, FAKE, FAKE, 0, FAKE, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_validate_decode_inputs(sp, FAKE, FAKE, 100, FAKE + 2, None) == mla.MLA_ERR_INVALID_ARG
+    bad = _shape(block_size=48)
+    assert lib.mla_validate_decode_inputs(ctypes.byref(bad), FAKE, FAKE, 100, FAKE, None) != mla.MLA_OK
+
+
 def test_status_strings():
     _lib()
     assert mla.mla_status_string(0) == "MLA_OK"
