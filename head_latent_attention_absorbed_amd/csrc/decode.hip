@@ -13,10 +13,13 @@
 //                                          the B-operand lane layout
 //
 // Each wave owns 32 query rows (r = s*H + h) and keeps, per row, the running
-// max m, the running sum l and O^T[512 or 256, 32] in accumulators; the
-// softmax is online (BLASST abstract on the same listing relies on the same
-// running state), with the max only re-based when it grows by more than 2^8
-// so the accumulator rescale is rare.  A work-group of NW waves shares each
+// max m, the running sum l and O^T[512 or 256, 32] in accumulators (with at
+// most 32 rows and a latency-bound launch, the two waves of a work-group may
+// own the same rows instead: both compute the scores and the softmax, and
+// each accumulates half of O^T's latent columns).  The softmax is online
+// (BLASST abstract on the same listing relies on the same running state),
+// with the max only re-based when it grows by more than 2^8 so the
+// accumulator rescale is rare.  A work-group of NW waves shares each
 // tile; tiles stream through an LDS ring (direct global->LDS DMA for bf16;
 // for fp8 the same DMA into a staging slot, then an exact e4m3->bf16 decode
 // in LDS).  Each sequence's token axis is cut into parts of W tiles (the
@@ -88,21 +91,21 @@ __device__ __forceinline__ void zero_tail(char* tb, int nv, int tid) {
   }
 }
 
-// Pitch of one row of a staged fp16 partial: the row plus 16 bytes, so that
-// the rows of one LDS write instruction start in different banks.
-template <int DC>
-constexpr int stage_pitch() { return DC * 2 + 16; }
+// Pitch of one row of NBK staged fp16 column blocks: the row plus 16 bytes,
+// so that the rows of one LDS write instruction start in different banks.
+template <int NBK>
+constexpr int stage_pitch() { return NBK * 64 + 16; }
 
 // The same write as store_partial<NB> for fp16 partials, through LDS: the
-// wave puts its 32 normalised rows into `stage` (row = lane % 32), then
-// writes them back out with every store instruction covering whole rows
-// (DC * 2 contiguous bytes), instead of 32 rows x 32 bytes per instruction.
-// `stage` is this wave's own region; nothing else may use it meanwhile.
-template <int DC>
+// wave puts its 32 normalised rows of NB column blocks (latent columns col0 ..
+// col0 + 32 NB) into `stage` (row = lane % 32), then writes them back out
+// with every store instruction covering whole rows (NB * 64 contiguous
+// bytes), instead of 32 rows x 32 bytes per instruction.  `stage` is this
+// wave's own region; nothing else may use it meanwhile.
+template <int DC, int NB>
 __device__ __forceinline__ void store_partial_staged(const DecodeParams& p, const f32x16* O, float inv, int64_t slot,
-                                                     int rowbase, char* stage) {
-  constexpr int NB = DC / 32;
-  constexpr int PITCH = stage_pitch<DC>();
+                                                     int rowbase, int col0, char* stage) {
+  constexpr int PITCH = stage_pitch<NB>();
   const int lane = opaque_lane();
   const int half = lane >> 5, col = lane & 31;
   char* mine = stage + col * PITCH + 16 * (1 - half);
@@ -123,18 +126,20 @@ __device__ __forceinline__ void store_partial_staged(const DecodeParams& p, cons
     __builtin_amdgcn_sched_barrier(0);  // one accumulator block at a time
   }
   // A wave's LDS accesses complete in order, so the reads below see the writes.
-  constexpr int LPR = DC / 8;       // lanes per row (16 bytes each)
+  constexpr int LPR = NB * 4;       // lanes per row (16 bytes each)
   constexpr int RPI = kWave / LPR;  // rows per store instruction
   const int sub = lane / LPR, gi = lane % LPR;
 #pragma unroll 4
   for (int r0 = 0; r0 < 32; r0 += RPI) {
     const int r = r0 + sub;
     const uint4 x = *(const uint4*)(stage + r * PITCH + 16 * gi);
-    if (rowbase + r < p.R) *(uint4*)((_Float16*)p.o_part + (slot * p.R + rowbase + r) * DC + 8 * gi) = x;
+    if (rowbase + r < p.R) *(uint4*)((_Float16*)p.o_part + (slot * p.R + rowbase + r) * DC + col0 + 8 * gi) = x;
   }
 }
 
-template <int DC, bool FP8, int NW, int NBUF>
+// CS: waves that share each query row, each accumulating NB / CS of the
+// latent column blocks (1, or 2 for at most 32 rows per work-group).
+template <int DC, bool FP8, int NW, int NBUF, int CS>
 __global__ void __launch_bounds__(NW * kWave)
     decode_kernel(DecodeParams p, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ block_table,
                   const float* __restrict__ kv_scale) {
@@ -142,6 +147,9 @@ __global__ void __launch_bounds__(NW * kWave)
   constexpr int TB = Gm::TILE_BYTES;
   constexpr int NI = Gm::GPT / (2 * NW);
   constexpr int AHEAD = NBUF - 1;  // tiles in flight ahead of the one computed
+  constexpr int RW = 32 * NW / CS;  // query rows per work-group
+  constexpr int NBW = Gm::NB / CS;  // accumulator blocks per wave
+  static_assert(NW % CS == 0 && Gm::NB % CS == 0, "column slices must divide the waves and the blocks");
   static_assert(Gm::GPT % (2 * NW) == 0, "tile rows must split evenly over the waves");
   static_assert(AHEAD >= 1, "ring too small");
   static_assert(FP8 || NI * AHEAD <= 63, "DMA groups must fit vmcnt");
@@ -155,6 +163,7 @@ __global__ void __launch_bounds__(NW * kWave)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = uniform(tid >> 6);
+  const int wr = w / CS, wc = w % CS;  // this wave's row slot and column slice
   const int half = lane >> 5, col = lane & 31;
 
   // XCD-aware placement: consecutive work items (the row groups of one token
@@ -184,7 +193,7 @@ __global__ void __launch_bounds__(NW * kWave)
   const int k0 = uniform(cu[pb]) + uniform(plan[1]);
   const int k1 = min(k0 + uniform(plan[2]), uniform(cu[pb + 1]));
 
-  const int row = rg * (32 * NW) + 32 * w + col;  // this lane's query row (S^T column)
+  const int row = rg * RW + 32 * wr + col;  // this lane's query row (S^T column)
   const uint32_t tiles_lds = lds_offset(tiles);
 
   // The first segment's query rows are touched (one dword per 128-byte line)
@@ -193,9 +202,9 @@ __global__ void __launch_bounds__(NW * kWave)
   int bc = uniform(seq_of_tile(cu, p.B, k0));
   uint32_t touch = 0;
   {
-    const char* qa = (const char*)(p.q_lat + ((int64_t)bc * p.R + rg * (32 * NW)) * DC);
-    const char* qb = (const char*)(p.q_rope + ((int64_t)bc * p.R + rg * (32 * NW)) * 64);
-    const int rows = min(32 * NW, p.R - rg * (32 * NW));
+    const char* qa = (const char*)(p.q_lat + ((int64_t)bc * p.R + rg * RW) * DC);
+    const char* qb = (const char*)(p.q_rope + ((int64_t)bc * p.R + rg * RW) * 64);
+    const int rows = min(RW, p.R - rg * RW);
     const int la = rows * DC * 2 / 128, lb = rows * 64 * 2 / 128;
     for (int i = tid; i < la + lb; i += NW * kWave)
       touch += i < la ? *(const uint32_t*)(qa + 128 * i) : *(const uint32_t*)(qb + 128 * (i - la));
@@ -306,7 +315,7 @@ __global__ void __launch_bounds__(NW * kWave)
     bf16x8 qf[Gm::KS];
     if (row < p.R) {
       const int ln = opaque_lane();
-      const int qrow = rg * (32 * NW) + 32 * w + (ln & 31);
+      const int qrow = rg * RW + 32 * wr + (ln & 31);
       const bf16x8* ql = (const bf16x8*)(p.q_lat + ((int64_t)bc * p.R + qrow) * DC + 8 * (ln >> 5));
       const bf16x8* qr = (const bf16x8*)(p.q_rope + ((int64_t)bc * p.R + qrow) * 64 + 8 * (ln >> 5));
 #pragma unroll
@@ -330,7 +339,7 @@ __global__ void __launch_bounds__(NW * kWave)
     } else {
       vm_wait<0>();
     }
-    f32x16 O[Gm::NB];
+    f32x16 O[NBW];
     float m_run = -__builtin_inff(), l_run = 0.0f;
     bf16x8 pf0, pf1;
     float alpha;
@@ -359,9 +368,9 @@ __global__ void __launch_bounds__(NW * kWave)
                                FULL, p.scale_log2, pf0, pf1, alpha, NoDma{});
       }
       if constexpr (!FIRST) {
-        if (__any(alpha != 1.0f)) rescale<DC>(O, alpha);
+        if (__any(alpha != 1.0f)) rescale(O, alpha);
       }
-      pv_tile<DC, kPvAhead, FIRST>(tiles + buf * TB, pf0, pf1, O);
+      pv_tile<DC, kPvAhead, FIRST>(tiles + buf * TB + wc * NBW * 4 * kRow, pf0, pf1, O);
       tile_end();
       ++k;
     };
@@ -385,16 +394,17 @@ __global__ void __launch_bounds__(NW * kWave)
       // spilled) across the tile loop
       const int ln = opaque_lane();
       const int lhalf = ln >> 5, lcol = ln & 31;
-      const int lrow = rg * (32 * NW) + 32 * w + lcol;
-      if (lrow < p.R && lhalf == 0) p.lse_part[slot * p.R + lrow] = lse;
+      const int lrow = rg * RW + 32 * wr + lcol;
+      if (lrow < p.R && lhalf == 0 && wc == 0) p.lse_part[slot * p.R + lrow] = lse;
       // After the part's last tile the ring is idle (every copy has landed and
       // been consumed), so an fp16 partial is staged through it.
-      constexpr bool STAGE_FITS = NW * 32 * stage_pitch<DC>() <= NBUF * TB;
+      constexpr bool STAGE_FITS = NW * 32 * stage_pitch<NBW>() <= NBUF * TB;
       if (STAGE_FITS && p.o_half && kend == k1) {
         block_sync();
-        store_partial_staged<DC>(p, O, inv, slot, rg * (32 * NW) + 32 * w, tiles + w * 32 * stage_pitch<DC>());
+        store_partial_staged<DC, NBW>(p, O, inv, slot, rg * RW + 32 * wr, wc * NBW * 32,
+                                      tiles + w * 32 * stage_pitch<NBW>());
       } else if (lrow < p.R) {
-        store_partial<Gm::NB>(p, O, inv, (slot * p.R + lrow) * DC, lhalf);
+        store_partial<NBW>(p, O, inv, (slot * p.R + lrow) * DC + wc * NBW * 32, lhalf);
       }
     }
     ++bc;
@@ -403,20 +413,29 @@ __global__ void __launch_bounds__(NW * kWave)
   }
 }
 
-template <int DC, bool FP8, int NW, int NBUF>
+template <int DC, bool FP8, int NW, int NBUF, int CS>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   const int grid = p.P * p.RG;
-  hipLaunchKernelGGL((decode_kernel<DC, FP8, NW, NBUF>), dim3(grid), dim3(NW * kWave), 0, stream, p,
+  hipLaunchKernelGGL((decode_kernel<DC, FP8, NW, NBUF, CS>), dim3(grid), dim3(NW * kWave), 0, stream, p,
                      p.seq_lens, p.block_table, p.kv_scale);
   return hipGetLastError();
 }
 
-// One- and two-wave groups (up to 64 query rows) run two work-groups per CU
-// on a 2-tile ring; 128-row groups use decode_wide.hip.
+// Work-groups run two per CU on a 2-tile ring; 128-row groups use
+// decode_wide.hip.  Up to 64 query rows, two waves own 32 rows each.  Up to
+// 32 rows, one wave issues a tile's copies and both products itself, and two
+// such work-groups per CU keep the CU's copy path busy (it bounds the tile
+// loop, so splitting a tile's work over more waves only adds a barrier per
+// tile) -- unless the block table holds at most one tile per two part slots:
+// then every part is one tile on an otherwise idle CU, the launch is bound
+// by the latency of that one tile, and two waves that split the latent
+// columns between them (both computing the scores) finish it sooner.
 template <int DC, bool FP8>
 hipError_t launch_dc(const DecodeParams& p, int nw, hipStream_t stream) {
-  if (nw == 2) return launch_one<DC, FP8, 2, 2>(p, stream);
-  return launch_one<DC, FP8, 1, 2>(p, stream);
+  if (nw == 2) return launch_one<DC, FP8, 2, 2, 1>(p, stream);
+  const int64_t max_tiles = (int64_t)p.B * p.bt_stride * p.block_size / kTile;
+  if (2 * max_tiles <= p.P) return launch_one<DC, FP8, 2, 2, 2>(p, stream);
+  return launch_one<DC, FP8, 1, 2, 1>(p, stream);
 }
 
 }  // namespace

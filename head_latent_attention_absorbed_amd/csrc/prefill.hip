@@ -122,7 +122,7 @@ prefill_kernel(PrefillParams p) {
     score_tile<128, false, 0>(tb, nullptr, qf, m_run, l_run, kt * kTile, limit, FULL, p.scale_log2, pf0, pf1,
                               alpha, NoDma{});
     if constexpr (!FIRST) {
-      if (__any(alpha != 1.0f)) rescale<128>(O, alpha);
+      if (__any(alpha != 1.0f)) rescale(O, alpha);
     }
     pv_tile<128, kPvAhead, FIRST>(tb + KROWS * kRow, pf0, pf1, O);
   };

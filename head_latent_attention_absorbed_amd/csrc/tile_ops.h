@@ -290,13 +290,14 @@ __device__ __forceinline__ void score_tile(const char* tb, const float* tsc, con
   alpha = sm.alpha;
 }
 
-// O^T += V^T . P^T for one tile; the four transposed reads of block nb + AH
-// are issued before the two MFMAs of block nb.  Source lane (group G = lane/16,
-// i = lane%16) reads token 16 j2 + 8 h + 4 (G/2) + i/4 and columns
-// 32 nb + 16 (G%2) + 4 (i%4) .. +3.
-template <int DC, int AH, bool FIRST>
-__device__ __forceinline__ void pv_tile(const char* tb, bf16x8 pf0, bf16x8 pf1, f32x16 (&O)[Geo<DC>::NB]) {
-  using Gm = Geo<DC>;
+// O^T += V^T . P^T for one tile over NBK 32-column blocks starting at `tb`
+// (a tile, or a tile advanced by 4 granule rows per skipped block); the four
+// transposed reads of block nb + AH are issued before the two MFMAs of block
+// nb.  Source lane (group G = lane/16, i = lane%16) reads token
+// 16 j2 + 8 h + 4 (G/2) + i/4 and columns 32 nb + 16 (G%2) + 4 (i%4) .. +3.
+template <int DC, int AH, bool FIRST, int NBK>
+__device__ __forceinline__ void pv_tile(const char* tb, bf16x8 pf0, bf16x8 pf1, f32x16 (&O)[NBK]) {
+  static_assert(NBK <= Geo<DC>::NB, "more blocks than latent columns");
   const int lane = opaque_lane();
   const int half = lane >> 5;
   const int i16 = lane & 15, grp = lane >> 4;
@@ -313,12 +314,12 @@ __device__ __forceinline__ void pv_tile(const char* tb, bf16x8 pf0, bf16x8 pf1, 
     f.y1 = lds_read_tr16(a + 24 * 16);
     return f;
   };
-  VF vf[Gm::NB];
+  VF vf[NBK];
 #pragma unroll
   for (int nb = 0; nb < AH; ++nb) vf[nb] = vread(nb);
 #pragma unroll
-  for (int nb = 0; nb < Gm::NB; ++nb) {
-    if (nb + AH < Gm::NB) vf[nb + AH] = vread(nb + AH);
+  for (int nb = 0; nb < NBK; ++nb) {
+    if (nb + AH < NBK) vf[nb + AH] = vread(nb + AH);
     const VF& cur = vf[nb];
     const s16x8 a0 = {cur.x0[0], cur.x0[1], cur.x0[2], cur.x0[3], cur.x1[0], cur.x1[1], cur.x1[2], cur.x1[3]};
     const s16x8 a1 = {cur.y0[0], cur.y0[1], cur.y0[2], cur.y0[3], cur.y1[0], cur.y1[1], cur.y1[2], cur.y1[3]};
@@ -329,8 +330,8 @@ __device__ __forceinline__ void pv_tile(const char* tb, bf16x8 pf0, bf16x8 pf1, 
   // nb + AH, MFMAs of block nb).
   __builtin_amdgcn_sched_group_barrier(0x100, 4 * AH, 1);
 #pragma unroll
-  for (int nb = 0; nb < Gm::NB; ++nb) {
-    if (nb + AH < Gm::NB) __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+  for (int nb = 0; nb < NBK; ++nb) {
+    if (nb + AH < NBK) __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
   }
 }
@@ -340,12 +341,12 @@ __device__ __forceinline__ void pv_tile(const char* tb, bf16x8 pf0, bf16x8 pf1, 
 // accumulators stay in AGPRs and one temporary VGPR suffices; the leading
 // wait states cover an MFMA that may just have written them (the compiler's
 // hazard check does not look inside inline asm).
-template <int DC>
-__device__ __forceinline__ void rescale(f32x16 (&O)[Geo<DC>::NB], float alpha) {
+template <int NBK>
+__device__ __forceinline__ void rescale(f32x16 (&O)[NBK], float alpha) {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-  for (int nb = 0; nb < Geo<DC>::NB; ++nb) {
+  for (int nb = 0; nb < NBK; ++nb) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float x = O[nb][i];

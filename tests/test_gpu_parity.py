@@ -65,8 +65,12 @@ SMALL_CASES = {
     # DeepSeek-V3-like heads over ragged lengths (one token, one partial tile, multi-page)
     "h128_ragged": small_workload("deepseek_v3", batch=3, seq_len=(1, 900), max_seq_len=1024,
                                   forced_lens=(1, 77, 515), spare_blocks=3),
-    # 32 heads (one wave per work-group)
+    # 32 heads: a block table of at most one tile per two part slots, so two
+    # waves split the latent columns of each single-tile part
     "h32": small_workload("gqa7b", batch=3, seq_len=(1, 700), max_seq_len=768, forced_lens=(129, 64, 33)),
+    # the same lengths under a block table with room for 8192 tokens: one wave
+    # per work-group, which issues the copies and both products itself
+    "h32_roomy": small_workload("gqa7b", batch=3, seq_len=(1, 700), max_seq_len=8192, forced_lens=(129, 64, 33)),
     # latent-split shard: d_c = 256, fp32 output
     "dc256": small_workload("tpla_shard", batch=2, seq_len=(40, 400), max_seq_len=512, forced_lens=(40, 300)),
     # 4-token causal tail over an e4m3 cache, 256 rows (two row groups)
@@ -77,7 +81,7 @@ SMALL_CASES = {
                                            forced_lens=(5, 97)), cache_dtype="bf16"),
     # an idle batch slot (seq_len 0) next to live ones
     "idle_slot": small_workload("deepseek_v3", batch=3, seq_len=(50, 300), max_seq_len=320, forced_lens=(0, 65, 0)),
-    # fp8 with 32 rows (one wave) and d_c = 512
+    # fp8 with 32 rows (two column-split waves) and d_c = 512
     "fp8_h32": replace(small_workload("gqa7b", batch=2, seq_len=(3, 200), max_seq_len=256, forced_lens=(3, 161)),
                        cache_dtype="fp8_e4m3"),
     # 3-token tail over 40 heads, bf16: 120 rows, one 128-row group with 8 rows past the end
@@ -103,7 +107,7 @@ def test_small_parity_default_split(name, merge):
 
 
 @pytest.mark.parametrize("merge", list(MERGES))
-@pytest.mark.parametrize("name", ["tiny", "h128_ragged", "dc256", "fp8_sq4_h64", "idle_slot", "h32"])
+@pytest.mark.parametrize("name", ["tiny", "h128_ragged", "dc256", "fp8_sq4_h64", "idle_slot", "h32", "h32_roomy"])
 def test_small_parity_fp32_partials(name, merge):
     """The same step with fp32 split partials (o_part) instead of fp16."""
     inputs = make_inputs(SMALL_CASES[name])
