@@ -62,15 +62,17 @@ def algorithmic(w, seq_lens):
                 step_flops=attn_flops + proj_flops, record_bytes=rec, tokens=sum(L))
 
 
-KERNEL_SOURCES = ("decode.hip", "decode_wide.hip", "decode_wide_fp8.hip", "wide_common.h", "decode_common.h",
-                  "split_plan.h", "tile_ops.h", "mla_device.h", "mla_kernels.h")
+KERNEL_SOURCES = ("decode.hip", "decode_wide.hip", "decode_wide_fp8.hip", "decode_wide_pair.hip", "wide_common.h",
+                  "decode_common.h", "split_plan.h", "tile_ops.h", "mla_device.h", "mla_kernels.h")
 RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # 312.5
 
 
 def decode_kernel_name(w) -> str:
     if w.q_len * w.heads <= 64:
         return "decode_kernel"
-    return "decode_f8_kernel" if w.cache_dtype == "fp8_e4m3" else "decode_wide_kernel"
+    if w.cache_dtype == "fp8_e4m3":
+        return "decode_f8_kernel"
+    return "decode_wide_pair_kernel" if w.d_latent == 256 else "decode_wide_kernel"
 
 
 def roofline_of(alg, us, measured=None):

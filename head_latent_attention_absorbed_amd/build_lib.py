@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmla_absorbed.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["decode.hip", "decode_wide.hip", "decode_wide_fp8.hip", "combine.hip", "head_gemm.hip", "append.hip", "prefill.hip", "prefill_expand.hip", "tpla.hip", "gqa.hip", "probes.hip", "validate.hip", "mla_api.cpp"]
+SOURCES = ["decode.hip", "decode_wide.hip", "decode_wide_fp8.hip", "decode_wide_pair.hip", "combine.hip", "head_gemm.hip", "append.hip", "prefill.hip", "prefill_expand.hip", "tpla.hip", "gqa.hip", "probes.hip", "validate.hip", "mla_api.cpp"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -89,23 +89,6 @@ __device__ __forceinline__ WideDma<DC> wide_dma(const DecodeParams& p, const Til
                      active};
 }
 
-// bf16 tile copy: this wave's NI granule-row pairs.  Lanes whose token is
-// past the sequence's length copy token 0 instead (finite data the softmax
-// weighs 0), so every instruction runs with all lanes.
-template <int DC>
-__device__ __forceinline__ void copy_tile(const DecodeParams& p, const TileSrc& s, uint32_t buf_lds, int w) {
-  constexpr int NW = 4, NI = Geo<DC>::GPT / (2 * NW);
-  const int ol = opaque_lane();
-  int tok = load_token(ol);
-  tok = tok < s.nv ? tok : 0;
-  const uint32_t lane_off = (uint32_t)tok * (uint32_t)p.token_stride + 16u * (ol >> 5);
-#pragma unroll
-  for (int q = 0; q < NI; ++q) {
-    const int g0 = 2 * (q * NW + w);
-    lds_dma16(s.run + granule_offset<DC, 16>(p, g0), lane_off, uniform(buf_lds + (q * NW + w) * 1024));
-  }
-}
-
 // Operands of the lagged P . V for this wave's column blocks over all four
 // row blocks: P from LDS (`pb`: [row block][k-step][lane] x 16 B), V^T
 // through transposing reads of the tile image `tb` (the pattern of pv_tile in
@@ -469,7 +452,7 @@ hipError_t launch_wide_one(const DecodeParams& p, hipStream_t stream) {
 
 hipError_t launch_decode_wide(const DecodeParams& p, int d_latent, bool fp8, hipStream_t stream) {
   if (fp8) return launch_decode_wide_fp8(p, d_latent, stream);
-  return d_latent == 512 ? launch_wide_one<512>(p, stream) : launch_wide_one<256>(p, stream);
+  return d_latent == 512 ? launch_wide_one<512>(p, stream) : launch_decode_wide_pair(p, d_latent, stream);
 }
 
 hipError_t launch_probe_tile_copy(const DecodeParams& p, int d_latent, uint32_t* sink, hipStream_t stream) {

@@ -42,6 +42,8 @@ hipError_t launch_decode(const DecodeParams& p, int d_latent, bool fp8, hipStrea
 hipError_t launch_decode_wide(const DecodeParams& p, int d_latent, bool fp8, hipStream_t stream);
 // Its e4m3 form (decode_wide_fp8.hip).
 hipError_t launch_decode_wide_fp8(const DecodeParams& p, int d_latent, hipStream_t stream);
+// Its bf16 form at d_c = 256 with two tiles per step (decode_wide_pair.hip).
+hipError_t launch_decode_wide_pair(const DecodeParams& p, int d_latent, hipStream_t stream);
 // The bf16 128-row decode's tile copies alone (same plan, grid and copy
 // instructions, one tile in flight, no products): a calibration probe.
 hipError_t launch_probe_tile_copy(const DecodeParams& p, int d_latent, uint32_t* sink, hipStream_t stream);

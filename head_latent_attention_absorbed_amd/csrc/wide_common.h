@@ -1,6 +1,6 @@
-// Pieces shared by the two 128-row decode kernels (gfx950): the tile
-// source of a part, the rare rescale of accumulator rows, the online softmax
-// of one tile in steps, and the step-less stand-in.
+// Pieces shared by the 128-row decode kernels (gfx950): the tile source of
+// a part, the bf16 tile copy, the rare rescale of accumulator rows, the
+// online softmax of one tile in steps, and the step-less stand-in.
 #pragma once
 #include "decode_common.h"
 #include "mla_device.h"
@@ -35,6 +35,23 @@ __device__ __forceinline__ TileSrc tile_src(const DecodeParams& p, int page, int
   s.nv = min(L - pos0, kTile);
   s.page_slot = page * p.block_size + slot0;
   return s;
+}
+
+// bf16 tile copy by four waves: this wave's NI granule-row pairs.  Lanes
+// whose token is past the sequence's length copy token 0 instead (finite data
+// the softmax weighs 0), so every instruction runs with all lanes.
+template <int DC>
+__device__ __forceinline__ void copy_tile(const DecodeParams& p, const TileSrc& s, uint32_t buf_lds, int w) {
+  constexpr int NW = 4, NI = Geo<DC>::GPT / (2 * NW);
+  const int ol = opaque_lane();
+  int tok = load_token(ol);
+  tok = tok < s.nv ? tok : 0;
+  const uint32_t lane_off = (uint32_t)tok * (uint32_t)p.token_stride + 16u * (ol >> 5);
+#pragma unroll
+  for (int q = 0; q < NI; ++q) {
+    const int g0 = 2 * (q * NW + w);
+    lds_dma16(s.run + granule_offset<DC, 16>(p, g0), lane_off, uniform(buf_lds + (q * NW + w) * 1024));
+  }
 }
 
 // Multiply rows of the accumulators by their factors (rare; see rescale in

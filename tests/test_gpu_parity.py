@@ -73,6 +73,13 @@ SMALL_CASES = {
     "h32_roomy": small_workload("gqa7b", batch=3, seq_len=(1, 700), max_seq_len=8192, forced_lens=(129, 64, 33)),
     # latent-split shard: d_c = 256, fp32 output
     "dc256": small_workload("tpla_shard", batch=2, seq_len=(40, 400), max_seq_len=512, forced_lens=(40, 300)),
+    # d_c = 256 with odd tile counts (4 and 15, the last tiles partial): parts
+    # that end on a pair with one tile
+    "dc256_odd": small_workload("tpla_shard", batch=2, seq_len=(97, 451), max_seq_len=512, forced_lens=(97, 451)),
+    # d_c = 256, two query tokens over 64 heads (128 rows): the causal tail
+    # inside a pair of tiles
+    "dc256_sq2_h64": small_workload("tpla_shard", batch=2, heads=64, q_len=2, seq_len=(2, 300), max_seq_len=320,
+                                    forced_lens=(2, 289)),
     # 4-token causal tail over an e4m3 cache, 256 rows (two row groups)
     "fp8_sq4_h64": small_workload("kimi_k2_fp8", batch=3, seq_len=(4, 300), max_seq_len=384,
                                   forced_lens=(4, 170, 33)),
@@ -118,7 +125,7 @@ def test_small_parity_fp32_partials(name, merge):
 
 
 @pytest.mark.parametrize("merge", list(MERGES))
-@pytest.mark.parametrize("name", ["h128_ragged", "dc256", "fp8_sq4_h64", "h32"])
+@pytest.mark.parametrize("name", ["h128_ragged", "dc256", "dc256_odd", "dc256_sq2_h64", "fp8_sq4_h64", "h32"])
 @pytest.mark.parametrize("extra_parts", [0, 1, 5])
 def test_small_parity_few_splits(name, extra_parts, merge):
     """Few token parts: each part runs many tiles (num_parts = B gives one
