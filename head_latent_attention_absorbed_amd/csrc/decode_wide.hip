@@ -215,80 +215,91 @@ __global__ void __launch_bounds__(256)
   const int rowbase = rg * ROWS;
   const uint32_t tiles_lds = lds_offset(tiles);
 
-  // ---- prologue: the first copies and the query block; wait for both.
+  // ---- prologue: the query block and the first tile.
   // Query fragments: lane (col, half) needs row col's values 16 ks + 8 half
-  // .. +8 for k-step ks, which as direct loads touch 32 rows (cache lines)
-  // per instruction.  The first KST k-steps are instead copied row-contiguous
-  // into free image slots (one instruction per 1 KiB, 16-byte chunks XOR
-  // swizzled by row so that the fragment reads spread over the banks) and
-  // read from LDS; the rest are loaded directly.
-  constexpr int KST = DC / 32;            // staged k-steps (half the latent)
-  constexpr int CPR = 2 * KST;            // staged 16-byte chunks per row
-  constexpr int SROW = CPR * 16;          // staged bytes per row
+  // .. +8 for k-step ks; loaded directly, each instruction would touch 32
+  // rows (cache lines).  The block instead reaches the registers through LDS
+  // by row-contiguous DMA (whole 1 KiB pieces per instruction, 16-byte
+  // chunks XOR-swizzled by row so that the fragment reads spread over the
+  // banks), in two rounds: round 1 the first half of the latent (into free
+  // image slots) and the RoPE part (into the P buffer), round 2 the second
+  // half of the latent into the slots round 1 used.  Each wave stages and
+  // reads only its own 32 rows, so the rounds need no barrier.  The first
+  // tile's page index is a scalar read waited for on its own counter while
+  // round 1 is in flight, so the tile's copy goes out before round 1 lands
+  // instead of queueing behind the query.
+  static_assert(AHEAD == 1, "the prologue copies one tile");
+  constexpr int KST = DC / 32;            // k-steps of one latent half
+  constexpr int CPR = 2 * KST;            // 16-byte chunks of a staged half row
+  constexpr int SROW = CPR * 16;          // bytes of a staged half row
   constexpr int RPI = 1024 / SROW;        // rows per copy instruction
-  static_assert(NW * 32 * SROW <= (NBUF - 1) * TB, "the staged query fits the free image slots");
+  static_assert(NW * 32 * SROW <= (NBUF - 1) * TB, "the staged latent half fits the free image slots");
+  static_assert(NW * 32 * 128 <= 2 * PB, "the staged RoPE rows fit the P buffer");
   char* stg = tiles + TB + w * 32 * SROW;
+  char* rstg = pbuf + w * 32 * 128;
   const int qrow0 = rowbase + 32 * w;     // this wave's first query row
   const char* qseq = (const char*)(p.q_lat + (int64_t)b * p.R * DC);
-  // Tiles copied before the loop: 0 .. AHEAD-1; page_pf: the page of the
-  // next tile the loop copies (tile AHEAD).
-  constexpr int PRE = AHEAD;
-  int page_pf = 0;
-  // The page reads go out first and the query copies right behind them; the
-  // tile copies, which need the pages, are issued after the query's loads, so
-  // that the query's round trip overlaps the page read's.
-  int pg[PRE];
-#pragma unroll
-  for (int a = 0; a < PRE; ++a) pg[a] = a < n ? tile_page_load(p, bt, t0 + a) : 0;
-  page_pf = PRE < n ? tile_page_load(p, bt, t0 + PRE) : 0;
-  {
+  const char* rseq = (const char*)(p.q_rope + (int64_t)b * p.R * 64);
+  // page of tile 1 (copied by iteration 0): a vector load, waited for at
+  // the first tile barrier
+  int page_pf = n > 1 ? tile_page_load(p, bt, t0 + 1) : 0;
+  // rows past R re-read row R-1 (zeroed after the reads)
+  auto stage_latent = [&](int hx) {
     const int ol = opaque_lane();
     const int rr = ol / CPR, cs = ol % CPR;
 #pragma unroll
     for (int j = 0; j < 32 / RPI; ++j) {
-      const int r = j * RPI + rr;                         // row of the wave's 32
-      const int rg_ = min(qrow0 + r, p.R - 1);            // rows past R re-read row R-1 (discarded)
-      const int chunk = cs ^ (r & (CPR - 1) & 15);        // the slot cs of row r holds this chunk
-      lds_dma16(qseq, (uint32_t)(rg_ * DC * 2 + chunk * 16), lds_offset(stg + j * 1024));
+      const int r = j * RPI + rr;
+      const int rg_ = min(qrow0 + r, p.R - 1);
+      const int chunk = cs ^ (r & (CPR - 1) & 15);  // the slot cs of row r holds this chunk
+      lds_dma16(qseq, (uint32_t)(rg_ * DC * 2 + (hx * CPR + chunk) * 16), lds_offset(stg + j * 1024));
+    }
+  };
+  stage_latent(0);
+  {
+    const int ol = opaque_lane();
+    const int rr = ol >> 3, cs = ol & 7;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // eight 128-byte RoPE rows per instruction
+      const int r = j * 8 + rr;
+      const int rg_ = min(qrow0 + r, p.R - 1);
+      const int chunk = cs ^ ((r >> 1) & 7);
+      lds_dma16(rseq, (uint32_t)(rg_ * 128 + chunk * 16), lds_offset(rstg + j * 1024));
     }
   }
+  const int pg0 = scalar_read_now(bt + ((t0 * kTile) >> p.block_shift));
+  copy_tile<DC>(p, tile_src(p, pg0, t0, L), tiles_lds, w);
+  vm_wait<NI>();  // the page of tile 1 and round 1 have landed (the tile's NI copies may not)
   bf16x8 qf[Gm::KS];
   const int ln0 = opaque_lane();
   const int qrow = qrow0 + (ln0 & 31);
-  {
-    const int qr_ = min(qrow, p.R - 1);
-    const bf16x8* ql = (const bf16x8*)(p.q_lat + ((int64_t)b * p.R + qr_) * DC + 8 * (ln0 >> 5));
-    const bf16x8* qr = (const bf16x8*)(p.q_rope + ((int64_t)b * p.R + qr_) * 64 + 8 * (ln0 >> 5));
-#pragma unroll
-    for (int ks = KST; ks < DC / 16; ++ks) qf[ks] = ql[2 * ks];
-#pragma unroll
-    for (int ks = DC / 16; ks < Gm::KS; ++ks) qf[ks] = qr[2 * (ks - DC / 16)];
-  }
-#pragma unroll
-  for (int a = 0; a < PRE; ++a) {
-    if (a < n) {
-      copy_tile<DC>(p, tile_src(p, uniform(pg[a]), t0 + a, L), tiles_lds + a * TB, w);
-    }
-  }
-  // The direct loads must be in registers before the loop;
-  // the asm makes the compiler place that wait here, not inside the loop.
-  // The copies were issued earlier, so they have landed too.
-#pragma unroll
-  for (int ks = KST; ks < Gm::KS; ++ks) asm volatile("" ::"v"(qf[ks]));
-  vm_wait<0>();
-  {
-    const int col_ = ln0 & 31, hf = ln0 >> 5;
+  const int col_ = ln0 & 31, hf = ln0 >> 5;
+  auto read_latent = [&](int hx) {
 #pragma unroll
     for (int ks = 0; ks < KST; ++ks) {
       const int c = 2 * ks + hf;
-      qf[ks] = *(const bf16x8*)(stg + col_ * SROW + ((c ^ (col_ & (CPR - 1) & 15)) << 4));
+      qf[hx * KST + ks] = *(const bf16x8*)(stg + col_ * SROW + ((c ^ (col_ & (CPR - 1) & 15)) << 4));
     }
 #pragma unroll
-    for (int ks = 0; ks < KST; ++ks) asm volatile("" ::"v"(qf[ks]));
-    if (qrow >= p.R) {
+    for (int ks = 0; ks < KST; ++ks) asm volatile("" ::"v"(qf[hx * KST + ks]));
+  };
+  read_latent(0);
 #pragma unroll
-      for (int ks = 0; ks < Gm::KS; ++ks) qf[ks] = bf16x8{};
-    }
+  for (int kr = 0; kr < 4; ++kr) {
+    const int c = 2 * kr + hf;
+    qf[DC / 16 + kr] = *(const bf16x8*)(rstg + col_ * 128 + ((c ^ ((col_ >> 1) & 7)) << 4));
+  }
+#pragma unroll
+  for (int kr = 0; kr < 4; ++kr) asm volatile("" ::"v"(qf[DC / 16 + kr]));
+  // round 1's reads are done (the asm uses above waited for them) before
+  // round 2 overwrites the slots
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  stage_latent(1);
+  vm_wait<0>();  // round 2 and the first tile have landed
+  read_latent(1);
+  if (qrow >= p.R) {
+#pragma unroll
+    for (int ks = 0; ks < Gm::KS; ++ks) qf[ks] = bf16x8{};
   }
   const int my_row = rowbase + 32 * w + col;
   const int limit = min(L - p.S + 1 + my_row / p.H, L);  // first position this lane's row may not see

@@ -70,6 +70,21 @@ __device__ __forceinline__ void lds_dma16(const void* base_any, uint32_t voff, u
       : "memory", "m0");
 }
 
+// One 32-bit value at a wave-uniform address, read through the scalar path
+// and waited for in the same statement.  Its counter is the one the LDS
+// instructions use, not the vector-memory one, so this read can complete
+// while LDS copies issued before it are still in flight (a vector load
+// could only be waited for together with them).
+__device__ __forceinline__ int scalar_read_now(const int32_t* addr) {
+  const uint64_t a = reinterpret_cast<uint64_t>(addr);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const uint64_t sa = ((uint64_t)hi << 32) | (uint64_t)lo;
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(sa) : "memory");
+  return v;
+}
+
 // A lane id the compiler cannot see through, so that lane-derived constants
 // are recomputed where they are used instead of being kept live (and spilled)
 // across the whole kernel.
