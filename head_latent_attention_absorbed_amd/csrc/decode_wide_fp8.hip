@@ -45,7 +45,6 @@ struct F8Wide {
   static constexpr int NI = NQ + 1;                  // + the scales
   static constexpr int PB = NW * 2 * 1024;           // P of one tile
   static_assert(Gm::KS == F::NP, "one score k-step per row pair");
-  static_assert(Gm::KS % NI == 0, "the copy instructions divide the score k-steps");
 };
 
 // 4-byte global -> LDS copy (lane i writes LDS `lds` + 4 i), as lds_dma16.
@@ -104,26 +103,146 @@ __device__ __forceinline__ bf16x8 e4m3x8(uint32_t lo, uint32_t hi) {
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
 typedef __attribute__((address_space(3))) i32x2* lds_i32x2_ptr;
 
-// S^T = K . Q^T of one staged tile (the chain of score_mfma), each K
-// fragment decoded from 8 LDS bytes, with the next tile's copy spread over
-// the MFMAs.
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef __attribute__((__vector_size__(2 * sizeof(short)))) short s16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+
+// The query block as operands of the e4m3 score product (the 32x32x64
+// f8f6f4 MFMA, whose A operand is the K fragment exactly as copied): lane
+// (row r = lane % 32, k-half kh = lane / 32) holds, for 64-deep k-step j,
+// the 32 consecutive values 64 j + 32 kh .. +31 of query row r in two e4m3
+// parts with one power-of-two scale 2^s per row (the same on both of its
+// lanes):  hi = e4m3(q / 2^s),  lo = e4m3((q - hi 2^s) / 2^(s - 4)).
+// s puts the row's largest magnitude in [128, 256), inside e4m3's range;
+// hi keeps 4 significant bits of each value and lo the next 4, so hi + lo
+// carry a bf16 query to about 2^-8 of each value.  The MFMA multiplies each
+// part by its scale (E8M0 bytes sh, sl), so both products accumulate into one
+// chain.
 template <int DC>
-__device__ __forceinline__ f32x16 score_f8(const char* tb, const bf16x8 (&qf)[Geo<DC>::KS], const F8Dma<DC>& dma) {
-  constexpr int KS = Geo<DC>::KS, PD = kScoreAhead, NI = F8Wide<DC>::NI;
-  const int lane = opaque_lane();
-  const char* kb = tb + (lane & 31) * 16 + (lane >> 5) * 8;
-  uint2 kr[KS];
-#pragma unroll
-  for (int ks = 0; ks < PD; ++ks) kr[ks] = *(const uint2*)(kb + ks * 512);
-  f32x16 s;
+struct QF8 {
+  static constexpr int NJ = (DC + 64) / 64;
+  i32x8 hi[NJ], lo[NJ];
+  int sh, sl;
+};
+
+template <int DC>
+__device__ __forceinline__ void make_qf8(const bf16x8 (&qf)[Geo<DC>::KS], QF8<DC>& q) {
+  constexpr int KS = Geo<DC>::KS, NJ = QF8<DC>::NJ;
+  static_assert(KS == 4 * NJ, "four 16-deep k-steps per 64-deep step");
+  // the row's largest magnitude (bf16 magnitudes order as integers), over
+  // this lane's values and its partner lane's (lane ^ 32)
+  uint32_t mx = 0;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    if (ks + PD < KS) kr[ks + PD] = *(const uint2*)(kb + (ks + PD) * 512);
-    if (ks % (KS / NI) == 0) dma.issue(ks / (KS / NI));
-    const bf16x8 a = e4m3x8(kr[ks].x, kr[ks].y);
-    if (ks == 0) mfma_v_first(s, a, qf[ks]);
-    else if (ks + 1 < KS) mfma_v_acc(s, a, qf[ks]);
-    else mfma_v_last(s, a, qf[ks]);
+    const uint4 u = __builtin_bit_cast(uint4, qf[ks]);
+    const uint32_t d[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = max(mx, max(d[i] & 0x7fffu, (d[i] >> 16) & 0x7fffu));
+  }
+  mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+  // exponent e of the largest magnitude (bf16 bits 14..7); s = e - 7, kept
+  // where both 2^s and 2^(s - 4) are normal fp32 values
+  const int e = (int)(mx >> 7) - 127;
+  const int sc = max(e - 7, -122);
+  q.sh = sc + 127;
+  q.sl = sc + 123;
+  const float f_hi = __builtin_bit_cast(float, (uint32_t)(sc + 127) << 23);
+  const float f_lo = __builtin_bit_cast(float, (uint32_t)(sc + 123) << 23);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    // this lane's 32 values: k-steps 4j + 2kh and 4j + 2kh + 1, both halves.
+    // Lane r holds half 0 of every k-step and lane r + 32 half 1; the swap
+    // gives the low lane the partner's half 1 of k-steps 4j, 4j + 1 and the
+    // high lane the partner's half 0 of k-steps 4j + 2, 4j + 3.
+    const uint4 a0 = __builtin_bit_cast(uint4, qf[4 * j]), a2 = __builtin_bit_cast(uint4, qf[4 * j + 2]);
+    const uint4 a1 = __builtin_bit_cast(uint4, qf[4 * j + 1]), a3 = __builtin_bit_cast(uint4, qf[4 * j + 3]);
+    const uint32_t x0[4] = {a0.x, a0.y, a0.z, a0.w}, x2[4] = {a2.x, a2.y, a2.z, a2.w};
+    const uint32_t x1[4] = {a1.x, a1.y, a1.z, a1.w}, x3[4] = {a3.x, a3.y, a3.z, a3.w};
+    uint32_t v[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto p02 = __builtin_amdgcn_permlane32_swap(x0[i], x2[i], false, false);
+      const auto p13 = __builtin_amdgcn_permlane32_swap(x1[i], x3[i], false, false);
+      v[i] = p02[0];       // values 0 .. 7
+      v[4 + i] = p02[1];   // values 8 .. 15
+      v[8 + i] = p13[0];   // values 16 .. 23
+      v[12 + i] = p13[1];  // values 24 .. 31
+    }
+    int h[8], l[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      s16x2 hb = {0, 0};
+      hb = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hb, __builtin_bit_cast(bf16x2, v[2 * m]), f_hi, false);
+      hb = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hb, __builtin_bit_cast(bf16x2, v[2 * m + 1]), f_hi, true);
+      h[m] = __builtin_bit_cast(int, hb);
+      const f32x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)h[m], f_hi, false);
+      const f32x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)h[m], f_hi, true);
+      const float y0 = __builtin_bit_cast(float, v[2 * m] << 16) - b0[0];
+      const float y1 = __builtin_bit_cast(float, v[2 * m] & 0xffff0000u) - b0[1];
+      const float y2 = __builtin_bit_cast(float, v[2 * m + 1] << 16) - b1[0];
+      const float y3 = __builtin_bit_cast(float, v[2 * m + 1] & 0xffff0000u) - b1[1];
+      s16x2 lb = {0, 0};
+      lb = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lb, y0, y1, f_lo, false);
+      lb = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lb, y2, y3, f_lo, true);
+      l[m] = __builtin_bit_cast(int, lb);
+    }
+    q.hi[j] = i32x8{h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]};
+    q.lo[j] = i32x8{l[0], l[1], l[2], l[3], l[4], l[5], l[6], l[7]};
+  }
+}
+
+// The scaled e4m3 score MFMA in inline asm, so that it stays where it is
+// placed between the copy instructions, with the hazard handling of the
+// bf16 chain helpers (s_nop 1 before each MFMA; the last one carries the
+// wait states a VALU read of its result needs).  sa, sb: E8M0 scale bytes.
+__device__ __forceinline__ void mf8_first(f32x16& acc, const i32x8& a, const i32x8& b, int sa, int sb) {
+  asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[0,0,0]"
+               : "=&v"(acc)
+               : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+__device__ __forceinline__ void mf8_acc(f32x16& acc, const i32x8& a, const i32x8& b, int sa, int sb) {
+  asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+               : "+v"(acc)
+               : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+__device__ __forceinline__ void mf8_last(f32x16& acc, const i32x8& a, const i32x8& b, int sa, int sb) {
+  asm volatile(
+      "s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : "+v"(acc)
+      : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+
+// S^T = K . Q^T of one staged tile: per 64-deep k-step j, lane (token t,
+// k-half kh) reads its 32 key bytes (row pairs 4 j + 2 kh and 4 j + 2 kh + 1
+// of token t) and two scaled MFMAs add K . hi and K . lo, with the next
+// tile's copy spread over the steps.
+template <int DC>
+__device__ __forceinline__ f32x16 score_f8(const char* tb, const QF8<DC>& q, const F8Dma<DC>& dma) {
+  constexpr int NJ = QF8<DC>::NJ, PD = 2, NI = F8Wide<DC>::NI;
+  static_assert(NJ >= NI, "at most one copy instruction per k-step");
+  const int lane = opaque_lane();
+  const char* kb = tb + (64 * (lane >> 5) + (lane & 31)) * 16;
+  auto kread = [&](int j) {
+    const uint4 x = *(const uint4*)(kb + j * 2048);
+    const uint4 y = *(const uint4*)(kb + j * 2048 + 512);
+    return i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+  };
+  i32x8 kr[NJ];
+#pragma unroll
+  for (int j = 0; j < PD; ++j) kr[j] = kread(j);
+  constexpr int kOne = 127;  // E8M0 2^0: the keys are used as stored
+  f32x16 s;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    if (j + PD < NJ) kr[j + PD] = kread(j + PD);
+#pragma unroll
+    for (int c = 0; c < NI; ++c)
+      if ((c * NJ) / NI == j) dma.issue(c);
+    if (j == 0) mf8_first(s, kr[j], q.hi[j], kOne, q.sh);
+    else mf8_acc(s, kr[j], q.hi[j], kOne, q.sh);
+    if (j + 1 < NJ) mf8_acc(s, kr[j], q.lo[j], kOne, q.sl);
+    else mf8_last(s, kr[j], q.lo[j], kOne, q.sl);
   }
   __builtin_amdgcn_sched_barrier(0);
   return s;
@@ -301,6 +420,8 @@ __global__ void __launch_bounds__(256)
       for (int ks = 0; ks < Gm::KS; ++ks) qf[ks] = bf16x8{};
     }
   }
+  QF8<DC> q8;
+  make_qf8<DC>(qf, q8);
 
   const int my_row = rowbase + 32 * w + col;
   const int limit = min(L - p.S + 1 + my_row / p.H, L);  // first position this lane's row may not see
@@ -330,7 +451,7 @@ __global__ void __launch_bounds__(256)
     if (i + AHEAD + 1 < n) page_pf = tile_page_load(p, bt, t + AHEAD + 1);
     const F8Dma<DC> dma = make_dma(i + AHEAD, page_cur, i + AHEAD < n);
     const int pos0 = t * kTile;
-    WideSoftmax<true> sm{score_f8<DC>(raw + (i % NBUF) * RAW, qf, dma), tscale[i % NBUF], limit - pos0 - 4 * half,
+    WideSoftmax<true> sm{score_f8<DC>(raw + (i % NBUF) * RAW, q8, dma), tscale[i % NBUF], limit - pos0 - 4 * half,
                          p.scale_log2, m_run, l_run, half};
     if constexpr (PV) {
       if (fl.x | fl.y | fl.z | fl.w) {
