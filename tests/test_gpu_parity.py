@@ -137,6 +137,62 @@ def test_small_parity_few_splits(name, extra_parts, merge):
     _check_all(inputs, st)
 
 
+def _scale_sequence(inputs, b, e):
+    """Sequence b's queries times 2^e and its cache's per-token scales times
+    2^-e (both exact): the scores, softmax weights and lse stay as they were,
+    the outputs scale by 2^-e."""
+    w = inputs["workload"]
+    f = np.float32(2.0 ** e)
+    for key in ("q_nope", "q_rope"):
+        x = oracle.bf16_to_f64(inputs[key][b]).astype(np.float32) * f
+        inputs[key][b] = (x.view(np.uint32) >> 16).astype(np.uint16)  # exact: a power-of-two factor
+    pages = inputs["block_table"][b][inputs["block_table"][b] >= 0]
+    inputs["kv_scale"][pages] *= np.float32(2.0 ** -e)
+    return inputs
+
+
+@pytest.mark.parametrize("merge", list(MERGES))
+def test_fp8_query_magnitude_range(merge):
+    """e4m3 cache with query rows far outside e4m3's range: one sequence's
+    queries times 2^12 (|q_lat| up to ~9e3, where e4m3 saturates at 448),
+    the other's times 2^-12 (|q_lat| ~ 5e-4, below e4m3's smallest
+    subnormal), each with the inverse factor on its cache scales so that the
+    attention is unchanged.  The 128-row kernel splits each query row into
+    e4m3 parts under a per-row power-of-two scale, so every result must equal
+    the unscaled run's bit for bit after the same power of two (lse
+    unchanged); the unscaled run is checked against the oracle."""
+    import torch
+
+    w = small_workload("kimi_k2_fp8", batch=2, heads=64, q_len=2, seq_len=(40, 300), max_seq_len=320,
+                       forced_lens=(300, 77))
+    base = make_inputs(w)
+    _announce(f"fp8_query_magnitude_range/unscaled/{merge}", base)
+    st0 = run_step(base, partial="fp32", fused=MERGES[merge])
+    _check_all(base, st0)
+    exps = (12, -12)
+    scaled = make_inputs(w)
+    for b, e in enumerate(exps):
+        _scale_sequence(scaled, b, e)
+    _announce(f"fp8_query_magnitude_range/scaled/{merge}", scaled)
+    st1 = run_step(scaled, partial="fp32", fused=MERGES[merge])
+
+    def same(name, got, ref, factor):
+        got, ref = got.double().cpu(), ref.double().cpu() * factor
+        ok = torch.equal(torch.nan_to_num(got, nan=7.0), torch.nan_to_num(ref, nan=7.0))
+        assert ok, f"{name}: max |diff| {float((got - ref).abs().nan_to_num(0.0).max()):.3e}"
+
+    from head_latent_attention_absorbed_amd import split_plan
+    for b, e in enumerate(exps):
+        same(f"q_lat[{b}]", st1.q_lat[b], st0.q_lat[b], 2.0 ** e)
+        same(f"out[{b}]", st1.out[b], st0.out[b], 2.0 ** -e)
+        if st0.o_lat is not None:
+            same(f"o_lat[{b}]", st1.o_lat[b], st0.o_lat[b], 2.0 ** -e)
+    same("lse", st1.lse, st0.lse, 1.0)
+    same("lse_part", st1.lse_part, st0.lse_part, 1.0)
+    for slot, b, _, _ in split_plan(base["seq_lens"], st0.num_parts):
+        same(f"o_part[{slot}]", st1.o_part[slot], st0.o_part[slot], 2.0 ** -exps[b])
+
+
 # Row tiles of the fused merge: 16 query rows (b*S_q + s) per work-group, so
 # B*S_q = 17 and 33 leave a ragged last tile of one row, 40 one of eight.
 RAGGED_ROWS = {
