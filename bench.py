@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 INFINITY_CACHE_BYTES = 256 << 20
 
 
@@ -51,20 +52,22 @@ def algorithmic(w, seq_lens):
     q_bytes = w.batch * R * (w.d_latent + w.d_rope) * 2          # q_lat + q_rope read by the decode
     w_bytes = 2 * w.heads * w.d_nope * w.d_latent * 2            # W_UK + W_UV
     io_bytes = w.batch * R * (w.d_nope + w.d_rope) * 2 + w.batch * R * w.d_v * (4 if w.out_dtype == "fp32" else 2)
-    attn_flops = 0
+    score_flops = pv_flops = 0
     for Lb in L:
         for s in range(w.q_len):
             vis = max(0, Lb - w.q_len + 1 + s)
-            attn_flops += 2 * w.heads * vis * (2 * w.d_latent + w.d_rope)
+            score_flops += 2 * w.heads * vis * (w.d_latent + w.d_rope)
+            pv_flops += 2 * w.heads * vis * w.d_latent
+    attn_flops = score_flops + pv_flops
     proj_flops = 4 * w.batch * R * w.d_nope * w.d_latent
     return dict(cache_bytes=cache_bytes, decode_bytes=cache_bytes + q_bytes,
-                step_bytes=cache_bytes + w_bytes + io_bytes, attn_flops=attn_flops,
+                step_bytes=cache_bytes + w_bytes + io_bytes, attn_flops=attn_flops, score_flops=score_flops,
+                pv_flops=pv_flops,
                 step_flops=attn_flops + proj_flops, record_bytes=rec, tokens=sum(L))
 
 
 KERNEL_SOURCES = ("decode.hip", "decode_wide.hip", "decode_wide_fp8.hip", "decode_wide_pair.hip", "wide_common.h",
                   "decode_common.h", "split_plan.h", "tile_ops.h", "mla_device.h", "mla_kernels.h")
-RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # 312.5
 
 
 def decode_kernel_name(w) -> str:
@@ -75,22 +78,38 @@ def decode_kernel_name(w) -> str:
     return "decode_wide_pair_kernel" if w.d_latent == 256 else "decode_wide_kernel"
 
 
-def roofline_of(alg, us, measured=None):
+def mfma_peak_tflops(w, alg) -> float:
+    """The dense MFMA peak of the decode's products.  bf16 for a bf16 cache
+    and for the few-rows kernel (which decodes e4m3 tiles to bf16).  The
+    128-row e4m3 kernel runs the score product on e4m3 MFMA (5.0 PFLOP/s) and
+    P . V on bf16 (2.5): its peak is the rate at which both finish at their
+    own peaks, flops / (score / 5.0 + pv / 2.5)."""
+    if w.cache_dtype != "fp8_e4m3" or w.q_len * w.heads <= 64:
+        return MFMA_BF16_PEAK_TFLOPS
+    t = alg["score_flops"] / MFMA_FP8_PEAK_TFLOPS + alg["pv_flops"] / MFMA_BF16_PEAK_TFLOPS
+    return alg["attn_flops"] / t
+
+
+def roofline_of(alg, us, measured=None, w=None):
     """The decode launch against the roofline that bounds it: HBM when its
     algorithmic flops per byte are below the ridge of the nominal peaks
-    (bf16 MFMA over HBM), bf16 MFMA above it (the e4m3 cache is decoded to
-    bf16, so its products run at the bf16 rate).  The other fraction is
-    given beside it, and each against the measured peaks when there are any."""
+    (the MFMA peak of its products over HBM), MFMA above it.  The other
+    fraction is given beside it, and each against the measured peaks when
+    there are any (the measured MFMA rate is bf16's)."""
     gbs = alg["decode_bytes"] / (us * 1e-6) / 1e9
     tflops = alg["attn_flops"] / (us * 1e-6) / 1e12
     ai = alg["attn_flops"] / alg["decode_bytes"]
+    peak = MFMA_BF16_PEAK_TFLOPS if w is None else mfma_peak_tflops(w, alg)
     r = {"flop_per_byte": round(ai, 1)}
-    if ai > RIDGE_FLOP_PER_BYTE:
-        r.update(bound="mfma", achieved=round(tflops, 1), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                 frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+    if ai > peak * 1e12 / (HBM_PEAK_GBS * 1e9):
+        r.update(bound="mfma", achieved=round(tflops, 1), peak=round(peak, 1), unit="TFLOP/s",
+                 frac=round(tflops / peak, 4), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+        if peak != MFMA_BF16_PEAK_TFLOPS:
+            r["peak_is"] = "score product on e4m3 MFMA (5.0 PFLOP/s), P.V on bf16 (2.5), weighted by their flops"
+            r["frac_of_bf16_peak"] = round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)
     else:
         r.update(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                 frac=round(gbs / HBM_PEAK_GBS, 4), mfma_frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4))
+                 frac=round(gbs / HBM_PEAK_GBS, 4), mfma_frac=round(tflops / peak, 4))
     if measured:
         r["frac_of_measured_hbm"] = round(gbs / measured["hbm_gbs"], 4)
         r["frac_of_measured_mfma"] = round(tflops / measured["mfma_bf16_tflops"], 4)
@@ -485,7 +504,7 @@ def leg_configs(torch, np, stream, K, args, exclude, measured=None):
                                    "merge_up": round(float(med[2]), 2)},
             "tbs_decode_merge": round(alg["cache_bytes"] / ((med[1] + med[2]) * 1e-6) / 1e12, 4),
             "tbs_step": round(alg["cache_bytes"] / (float(np.median(step)) * 1e-6) / 1e12, 4),
-            "decode_roofline": dict(kernel=decode_kernel_name(w), **roofline_of(alg, dec_mean, measured)),
+            "decode_roofline": dict(kernel=decode_kernel_name(w), **roofline_of(alg, dec_mean, measured, w)),
         }
         log(f"configs: {name} step {res[name]['us_per_step']['median']} us, decode {med[1]:.1f} us")
         del steps, inputs
@@ -707,7 +726,7 @@ def main():
         "step_hbm_frac": round(value * 1e3 / HBM_PEAK_GBS, 4),
         "roofline": dict(
             kernel=f"{decode_kernel_name(w)} (mla_decode_paged)",
-            **roofline_of(alg, dec_us, measured),
+            **roofline_of(alg, dec_us, measured, w),
             traffic=measured_traffic(w.name, decode_kernel_name(w)) if args.partial == "fp16" else None,
             algorithmic_bytes_per_launch=alg["decode_bytes"],
             algorithmic_flops_per_launch=alg["attn_flops"],

@@ -80,12 +80,13 @@ def test_hashed_sources_exist(name):
 
 def test_roofline_bound_follows_the_ridge():
     """The headline workload (about 242 flop/B) is reported against HBM, the
-    4-token e4m3 workload (about 960 flop/B) against the bf16 MFMA peak."""
+    4-token e4m3 workload (about 960 flop/B) against the MFMA peak of its
+    products: e4m3 for the score product, bf16 for P . V."""
     from workloads.generate import make_inputs
     for name, bound in (("deepseek_v3", "hbm"), ("kimi_k2_fp8", "mfma")):
         w = get_workload(name)
         a = bench.algorithmic(w, make_inputs(w, poison=False)["seq_lens"])
-        r = bench.roofline_of(a, 100.0, {"hbm_gbs": 6000.0, "mfma_bf16_tflops": 2000.0})
+        r = bench.roofline_of(a, 100.0, {"hbm_gbs": 6000.0, "mfma_bf16_tflops": 2000.0}, w)
         assert r["bound"] == bound, (name, r)
         us = 100e-6
         if bound == "hbm":
@@ -93,5 +94,22 @@ def test_roofline_bound_follows_the_ridge():
             assert r["frac"] == round(r["achieved"] / bench.HBM_PEAK_GBS, 4)
         else:
             assert r["achieved"] == round(a["attn_flops"] / us / 1e12, 1) and r["unit"] == "TFLOP/s"
-            assert r["frac"] == round(r["achieved"] / bench.MFMA_BF16_PEAK_TFLOPS, 4)
+            assert r["frac"] == round(a["attn_flops"] / us / 1e12 / bench.mfma_peak_tflops(w, a), 4)
         assert r["frac_of_measured_hbm"] == round(a["decode_bytes"] / us / 1e9 / 6000.0, 4)
+
+
+def test_mixed_mfma_peak():
+    """Per token and query row the score product is 2 (d_c + d_r) flops and
+    P . V 2 d_c; at d_c = 512, d_r = 64 the two at 5.0 and 2.5 PFLOP/s give
+    1088 / (576 / 5 + 512 / 2.5) = 3400 TFLOP/s.  bf16 caches, and e4m3 with
+    at most 64 query rows (decoded to bf16), stay at 2.5."""
+    from workloads.generate import make_inputs
+    w = get_workload("kimi_k2_fp8")
+    a = bench.algorithmic(w, make_inputs(w, poison=False)["seq_lens"])
+    assert a["score_flops"] + a["pv_flops"] == a["attn_flops"]
+    assert a["score_flops"] * 512 == a["pv_flops"] * 576
+    assert abs(bench.mfma_peak_tflops(w, a) - 3400.0) < 1e-6
+    w2 = get_workload("deepseek_v3")
+    assert bench.mfma_peak_tflops(w2, bench.algorithmic(w2, [4096] * 32)) == bench.MFMA_BF16_PEAK_TFLOPS
+    w3 = small_workload("kimi_k2_fp8", heads=16)  # 64 rows: the few-rows kernel
+    assert bench.mfma_peak_tflops(w3, bench.algorithmic(w3, [300] * w3.batch)) == bench.MFMA_BF16_PEAK_TFLOPS
