@@ -389,7 +389,7 @@ def leg_tpla(torch, np, stream, K, args, w, inputs, alg, step0):
                 "at d_c/2 each) + mla_tpla_reduce",
         "n_shards": tst.n, "us_per_step": round(tp_step, 2), "shard_decode_us_median": round(tp_dec, 2),
         "rel_l2_vs_mla": {k: round(v, 5) for k, v in tp_err.items()},
-        "roofline": {"kernel": "decode_kernel (one shard, d_latent %d)" % tst.dcs, "bound": "hbm",
+        "roofline": {"kernel": "decode_wide_pair_kernel (one shard, d_latent %d)" % tst.dcs, "bound": "hbm",
                      "achieved": round(sh_bytes / (tp_dec * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(sh_bytes / (tp_dec * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes_per_launch": sh_bytes},

@@ -97,6 +97,11 @@ SMALL_CASES = {
     # 4-token tail over 40 heads, e4m3: 160 rows, the second 128-row group 32 rows deep
     "fp8_sq4_h40": small_workload("kimi_k2_fp8", batch=2, heads=40, seq_len=(4, 300), max_seq_len=320,
                                   forced_lens=(4, 257)),
+    # e4m3 at d_c = 256 with 128 rows (2-token tail over 64 heads): the 128-row
+    # e4m3 kernel's five 64-deep score steps
+    "fp8_dc256_sq2_h64": replace(small_workload("tpla_shard", batch=2, heads=64, q_len=2, seq_len=(2, 300),
+                                                max_seq_len=320, forced_lens=(2, 299)),
+                                 cache_dtype="fp8_e4m3"),
 }
 
 
@@ -125,7 +130,8 @@ def test_small_parity_fp32_partials(name, merge):
 
 
 @pytest.mark.parametrize("merge", list(MERGES))
-@pytest.mark.parametrize("name", ["h128_ragged", "dc256", "dc256_odd", "dc256_sq2_h64", "fp8_sq4_h64", "h32"])
+@pytest.mark.parametrize("name", ["h128_ragged", "dc256", "dc256_odd", "dc256_sq2_h64", "fp8_sq4_h64", "fp8_dc256_sq2_h64",
+                                  "h32"])
 @pytest.mark.parametrize("extra_parts", [0, 1, 5])
 def test_small_parity_few_splits(name, extra_parts, merge):
     """Few token parts: each part runs many tiles (num_parts = B gives one
