@@ -97,6 +97,17 @@ SMALL_CASES = {
     # 4-token tail over 40 heads, e4m3: 160 rows, the second 128-row group 32 rows deep
     "fp8_sq4_h40": small_workload("kimi_k2_fp8", batch=2, heads=40, seq_len=(4, 300), max_seq_len=320,
                                   forced_lens=(4, 257)),
+    # pages of 32, 128 and 256 records (power-of-two page sizes >= one tile)
+    # through the 128-row bf16 kernel, the 128-row e4m3 kernel and the
+    # few-rows kernel
+    "h128_bs32": small_workload("deepseek_v3", batch=3, seq_len=(1, 900), max_seq_len=1024, block_size=32,
+                                forced_lens=(900, 33, 417)),
+    "h128_bs128": small_workload("deepseek_v3", batch=3, seq_len=(1, 900), max_seq_len=1024, block_size=128,
+                                 forced_lens=(129, 800, 5)),
+    "fp8_sq4_h64_bs128": small_workload("kimi_k2_fp8", batch=2, seq_len=(4, 600), max_seq_len=640, block_size=128,
+                                        forced_lens=(600, 131)),
+    "h32_bs256": small_workload("gqa7b", batch=3, seq_len=(1, 700), max_seq_len=768, block_size=256,
+                                forced_lens=(700, 257, 40)),
     # e4m3 at d_c = 256 with 128 rows (2-token tail over 64 heads): the 128-row
     # e4m3 kernel's five 64-deep score steps
     "fp8_dc256_sq2_h64": replace(small_workload("tpla_shard", batch=2, heads=64, q_len=2, seq_len=(2, 300),
@@ -131,7 +142,7 @@ def test_small_parity_fp32_partials(name, merge):
 
 @pytest.mark.parametrize("merge", list(MERGES))
 @pytest.mark.parametrize("name", ["h128_ragged", "dc256", "dc256_odd", "dc256_sq2_h64", "fp8_sq4_h64", "fp8_dc256_sq2_h64",
-                                  "h32"])
+                                  "h32", "h128_bs32", "fp8_sq4_h64_bs128"])
 @pytest.mark.parametrize("extra_parts", [0, 1, 5])
 def test_small_parity_few_splits(name, extra_parts, merge):
     """Few token parts: each part runs many tiles (num_parts = B gives one
