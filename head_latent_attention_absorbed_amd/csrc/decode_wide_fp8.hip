@@ -217,8 +217,8 @@ __device__ __forceinline__ void mf8_last(f32x16& acc, const i32x8& a, const i32x
 // k-half kh) reads its 32 key bytes (row pairs 4 j + 2 kh and 4 j + 2 kh + 1
 // of token t) and two scaled MFMAs add K . hi and K . lo, with the next
 // tile's copy spread over the steps.
-template <int DC>
-__device__ __forceinline__ f32x16 score_f8(const char* tb, const QF8<DC>& q, const F8Dma<DC>& dma) {
+template <int DC, class Pre = NoPre>
+__device__ __forceinline__ f32x16 score_f8(const char* tb, const QF8<DC>& q, const F8Dma<DC>& dma, Pre&& pre = Pre{}) {
   constexpr int NJ = QF8<DC>::NJ, PD = 2, NI = F8Wide<DC>::NI;
   static_assert(NJ >= NI, "at most one copy instruction per k-step");
   const int lane = opaque_lane();
@@ -239,6 +239,7 @@ __device__ __forceinline__ f32x16 score_f8(const char* tb, const QF8<DC>& q, con
 #pragma unroll
     for (int c = 0; c < NI; ++c)
       if ((c * NJ) / NI == j) dma.issue(c);
+    if (j == NJ - 4) pre.load();  // the lagged P . V's first operands, eight MFMAs ahead of it
     if (j == 0) mf8_first(s, kr[j], q.hi[j], kOne, q.sh);
     else mf8_acc(s, kr[j], q.hi[j], kOne, q.sh);
     if (j + 1 < NJ) mf8_acc(s, kr[j], q.lo[j], kOne, q.sl);
@@ -263,20 +264,40 @@ __device__ __forceinline__ bf16x8 v_frag_f8(const char* vb, int nb, int j) {
 // addresses bytes 8 (s % 2) .. +7 of row pair 2 nb + G % 2 of token
 // 16 j + 4 (G / 2) + e % 4 + 8 (e / 4), e = s / 2 (result byte e of the
 // receiving lanes).
-template <int DC, bool STEPS, class SM>
-__device__ __forceinline__ void pv_f8(const char* tb, const char* pb, f32x16 (&O)[4][Geo<DC>::NB / 4], int w, SM& sm) {
-  constexpr int NBW = Geo<DC>::NB / 4;
-  const int lane = opaque_lane();
-  const int G = lane >> 4, s = lane & 15;
-  const int e = s >> 1;
-  const char* vb = tb + (32 * (G & 1) + 4 * (G >> 1) + (e & 3) + 8 * (e >> 2)) * 16 + 8 * (s & 1);
+template <int DC>
+struct F8PvOperands {
+  static constexpr int NBW = Geo<DC>::NB / 4;
+  const char* vb;
+  const char* pb;
+  int w;
   bf16x8 pf[4][2];
+  bf16x8 c0, c1;
+  __device__ __forceinline__ F8PvOperands(const char* tb, const char* pb_, int w_) : pb(pb_), w(w_) {
+    const int lane = opaque_lane();
+    const int G = lane >> 4, s = lane & 15;
+    const int e = s >> 1;
+    vb = tb + (32 * (G & 1) + 4 * (G >> 1) + (e & 3) + 8 * (e >> 2)) * 16 + 8 * (s & 1);
+  }
+  // P of all four row blocks and the first column block's V (read by the
+  // score chain before its end, so that the first P . V MFMA finds them).
+  __device__ __forceinline__ void load() {
+    const int lane = opaque_lane();
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) pf[rb][j] = *(const bf16x8*)(pb + (rb * 2 + j) * 1024 + lane * 16);
+      for (int j = 0; j < 2; ++j) pf[rb][j] = *(const bf16x8*)(pb + (rb * 2 + j) * 1024 + lane * 16);
+    c0 = v_frag_f8(vb, w * NBW, 0);
+    c1 = v_frag_f8(vb, w * NBW, 1);
+  }
+};
+
+template <int DC, bool STEPS, class SM>
+__device__ __forceinline__ void pv_f8(const F8PvOperands<DC>& op, f32x16 (&O)[4][Geo<DC>::NB / 4], SM& sm) {
+  constexpr int NBW = Geo<DC>::NB / 4;
+  const char* vb = op.vb;
+  const int w = op.w;
   constexpr int SPB = (SM::STEPS + NBW - 1) / NBW;
-  bf16x8 c0 = v_frag_f8(vb, w * NBW, 0), c1 = v_frag_f8(vb, w * NBW, 1);
+  bf16x8 c0 = op.c0, c1 = op.c1;
 #pragma unroll
   for (int cb = 0; cb < NBW; ++cb) {
     bf16x8 n0 = c0, n1 = c1;
@@ -286,8 +307,8 @@ __device__ __forceinline__ void pv_f8(const char* tb, const char* pb, f32x16 (&O
     }
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      O[rb][cb] = mfma32(c0, pf[rb][0], O[rb][cb]);
-      O[rb][cb] = mfma32(c1, pf[rb][1], O[rb][cb]);
+      O[rb][cb] = mfma32(c0, op.pf[rb][0], O[rb][cb]);
+      O[rb][cb] = mfma32(c1, op.pf[rb][1], O[rb][cb]);
     }
     if constexpr (STEPS) {
 #pragma unroll
@@ -451,8 +472,10 @@ __global__ void __launch_bounds__(256)
     if (i + AHEAD + 1 < n) page_pf = tile_page_load(p, bt, t + AHEAD + 1);
     const F8Dma<DC> dma = make_dma(i + AHEAD, page_cur, i + AHEAD < n);
     const int pos0 = t * kTile;
-    WideSoftmax<true> sm{score_f8<DC>(raw + (i % NBUF) * RAW, q8, dma), tscale[i % NBUF], limit - pos0 - 4 * half,
-                         p.scale_log2, m_run, l_run, half};
+    F8PvOperands<DC> pv(raw + ((i + NBUF - 1) % NBUF) * RAW, pbuf + ((i - 1) & 1) * PB, w);
+    WideSoftmax<true> sm{PV ? score_f8<DC>(raw + (i % NBUF) * RAW, q8, dma, pv)
+                            : score_f8<DC>(raw + (i % NBUF) * RAW, q8, dma),
+                         tscale[i % NBUF], limit - pos0 - 4 * half, p.scale_log2, m_run, l_run, half};
     if constexpr (PV) {
       if (fl.x | fl.y | fl.z | fl.w) {
         float a[4];
@@ -460,7 +483,7 @@ __global__ void __launch_bounds__(256)
         for (int rb = 0; rb < 4; ++rb) a[rb] = alph[(i - 1) & 1][32 * rb + col];
         rescale_rows<NBW>(O, a);
       }
-      pv_f8<DC, true>(raw + ((i - 1) % NBUF) * RAW, pbuf + ((i - 1) & 1) * PB, O, w, sm);
+      pv_f8<DC, true>(pv, O, sm);
     } else {
       sm.all();
     }
@@ -486,7 +509,9 @@ __global__ void __launch_bounds__(256)
       rescale_rows<NBW>(O, a);
     }
     NoSteps none;
-    pv_f8<DC, false>(raw + ((n - 1) % NBUF) * RAW, pbuf + pbi * PB, O, w, none);
+    F8PvOperands<DC> pv(raw + ((n - 1) % NBUF) * RAW, pbuf + pbi * PB, w);
+    pv.load();
+    pv_f8<DC, false>(pv, O, none);
   }
 
   // ---- normalise and write this part's partial and lse
