@@ -264,6 +264,11 @@ __device__ __forceinline__ bf16x8 v_frag_f8(const char* vb, int nb, int j) {
 // addresses bytes 8 (s % 2) .. +7 of row pair 2 nb + G % 2 of token
 // 16 j + 4 (G / 2) + e % 4 + 8 (e / 4), e = s / 2 (result byte e of the
 // receiving lanes).
+// The no-op publication hook of pv_f8.
+struct NoPublish {
+  __device__ __forceinline__ void operator()() const {}
+};
+
 template <int DC>
 struct F8PvOperands {
   static constexpr int NBW = Geo<DC>::NB / 4;
@@ -291,12 +296,16 @@ struct F8PvOperands {
   }
 };
 
-template <int DC, bool STEPS, class SM>
-__device__ __forceinline__ void pv_f8(const F8PvOperands<DC>& op, f32x16 (&O)[4][Geo<DC>::NB / 4], SM& sm) {
+template <int DC, bool STEPS, class SM, class Pub = NoPublish>
+__device__ __forceinline__ void pv_f8(const F8PvOperands<DC>& op, f32x16 (&O)[4][Geo<DC>::NB / 4], SM& sm,
+                                      const Pub& pub = Pub{}) {
   constexpr int NBW = Geo<DC>::NB / 4;
   const char* vb = op.vb;
   const int w = op.w;
-  constexpr int SPB = (SM::STEPS + NBW - 1) / NBW;
+  // softmax steps per column block, front-loaded (the last block gets none)
+  // so that the softmax's tail and the publication of its results (pub)
+  // run under the last block's MFMAs
+  constexpr int SPB = (SM::STEPS + NBW - 2) / (NBW - 1);
   bf16x8 c0 = op.c0, c1 = op.c1;
 #pragma unroll
   for (int cb = 0; cb < NBW; ++cb) {
@@ -314,6 +323,7 @@ __device__ __forceinline__ void pv_f8(const F8PvOperands<DC>& op, f32x16 (&O)[4]
 #pragma unroll
       for (int j = 0; j < SPB; ++j)
         if (cb * SPB + j < SM::STEPS) sm.step(cb * SPB + j);
+      if (cb * SPB < SM::STEPS && (cb + 1) * SPB >= SM::STEPS) pub();
     }
     c0 = n0;
     c1 = n1;
@@ -476,6 +486,17 @@ __global__ void __launch_bounds__(256)
     WideSoftmax<true> sm{PV ? score_f8<DC>(raw + (i % NBUF) * RAW, q8, dma, pv)
                             : score_f8<DC>(raw + (i % NBUF) * RAW, q8, dma),
                          tscale[i % NBUF], limit - pos0 - 4 * half, p.scale_log2, m_run, l_run, half};
+    // Publish P and the rescale factor of tile i (their buffers [i & 1] were
+    // last read in iteration i - 1, before this iteration's barrier).
+    auto publish = [&]() {
+      const int ol = opaque_lane();
+      char* pw = pbuf + (i & 1) * PB + (w * 2) * 1024 + ol * 16;
+      *(bf16x8*)pw = sm.pf0;
+      *(bf16x8*)(pw + 1024) = sm.pf1;
+      if (ol < 32) alph[i & 1][32 * w + ol] = sm.alpha;
+      const bool any = PV && __any(sm.alpha != 1.0f);
+      if (ol == 0) rflag[i & 1][w] = any;
+    };
     if constexpr (PV) {
       if (fl.x | fl.y | fl.z | fl.w) {
         float a[4];
@@ -483,17 +504,11 @@ __global__ void __launch_bounds__(256)
         for (int rb = 0; rb < 4; ++rb) a[rb] = alph[(i - 1) & 1][32 * rb + col];
         rescale_rows<NBW>(O, a);
       }
-      pv_f8<DC, true>(pv, O, sm);
+      pv_f8<DC, true>(pv, O, sm, publish);
     } else {
       sm.all();
+      publish();
     }
-    const int ol = opaque_lane();
-    char* pw = pbuf + (i & 1) * PB + (w * 2) * 1024 + ol * 16;
-    *(bf16x8*)pw = sm.pf0;
-    *(bf16x8*)(pw + 1024) = sm.pf1;
-    if (ol < 32) alph[i & 1][32 * w + ol] = sm.alpha;
-    const bool any = PV && __any(sm.alpha != 1.0f);
-    if (ol == 0) rflag[i & 1][w] = any;
   };
   tile_step(0, std::false_type{});
 #pragma nounroll
