@@ -6,21 +6,22 @@
 // P . V: wave w owns latent columns (DC/4) w .. for all 128 rows, P through
 // LDS, one tile late).  The difference is the tile image: the e4m3 bytes
 // stay in LDS as copied (row pair m = bytes 16m .. 16m+15 of the latent, then
-// of the RoPE key, token t at byte (32 m + t) 16) and each MFMA operand is
-// decoded in registers right before its MFMA, so there is no bf16 image, no
-// decode pass over the tile and no second barrier per tile:
-//   K fragment (score A operand): token col, bytes 16 ks + 8 half .. +8 of
-//     its record: one 8-byte LDS read, four e4m3 -> bf16 conversions;
-//   V^T fragment (P . V A operand): column c, the eight tokens of the P
-//     fragment it meets: one 8-bit transposing LDS read (each lane i of a
-//     16-lane group receives byte i % 8 of the words of lanes i / 8,
+// of the RoPE key, token t at byte (32 m + t) 16), so there is no bf16 image,
+// no decode pass over the tile and no second barrier per tile:
+//   scores: the e4m3 MFMA (32x32x64 f8f6f4) takes the key bytes as copied
+//     (two 16-byte LDS reads per lane and 64-deep k-step) against the query
+//     split once into two e4m3 parts under a per-row power-of-two scale
+//     (QF8 below);
+//   V^T fragment (P . V A operand, bf16 MFMA): column c, the eight tokens of
+//     the P fragment it meets: one 8-bit transposing LDS read (each lane i
+//     of a 16-lane group receives byte i % 8 of the words of lanes i / 8,
 //     i / 8 + 2, ..., i / 8 + 14, which address those tokens' halves of the
-//     column's row pair), four conversions.
-// Every e4m3 value is a bf16 value, so the conversions are exact (scale 1);
-// the keys' scale multiplies the raw scores and the values' scale is carried
-// by P (WideSoftmax<true>).  A tile is a quarter of a bf16 image's bytes in
-// LDS, so two tiles are kept in flight; their scales come with them by DMA.
-// Copy lanes past a sequence's length re-read its first record and scale.
+//     column's row pair), four e4m3 -> bf16 conversions (exact: every e4m3
+//     value is a bf16 value).
+// The keys' scale multiplies the raw scores and the values' scale is carried
+// by P (WideSoftmax<true>).  A staged tile is half a bf16 image's bytes, so
+// two tiles are kept in flight; their scales come with them by DMA.  Copy
+// lanes past a sequence's length re-read its first record and scale.
 #include <type_traits>
 
 #include "decode_common.h"
